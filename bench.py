@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE-layer forward pass on one MI355X (gfx950).
+
+A step is one whole layer: route, dispatch, grouped gate/up GEMM with the
+SwiGLU epilogue, grouped down GEMM (routed and shared experts), combine, all
+through ``moe_layer_fwd_timed`` of the C ABI on one stream, with inputs
+already resident in HBM.  The default workload is the DeepSeek-V2-Lite-shaped
+layer (T=4096, d=2048, 64 experts top-6 + 2 shared, I=1408), bf16 inputs with
+fp32 accumulation, synthetic seeded data.
+
+Prints one JSON line.  Per-stage times come from HIP events that the library
+records on the layer's stream between its kernels, averaged over the timed
+steps.  The oracle (fp64 NumPy on the host cores) is timed on a bounded token
+sample of the same workload as a CPU baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec + grouped-GEMM % bf16 MFMA peak, 1×MI355X"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+STAGES = ("route", "dispatch", "gate_up", "down", "combine")
+
+
+def stage_bytes(cfg):
+    """Algorithmic HBM bytes of the bandwidth-bound stages."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    R = T * k
+    return {
+        # x and W_r read, bias read, ids and weights written
+        "route": T * d * es + E * d * es + E * 4 + R * 8,
+        # ids read, x read once, x_sorted written, perm and inv_perm written
+        "dispatch": T * d * es + R * 4 + R * d * es + 2 * R * 4,
+        # y_sorted gathered, ids/weights read, shared output read, out written
+        "combine": R * d * 4 + R * 8 + (T * d * 4 if cfg.n_shared else 0) + T * d * 4,
+    }
+
+
+def gemm_flops(cfg):
+    R = cfg.T * cfg.k
+    gate_up = 4 * R * cfg.d * cfg.I + 4 * cfg.T * cfg.d * cfg.n_shared * cfg.I_shared
+    down = 2 * R * cfg.d * cfg.I + 2 * cfg.T * cfg.d * cfg.n_shared * cfg.I_shared
+    return gate_up, down
+
+
+def cpu_baseline(cfg, arrays, budget_s=10.0):
+    """Time the oracle on the first Ts tokens, doubling Ts until one run takes
+    at least budget_s or covers the whole workload."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    cores = len(os.sched_getaffinity(0))
+    Ts = min(512, cfg.T)
+    with threadpool_limits(limits=cores):
+        while True:
+            t0 = time.perf_counter()
+            oracle.moe_layer(arrays["x"][:Ts], arrays["w_router"], arrays["bias"], arrays["w_gate"],
+                             arrays["w_up"], arrays["w_down"], cfg.k, arrays["wsh_gate"],
+                             arrays["wsh_up"], arrays["wsh_down"], round_a=cfg.dtype == "bf16")
+            el = time.perf_counter() - t0
+            if el >= budget_s or Ts >= cfg.T:
+                break
+            Ts = min(cfg.T, Ts * 2)
+    return {"value": Ts / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {Ts} of {cfg.T} tokens, all {cfg.E} experts"
+                      f"{' + shared' if cfg.n_shared else ''}, fp64 NumPy oracle, {el:.1f} s"}
+
+
+def main():
+    import moe_synth
+
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="deepseek_v2_lite", choices=list(moe_synth.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (HBM counter scale)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's share of tokens; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import expert_routing_grouped_route_amd as moe
+
+    moe.lib()
+    torch.cuda.set_device(0)
+    cfg = moe_synth.CONFIGS[args.workload]
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    arrays = moe_synth.generate(cfg, workers=min(16, len(os.sched_getaffinity(0))))
+    wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = {n: (None if v is None else torch.from_numpy(v).to(
+        torch.float32 if n == "bias" else wdt).cuda()) for n, v in arrays.items()}
+    d = moe.dims(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.I_shared, cfg.dtype)
+    ws_bytes = moe.moe_workspace_bytes(d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(cfg.T, cfg.d, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    n_ev = 6
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+              for _ in range(args.steps)]
+    for step_ev in events:
+        for e in step_ev:
+            e.record(stream)  # creates the underlying hipEvent_t
+
+    def step(ev):
+        moe.moe_layer_fwd_timed(d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
+                                dev["w_down"], dev["wsh_gate"], dev["wsh_up"], dev["wsh_down"], out,
+                                None, None, None, None, None, ws, ws_bytes,
+                                [e.cuda_event for e in ev], stream)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(events[0])
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_ms = {s: 0.0 for s in STAGES}
+    for ev in events:
+        for j, s in enumerate(STAGES):
+            stage_ms[s] += ev[j].elapsed_time(ev[j + 1]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = cfg.T / (wall / args.steps)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    fl_gu, fl_dn = gemm_flops(cfg)
+    gu_s, dn_s = stage_ms["gate_up"] * 1e-3, stage_ms["down"] * 1e-3
+    gu_tflops = fl_gu / gu_s / 1e12
+    gemm_tflops = (fl_gu + fl_dn) / (gu_s + dn_s) / 1e12
+    sb = stage_bytes(cfg)
+    hbm = {s: {"GB/s": round(sb[s] / (stage_ms[s] * 1e-3) / 1e9, 1),
+               "frac_of_8TB/s": round(sb[s] / (stage_ms[s] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+               "bytes": sb[s]} for s in sb}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k,
+                   "I": cfg.I, "n_shared": cfg.n_shared, "I_shared": cfg.I_shared,
+                   "router_bias": cfg.bias, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "gate_up_bf16_kernel",
+                     "achieved": round(gu_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": fl_gu, "avg_launch_ms": round(stage_ms["gate_up"], 4)},
+        "grouped_gemm": {"tflops": round(gemm_tflops, 1),
+                         "frac_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                         "down_tflops": round(fl_dn / dn_s / 1e12, 1)},
+        "stages_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "hbm": hbm,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host cores", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, arrays)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,54 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Rows per M-tile of both grouped GEMMs; the dispatch scan builds the
+// per-expert M-tile prefix table in units of this.
+constexpr int kBM = 128;
+// Assignments handled per block of the dispatch count/rank kernels (minimum).
+constexpr int kDispatchChunk = 1024;
+// Tokens per block of the router.
+constexpr int kRouteTokens = 16;
+// Top-k upper limit.
+constexpr int kMaxK = 16;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(uint32_t(h) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ u32x4 ld_u32x4(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// D = A(16x32) * B(32x16) + C on the bf16 matrix cores.  Lane l supplies row
+// (l % 16) of A and column (l % 16) of B, each with the 8 K-elements of group
+// (l / 16); D comes back with column (l % 16), rows 4*(l/16) + 0..3.
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_times(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+}  // namespace moe

@@ -1,0 +1,202 @@
+// Dispatch of the MoE layer on one GPU: every (token, slot) assignment gets a
+// row in a per-expert contiguous segment, and the token rows are copied there.
+//
+// On the pages Dispatch is the all-to-all that sends each token to the device
+// holding its expert (FarSkip-Collective review, "Core claim" and Fig. 11
+// caption; the Luffy review, "Core claim", on dispatch and combine traffic).
+// On one GPU's share it is a stable counting sort by expert plus a row gather.
+// The order inside a segment (ascending assignment index t*k + j) is a
+// reading; the pages do not fix it.
+//
+// Four kernels, no atomics on results and no host round trip:
+//   count:  per block of `chunk` assignments, an LDS histogram of expert ids
+//   scan:   one block; per expert, an exclusive scan over the blocks (block
+//           bases), then exclusive scans over experts of the counts
+//           (offsets) and of the M-tiles per expert (tile table of the GEMMs)
+//   rank:   per block, its chunk in order, 256 assignments at a time: the
+//           stable rank within a wave from 8 ballots on the id bits, across
+//           waves from LDS counts; writes perm and inv_perm
+//   gather: one wave per sorted row, 16-byte vector copies of the token row
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+int dispatch_chunk(int64_t R) {
+  // at most 256 blocks, so the per-expert scan over blocks stays short
+  int64_t c = (R + 255) / 256;
+  c = (c + 255) / 256 * 256;
+  return (int)(c < kDispatchChunk ? kDispatchChunk : c);
+}
+
+int dispatch_blocks(int64_t R) {
+  const int64_t c = dispatch_chunk(R);
+  return (int)((R + c - 1) / c);
+}
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ ids,
+                                                             int R, int E, int chunk,
+                                                             int32_t* __restrict__ blk) {
+  __shared__ int h[256];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * chunk, a1 = min(R, a0 + chunk);
+  for (int a = a0 + threadIdx.x; a < a1; a += 256) {
+    const int e = ids[a];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) blk[(size_t)blockIdx.x * E + e] = h[e];
+}
+
+// Inclusive scan of one value per thread over a 256-thread block.
+__device__ __forceinline__ int block_inclusive_scan(int v, int* buf) {
+  buf[threadIdx.x] = v;
+  __syncthreads();
+#pragma unroll
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+    __syncthreads();
+    buf[threadIdx.x] += add;
+    __syncthreads();
+  }
+  return buf[threadIdx.x];
+}
+
+// Per-expert counts -> offsets [E+1] and the M-tile prefix [E+1].
+__device__ __forceinline__ void write_offsets(int cnt, int E, int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ tile_off, int* buf) {
+  const int e = threadIdx.x;
+  const int tiles = (cnt + kBM - 1) / kBM;
+  const int incl = block_inclusive_scan(cnt, buf);
+  if (e < E) offsets[e] = incl - cnt;
+  if (e == E - 1) offsets[E] = incl;
+  __syncthreads();
+  const int tincl = block_inclusive_scan(tiles, buf);
+  if (tile_off) {
+    if (e < E) tile_off[e] = tincl - tiles;
+    if (e == E - 1) tile_off[E] = tincl;
+  }
+}
+
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ blk, int nblk,
+                                                            int E, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ tile_off) {
+  __shared__ int buf[256];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    int b = 0;
+    for (; b + 4 <= nblk; b += 4) {  // four independent loads in flight
+      const int c0 = blk[(size_t)(b + 0) * E + e], c1 = blk[(size_t)(b + 1) * E + e];
+      const int c2 = blk[(size_t)(b + 2) * E + e], c3 = blk[(size_t)(b + 3) * E + e];
+      blk[(size_t)(b + 0) * E + e] = run;
+      blk[(size_t)(b + 1) * E + e] = run + c0;
+      blk[(size_t)(b + 2) * E + e] = run + c0 + c1;
+      blk[(size_t)(b + 3) * E + e] = run + c0 + c1 + c2;
+      run += c0 + c1 + c2 + c3;
+    }
+    for (; b < nblk; ++b) {
+      const int c = blk[(size_t)b * E + e];
+      blk[(size_t)b * E + e] = run;
+      run += c;
+    }
+    if (counts) counts[e] = run;
+  }
+  write_offsets(e < E ? run : 0, E, offsets, tile_off, buf);
+}
+
+__global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
+                                                         int E, int32_t* __restrict__ tile_off) {
+  __shared__ int buf[256];
+  const int e = threadIdx.x;
+  const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int tiles = (cnt + kBM - 1) / kBM;
+  const int tincl = block_inclusive_scan(tiles, buf);
+  if (e < E) tile_off[e] = tincl - tiles;
+  if (e == E - 1) tile_off[E] = tincl;
+}
+
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int chunk, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+  __shared__ int run[256];     // next free row per expert for this block
+  __shared__ int wc[4][256];   // per-wave counts of the current 256 assignments
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int a0 = blockIdx.x * chunk, a1 = min(R, a0 + chunk);
+  for (int e = tid; e < E; e += 256) run[e] = offsets[e] + base[(size_t)blockIdx.x * E + e];
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int p = a0; p < a1; p += 256) {
+    for (int i = tid; i < 4 * 256; i += 256) (&wc[0][0])[i] = 0;
+    __syncthreads();
+    const int a = p + tid;
+    const int e = a < a1 ? ids[a] : -1;
+    const bool ok = (unsigned)e < (unsigned)E;
+    uint64_t peers = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = ok && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    if (ok && rank == 0) wc[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (ok) {
+      int dest = run[e] + rank;
+      for (int w = 0; w < wave; ++w) dest += wc[w][e];
+      perm[dest] = a;
+      inv_perm[a] = dest;
+    }
+    __syncthreads();
+    for (int e2 = tid; e2 < E; e2 += 256)
+      run[e2] += wc[0][e2] + wc[1][e2] + wc[2][e2] + wc[3][e2];
+    __syncthreads();
+  }
+}
+
+// x_sorted[i] = x[perm[i] / k], one wave per row, 16-byte vectors.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ x,
+                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ total_ptr,
+                                                          int k, int T, int vec_per_row,
+                                                          u32x4* __restrict__ xs) {
+  const int total = *total_ptr;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = blockIdx.x * 4 + wave; i < total; i += gridDim.x * 4) {
+    const int tok = perm[i] / k;
+    if ((unsigned)tok >= (unsigned)T) continue;
+    const u32x4* src = x + (size_t)tok * vec_per_row;
+    u32x4* dst = xs + (size_t)i * vec_per_row;
+    for (int c = lane; c < vec_per_row; c += 64) dst[c] = src[c];
+  }
+}
+
+void launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
+  const int64_t R = a.T * a.k;
+  const int chunk = dispatch_chunk(R);
+  const int nblk = dispatch_blocks(R);
+  const dim3 block(256);
+  if (nblk > 0)
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), block, 0, stream, a.ids, (int)R, a.E,
+                       chunk, a.blk);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), block, 0, stream, a.blk, nblk, a.E, a.counts,
+                     a.offsets, a.tile_off);
+  if (nblk == 0) return;
+  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nblk), block, 0, stream, a.ids, (int)R, a.E, chunk,
+                     a.offsets, a.blk, a.perm, a.inv_perm);
+  if (a.x_sorted) {
+    const int vec = (int)((size_t)a.d * a.elem_bytes / 16);
+    const int64_t grid = (R + 3) / 4;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)grid), block, 0, stream,
+                       static_cast<const u32x4*>(a.x), a.perm, a.offsets + a.E, a.k, (int)a.T, vec,
+                       static_cast<u32x4*>(a.x_sorted));
+  }
+}
+
+void launch_tile_table(const int32_t* offsets, int E, int32_t* tile_off, hipStream_t stream) {
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(256), 0, stream, offsets, E, tile_off);
+}
+
+}  // namespace moe

@@ -1,0 +1,367 @@
+// C ABI of the MoE-layer forward pass: argument validation, workspace
+// carving and launch sequencing on the caller's stream.  Declarations and
+// the contract of every entry point are in include/moe.h.
+#include <initializer_list>
+
+#include "moe.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr int64_t kI32Limit = int64_t(1) << 31;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t elem_bytes(const moe_dims_t& D) { return D.dtype == MOE_BF16 ? 2 : 4; }
+
+// Workspace layout.  The grouped FFN's SwiGLU products come first (the
+// documented contents of the workspace after moe_grouped_ffn).
+struct Layout {
+  size_t a, ash, tile_off, blk, ids, wts, counts, offsets, perm, inv, xs, y, ysh, total;
+};
+
+Layout layout_of(const moe_dims_t& D) {
+  const size_t es = elem_bytes(D);
+  const size_t T = (size_t)D.T, R = T * (size_t)D.k, E = (size_t)D.E;
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.a = take(R * D.I * es);
+  L.ash = take(T * (size_t)D.n_shared * D.I_shared * es);
+  L.tile_off = take((E + 1) * 4);
+  L.blk = take((size_t)dispatch_blocks((int64_t)R) * E * 4);
+  L.ids = take(R * 4);
+  L.wts = take(R * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(R * 4);
+  L.inv = take(R * 4);
+  L.xs = take(R * D.d * es);
+  L.y = take(R * D.d * 4);
+  L.ysh = take(D.n_shared ? T * D.d * 4 : 0);
+  L.total = o;
+  return L;
+}
+
+FfnArgs ffn_shape(const moe_dims_t& D) {
+  FfnArgs f = {};
+  f.T = D.T;
+  f.R = D.T * D.k;
+  f.d = D.d;
+  f.E = D.E;
+  f.I = D.I;
+  f.ns = D.n_shared;
+  f.Is = D.I_shared;
+  f.bf16 = D.dtype == MOE_BF16;
+  return f;
+}
+
+moe_status_t check_dims(const moe_dims_t* D) {
+  if (!D) return MOE_ERR_INVALID_ARG;
+  if (D->T < 0 || D->d <= 0 || D->E <= 0 || D->k <= 0 || D->I <= 0 || D->n_shared < 0 ||
+      D->I_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if ((D->n_shared == 0) != (D->I_shared == 0)) return MOE_ERR_INVALID_ARG;
+  if (D->dtype != MOE_F32 && D->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (D->E > 256 || D->k > D->E || D->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (D->d % 64 || D->I % 64 || D->I_shared % 64) return MOE_ERR_UNSUPPORTED;
+  if (D->T * (int64_t)D->k >= kI32Limit) return MOE_ERR_UNSUPPORTED;
+  const FfnArgs f = ffn_shape(*D);
+  if (gate_up_grid(f) >= kI32Limit || down_grid(f) >= kI32Limit) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)D->n_shared * D->I_shared >= kI32Limit) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+  bool required;
+  bool output;
+};
+
+// Presence, 16-byte alignment, and no overlap of an output with any other buffer.
+moe_status_t check_bufs(std::initializer_list<Buf> bufs) {
+  for (const Buf& b : bufs) {
+    if (b.bytes == 0) continue;
+    if (!b.p) {
+      if (b.required) return MOE_ERR_INVALID_ARG;
+      continue;
+    }
+    if (reinterpret_cast<uintptr_t>(b.p) & 15u) return MOE_ERR_INVALID_ARG;
+  }
+  for (const Buf* i = bufs.begin(); i != bufs.end(); ++i) {
+    if (!i->p || !i->bytes) continue;
+    for (const Buf* j = i + 1; j != bufs.end(); ++j) {
+      if (!j->p || !j->bytes || !(i->output || j->output)) continue;
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(i->p), a1 = a0 + i->bytes;
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(j->p), b1 = b0 + j->bytes;
+      if (a0 < b1 && b0 < a1) return MOE_ERR_INVALID_ARG;
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status_t launched() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<uint8_t*>(ws) + off);
+}
+
+moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_router,
+                       const float* bias, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* wsh_gate, const void* wsh_up,
+                       const void* wsh_down, float* out, int32_t* topk_ids_out,
+                       float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                       int32_t* perm_out, void* ws, size_t ws_bytes, hipEvent_t* events,
+                       int n_events, hipStream_t stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims_t& D = *dims;
+  if (n_events < 0 || n_events > 6 || (n_events > 0 && !events)) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(D);
+  const size_t es = elem_bytes(D);
+  const size_t T = (size_t)D.T, R = T * D.k, E = D.E, d = D.d;
+  const bool sh = D.n_shared > 0;
+  const size_t wsh_in = (size_t)D.n_shared * D.I_shared * d * es;
+  st = check_bufs({{x, T * d * es, true, false},
+                   {w_router, E * d * es, true, false},
+                   {bias, E * 4, false, false},
+                   {w_gate, E * D.I * d * es, true, false},
+                   {w_up, E * D.I * d * es, true, false},
+                   {w_down, E * D.I * d * es, true, false},
+                   {wsh_gate, wsh_in, sh, false},
+                   {wsh_up, wsh_in, sh, false},
+                   {wsh_down, wsh_in, sh, false},
+                   {out, T * d * 4, true, true},
+                   {topk_ids_out, R * 4, false, true},
+                   {topk_w_out, R * 4, false, true},
+                   {counts_out, E * 4, false, true},
+                   {offsets_out, (E + 1) * 4, false, true},
+                   {perm_out, R * 4, false, true},
+                   {ws, L.total, true, true}});
+  if (st != MOE_OK) return st;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  (void)hipGetLastError();
+  auto mark = [&](int i) -> bool {
+    return i >= n_events || hipEventRecord(events[i], stream) == hipSuccess;
+  };
+  if (!mark(0)) return MOE_ERR_HIP;
+
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+  float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.wts);
+  int32_t* counts = counts_out ? counts_out : at<int32_t>(ws, L.counts);
+  int32_t* offsets = offsets_out ? offsets_out : at<int32_t>(ws, L.offsets);
+  int32_t* perm = perm_out ? perm_out : at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+
+  RouteArgs ra = {x, w_router, bias, nullptr, nullptr, ids, wts, D.T, D.d, D.E, D.k,
+                  D.dtype == MOE_BF16};
+  launch_route(ra, stream);
+  if (!mark(1)) return MOE_ERR_HIP;
+
+  DispatchArgs da = {x, ids, counts, offsets, at<int32_t>(ws, L.tile_off), perm, inv,
+                     at<void>(ws, L.xs), at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k, (int)es};
+  launch_dispatch(da, stream);
+  if (!mark(2)) return MOE_ERR_HIP;
+
+  FfnArgs fa = ffn_shape(D);
+  fa.xs = at<void>(ws, L.xs);
+  fa.x = x;
+  fa.wg = w_gate;
+  fa.wu = w_up;
+  fa.wd = w_down;
+  fa.wsg = wsh_gate;
+  fa.wsu = wsh_up;
+  fa.wsd = wsh_down;
+  fa.offsets = offsets;
+  fa.tile_off = at<int32_t>(ws, L.tile_off);
+  fa.a = at<void>(ws, L.a);
+  fa.ash = at<void>(ws, L.ash);
+  fa.y = at<float>(ws, L.y);
+  fa.ysh = sh ? at<float>(ws, L.ysh) : nullptr;
+  launch_gate_up(fa, stream);
+  if (!mark(3)) return MOE_ERR_HIP;
+  launch_down(fa, stream);
+  if (!mark(4)) return MOE_ERR_HIP;
+
+  CombineArgs ca = {fa.y, inv, wts, fa.ysh, out, D.T, D.d, D.k};
+  launch_combine(ca, stream);
+  if (!mark(5)) return MOE_ERR_HIP;
+  return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_dims_t* dims) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  return layout_of(*dims).total;
+}
+
+const char* moe_status_str(moe_status_t status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null, misaligned or overlapping buffer, or invalid size";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: sizes outside the supported limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_bytes()";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown moe_status_t";
+}
+
+moe_status_t moe_route(const moe_dims_t* dims, const void* x, const void* w_router,
+                       const float* bias, const float* logits_in, float* logits_out,
+                       int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims_t& D = *dims;
+  const size_t es = elem_bytes(D), T = (size_t)D.T, E = D.E, d = D.d;
+  const bool computed = logits_in == nullptr;
+  st = check_bufs({{x, T * d * es, computed, false},
+                   {w_router, E * d * es, computed, false},
+                   {bias, E * 4, false, false},
+                   {logits_in, T * E * 4, false, false},
+                   {logits_out, T * E * 4, false, true},
+                   {topk_ids, T * D.k * 4, true, true},
+                   {topk_w, T * D.k * 4, true, true}});
+  if (st != MOE_OK) return st;
+  if (D.T == 0) return MOE_OK;
+  (void)hipGetLastError();
+  RouteArgs ra = {x, w_router, bias, logits_in, logits_out, topk_ids, topk_w, D.T, D.d, D.E, D.k,
+                  D.dtype == MOE_BF16};
+  launch_route(ra, stream);
+  return launched();
+}
+
+moe_status_t moe_dispatch(const moe_dims_t* dims, const void* x, const int32_t* topk_ids,
+                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                          void* x_sorted, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims_t& D = *dims;
+  const Layout L = layout_of(D);
+  const size_t es = elem_bytes(D), T = (size_t)D.T, R = T * D.k, E = D.E, d = D.d;
+  st = check_bufs({{x, T * d * es, true, false},
+                   {topk_ids, R * 4, true, false},
+                   {counts, E * 4, true, true},
+                   {offsets, (E + 1) * 4, true, true},
+                   {perm, R * 4, true, true},
+                   {inv_perm, R * 4, true, true},
+                   {x_sorted, R * d * es, true, true},
+                   {ws, L.total, true, true}});
+  if (st != MOE_OK) return st;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  DispatchArgs da = {x, topk_ids, counts, offsets, nullptr, perm, inv_perm, x_sorted,
+                     at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k, (int)es};
+  launch_dispatch(da, stream);
+  return launched();
+}
+
+moe_status_t moe_grouped_ffn(const moe_dims_t* dims, const void* x_sorted, const int32_t* offsets,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* x, const void* wsh_gate, const void* wsh_up,
+                             const void* wsh_down, float* y_sorted, float* y_shared, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims_t& D = *dims;
+  const Layout L = layout_of(D);
+  const size_t es = elem_bytes(D), T = (size_t)D.T, R = T * D.k, E = D.E, d = D.d;
+  const bool sh = D.n_shared > 0;
+  const size_t wsh_in = (size_t)D.n_shared * D.I_shared * d * es;
+  st = check_bufs({{x_sorted, R * d * es, true, false},
+                   {offsets, (E + 1) * 4, true, false},
+                   {w_gate, E * D.I * d * es, true, false},
+                   {w_up, E * D.I * d * es, true, false},
+                   {w_down, E * D.I * d * es, true, false},
+                   {x, sh ? T * d * es : 0, sh, false},
+                   {wsh_gate, wsh_in, sh, false},
+                   {wsh_up, wsh_in, sh, false},
+                   {wsh_down, wsh_in, sh, false},
+                   {y_sorted, R * d * 4, true, true},
+                   {y_shared, sh ? T * d * 4 : 0, sh, true},
+                   {ws, L.total, true, true}});
+  if (st != MOE_OK) return st;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (D.T == 0) return MOE_OK;
+  (void)hipGetLastError();
+  FfnArgs fa = ffn_shape(D);
+  fa.xs = x_sorted;
+  fa.x = x;
+  fa.wg = w_gate;
+  fa.wu = w_up;
+  fa.wd = w_down;
+  fa.wsg = wsh_gate;
+  fa.wsu = wsh_up;
+  fa.wsd = wsh_down;
+  fa.offsets = offsets;
+  fa.tile_off = at<int32_t>(ws, L.tile_off);
+  fa.a = at<void>(ws, L.a);
+  fa.ash = at<void>(ws, L.ash);
+  fa.y = y_sorted;
+  fa.ysh = sh ? y_shared : nullptr;
+  launch_tile_table(offsets, D.E, at<int32_t>(ws, L.tile_off), stream);
+  launch_gate_up(fa, stream);
+  launch_down(fa, stream);
+  return launched();
+}
+
+moe_status_t moe_combine(const moe_dims_t* dims, const float* y_sorted, const int32_t* inv_perm,
+                         const float* topk_w, const float* y_shared, float* out,
+                         hipStream_t stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims_t& D = *dims;
+  const size_t T = (size_t)D.T, R = T * D.k, d = D.d;
+  st = check_bufs({{y_sorted, R * d * 4, true, false},
+                   {inv_perm, R * 4, true, false},
+                   {topk_w, R * 4, true, false},
+                   {y_shared, T * d * 4, false, false},
+                   {out, T * d * 4, true, true}});
+  if (st != MOE_OK) return st;
+  if (D.T == 0) return MOE_OK;
+  (void)hipGetLastError();
+  CombineArgs ca = {y_sorted, inv_perm, topk_w, y_shared, out, D.T, D.d, D.k};
+  launch_combine(ca, stream);
+  return launched();
+}
+
+moe_status_t moe_layer_fwd(const moe_dims_t* dims, const void* x, const void* w_router,
+                           const float* bias, const void* w_gate, const void* w_up,
+                           const void* w_down, const void* wsh_gate, const void* wsh_up,
+                           const void* wsh_down, float* out, int32_t* topk_ids_out,
+                           float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                           int32_t* perm_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return layer_fwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down, out,
+                   topk_ids_out, topk_w_out, counts_out, offsets_out, perm_out, ws, ws_bytes,
+                   nullptr, 0, stream);
+}
+
+moe_status_t moe_layer_fwd_timed(const moe_dims_t* dims, const void* x, const void* w_router,
+                                 const float* bias, const void* w_gate, const void* w_up,
+                                 const void* w_down, const void* wsh_gate, const void* wsh_up,
+                                 const void* wsh_down, float* out, int32_t* topk_ids_out,
+                                 float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                                 int32_t* perm_out, void* ws, size_t ws_bytes,
+                                 hipEvent_t* events, int n_events, hipStream_t stream) {
+  return layer_fwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down, out,
+                   topk_ids_out, topk_w_out, counts_out, offsets_out, perm_out, ws, ws_bytes,
+                   events, n_events, stream);
+}
+
+}  // extern "C"

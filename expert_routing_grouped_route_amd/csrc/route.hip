@@ -1,0 +1,235 @@
+// Gate of the MoE layer: router logits, top-k with lowest-index tie-break,
+// renormalised softmax weights.
+//
+// Top-k routing over the router's scores is the gate the expert-prototyping
+// abstract of the "Daily Papers" search page speaks of ("k ... in top-k
+// routing"); it is the T_gate term of the overlap window in the
+// FarSkip-Collective review (axiom ledger, Eq. 9).  Softmax, renormalisation
+// over the kept k and the tie rule are readings: the pages name none of them.
+//
+// One block handles 16 tokens.  bf16 logits run on the matrix cores: the four
+// waves split the hidden dimension (K-steps of 32 taken round-robin), each
+// wave holding 16 tokens x E experts of fp32 partial sums; the partials meet
+// in LDS in a fixed order.  fp32 logits run on the vector ALUs in a fixed
+// lane order.  Then each wave takes the top-k of 4 tokens, one wave-wide
+// arg-max per slot.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Top-k of one token whose E logits sit in LDS at `L`.  All 64 lanes take
+// part; lane j < k writes slot j.
+__device__ __forceinline__ void topk_one_token(const float* L, int E, int k, int lane,
+                                               int32_t* __restrict__ ids_out,
+                                               float* __restrict__ w_out) {
+  constexpr int NV = 4;  // E <= 256 = 4 * 64 logits per token
+  float v[NV];
+  bool live[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    live[i] = e < E;
+    v[i] = live[i] ? L[e] : 0.0f;
+  }
+  float selv[kMaxK];
+  int seli[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    selv[j] = 0.0f;
+    seli[j] = 0;
+    if (j < k) {
+      float bv = 0.0f;
+      int bi = 0x7fffffff;  // none yet
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        // within a lane the index grows with i, so a strict '>' keeps the
+        // lowest index among equal values
+        if (live[i] && (bi == 0x7fffffff || v[i] > bv)) {
+          bv = v[i];
+          bi = lane + 64 * i;
+        }
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(bv, m);
+        const int oi = __shfl_xor(bi, m);
+        const bool take = oi != 0x7fffffff &&
+                          (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
+        if (take) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      selv[j] = bv;
+      seli[j] = bi;
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (bi == lane + 64 * i) live[i] = false;
+    }
+  }
+  // w_j = exp(L_j - L_0) / sum_j' exp(L_j' - L_0): the softmax over all E
+  // restricted to the kept k and renormalised (the full denominator cancels).
+  float z[kMaxK];
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    z[j] = 0.0f;
+    if (j < k) {
+      z[j] = expf(selv[j] - selv[0]);
+      s += z[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k && lane == j) {
+      ids_out[j] = seli[j];
+      w_out[j] = z[j] / s;
+    }
+  }
+}
+
+// Logits of 16 tokens x E experts, bf16 in, fp32 accumulate on the matrix cores.
+template <int NET>  // 16-expert column tiles: E <= 16 * NET
+__global__ __launch_bounds__(256) void route_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int d, int E, int k,
+    float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ wts) {
+  constexpr int EP = NET * 16 + 1;
+  __shared__ float part[4][kRouteTokens][EP];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * kRouteTokens;
+  const int r = lane & 15, kq = (lane >> 4) * 8;
+  // rows past T and experts past E read a valid row; their results are dropped
+  const uint16_t* xp = x + (size_t)min(t0 + r, T - 1) * d + kq;
+  const uint16_t* wp[NET];
+#pragma unroll
+  for (int et = 0; et < NET; ++et) wp[et] = wr + (size_t)min(et * 16 + r, E - 1) * d + kq;
+
+  f32x4 acc[NET];
+#pragma unroll
+  for (int et = 0; et < NET; ++et) acc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nks = d >> 5;
+  for (int s = wave; s < nks; s += 4) {
+    const bf16x8 a = as_bf16x8(ld_u32x4(xp + s * 32));
+#pragma unroll
+    for (int et = 0; et < NET; ++et) {
+      const bf16x8 b = as_bf16x8(ld_u32x4(wp[et] + s * 32));
+      acc[et] = mfma_16x16x32_bf16(a, b, acc[et]);
+    }
+  }
+#pragma unroll
+  for (int et = 0; et < NET; ++et)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) part[wave][(lane >> 4) * 4 + q][et * 16 + r] = acc[et][q];
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < kRouteTokens * E; idx += 256) {
+    const int t = idx / E, e = idx - t * E;
+    float v = ((part[0][t][e] + part[1][t][e]) + part[2][t][e]) + part[3][t][e];
+    if (bias) v += bias[e];
+    part[0][t][e] = v;
+    if (logits_out && t0 + t < T) logits_out[(size_t)(t0 + t) * E + e] = v;
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int q = 0; q < 4; ++q) {
+    const int t = wave * 4 + q;
+    if (t0 + t < T)
+      topk_one_token(&part[0][t][0], E, k, lane, ids + (size_t)(t0 + t) * k,
+                     wts + (size_t)(t0 + t) * k);
+  }
+}
+
+// fp32 logits on the vector ALUs in a fixed order: lane l sums the rounded
+// products of i = l, l+64, ... in ascending i (no fused multiply-add), a xor
+// butterfly over 32..1 combines the 64 partials, then the bias is added.
+__global__ __launch_bounds__(256) void route_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    int T, int d, int E, int k, float* __restrict__ logits_out, int32_t* __restrict__ ids,
+    float* __restrict__ wts) {
+  __shared__ float Ls[kRouteTokens][257];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * kRouteTokens;
+#pragma unroll 1
+  for (int q = 0; q < 4; ++q) {
+    const int t = t0 + wave * 4 + q;
+    if (t >= T) break;
+    const float* xr = x + (size_t)t * d;
+#pragma unroll 1
+    for (int e = 0; e < E; ++e) {
+      const float* w = wr + (size_t)e * d;
+      float s = 0.0f;
+      for (int i = lane; i < d; i += 64) s = __fadd_rn(s, __fmul_rn(xr[i], w[i]));
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) s = __fadd_rn(s, __shfl_xor(s, m));
+      if (bias) s = __fadd_rn(s, bias[e]);
+      if (lane == 0) Ls[wave * 4 + q][e] = s;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kRouteTokens * E; idx += 256) {
+    const int t = idx / E, e = idx - t * E;
+    if (logits_out && t0 + t < T) logits_out[(size_t)(t0 + t) * E + e] = Ls[t][e];
+  }
+#pragma unroll 1
+  for (int q = 0; q < 4; ++q) {
+    const int t = wave * 4 + q;
+    if (t0 + t < T)
+      topk_one_token(&Ls[t][0], E, k, lane, ids + (size_t)(t0 + t) * k, wts + (size_t)(t0 + t) * k);
+  }
+}
+
+// Top-k on logits given from outside.
+__global__ __launch_bounds__(256) void route_from_logits_kernel(
+    const float* __restrict__ logits_in, int T, int E, int k, float* __restrict__ logits_out,
+    int32_t* __restrict__ ids, float* __restrict__ wts) {
+  __shared__ float Ls[kRouteTokens][257];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * kRouteTokens;
+  for (int idx = threadIdx.x; idx < kRouteTokens * E; idx += 256) {
+    const int t = idx / E, e = idx - t * E;
+    if (t0 + t < T) {
+      const float v = logits_in[(size_t)(t0 + t) * E + e];
+      Ls[t][e] = v;
+      if (logits_out) logits_out[(size_t)(t0 + t) * E + e] = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int q = 0; q < 4; ++q) {
+    const int t = wave * 4 + q;
+    if (t0 + t < T)
+      topk_one_token(&Ls[t][0], E, k, lane, ids + (size_t)(t0 + t) * k, wts + (size_t)(t0 + t) * k);
+  }
+}
+
+void launch_route(const RouteArgs& a, hipStream_t stream) {
+  const int grid = (int)((a.T + kRouteTokens - 1) / kRouteTokens);
+  if (grid == 0) return;
+  const dim3 block(256);
+  if (a.logits_in) {
+    hipLaunchKernelGGL(route_from_logits_kernel, dim3(grid), block, 0, stream, a.logits_in,
+                       (int)a.T, a.E, a.k, a.logits_out, a.ids, a.wts);
+    return;
+  }
+  if (!a.bf16) {
+    hipLaunchKernelGGL(route_f32_kernel, dim3(grid), block, 0, stream,
+                       static_cast<const float*>(a.x), static_cast<const float*>(a.wr), a.bias,
+                       (int)a.T, a.d, a.E, a.k, a.logits_out, a.ids, a.wts);
+    return;
+  }
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
+#define MOE_ROUTE_CASE(N)                                                                   \
+  hipLaunchKernelGGL(route_bf16_kernel<N>, dim3(grid), block, 0, stream, x, wr, a.bias,      \
+                     (int)a.T, a.d, a.E, a.k, a.logits_out, a.ids, a.wts)
+  if (a.E <= 16) MOE_ROUTE_CASE(1);
+  else if (a.E <= 32) MOE_ROUTE_CASE(2);
+  else if (a.E <= 64) MOE_ROUTE_CASE(4);
+  else if (a.E <= 128) MOE_ROUTE_CASE(8);
+  else MOE_ROUTE_CASE(16);
+#undef MOE_ROUTE_CASE
+}
+
+}  // namespace moe

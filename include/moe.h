@@ -1,0 +1,177 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) Mixture-of-Experts layer forward pass.
+ *
+ * One MoE layer on one GPU's share of T tokens: a top-k softmax gate, Dispatch
+ * of every (token, slot) assignment into per-expert contiguous rows, the
+ * routed SwiGLU experts run as a grouped GEMM, optional always-on shared
+ * experts, and Combine back to token order.  The operator chain is the MoE
+ * sub-block of the FarSkip-Collective review ("Core claim"; Fig. 2 caption,
+ * "MoE layer main operator execution"; Fig. 11 caption: Dispatch, routed
+ * experts, Combine, shared expert).  Top-k routing is the gate of the
+ * expert-prototyping abstract on the "Daily Papers" search page; running each
+ * expert as one dense product over its grouped tokens is the "Expert-Centric
+ * Scheduling" of the OmniMoE abstract on that page.  The layer's formulas are
+ * not written on the pages; the readings used here are:
+ *
+ *   L[t,e]   = sum_i x[t,i] * w_router[e,i] + bias[e]            (fp32)
+ *   ids[t,j] = expert with the (j+1)-th largest L[t,.]; equal logits go to
+ *              the lower expert index
+ *   w[t,j]   = exp(L[t,ids[t,j]] - L[t,ids[t,0]]) / sum_j' (same)
+ *              (= softmax over all E restricted to the top k, renormalised)
+ *   rows of expert e: assignments a = t*k + j with ids[t,j] == e, ascending a
+ *   A        = bf16(silu(X Wg^T) * (X Wu^T)), silu(z) = z / (1 + e^-z)
+ *              (fp32 workloads keep A in fp32)
+ *   y        = A Wd^T                                              (fp32)
+ *   shared   = sum_s  bf16(silu(x Wsg_s^T) * (x Wsu_s^T)) Wsd_s^T  (fp32)
+ *   out[t]   = sum_j w[t,j] * y[row of (t,j)] + shared[t]         (fp32)
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * Layouts: row-major, reduction dimension contiguous.
+ *   x [T,d]; w_router [E,d]; bias [E] (fp32);
+ *   w_gate, w_up [E,I,d]; w_down [E,d,I];
+ *   wsh_gate, wsh_up [n_shared,I_shared,d]; wsh_down [n_shared,d,I_shared].
+ *   dims.dtype gives the element type of x and of every weight tensor
+ *   (MOE_BF16: bfloat16, MOE_F32: float32).  Everything else is int32 or fp32.
+ * Ownership: the caller owns every buffer.  All pointers are device pointers,
+ *   16-byte aligned, and no output may overlap another buffer.  The library
+ *   allocates nothing and keeps no state; its entry points are re-entrant.
+ * Asynchrony: work is enqueued on `stream` (0 = the null stream).  No entry
+ *   point synchronises or copies device data to the host; MOE_OK means
+ *   "enqueued".
+ * Errors: arguments are validated on the host before anything is enqueued;
+ *   on a validation failure nothing is enqueued and no output is touched.
+ *   A failed launch returns MOE_ERR_HIP.  Limits: T >= 0 (with T == 0 only
+ *   the per-expert counts and offsets are written, as zeros, by moe_dispatch
+ *   and moe_layer_fwd); 1 <= k <= min(E, 16); E <= 256;
+ *   d % 64 == 0; I % 64 == 0; I_shared % 64 == 0; T*k < 2^31;
+ *   n_shared == 0 exactly when I_shared == 0.
+ *   Expert ids outside [0,E) given to moe_dispatch are skipped (the
+ *   assignment gets no row); results are then meaningless but every kernel
+ *   keeps its memory accesses in bounds.
+ * Determinism: no floating-point atomics; two calls on the same inputs give
+ *   bit-identical outputs.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null, misaligned or overlapping pointer; bad sizes */
+  MOE_ERR_UNSUPPORTED = 2, /* sizes outside the limits above */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes below moe_workspace_bytes() */
+  MOE_ERR_HIP = 4          /* a kernel launch failed */
+} moe_status_t;
+
+/* Sizes of one layer call: T tokens, hidden size d, E routed experts, top-k,
+ * expert intermediate size I, n_shared shared experts of intermediate size
+ * I_shared, element type of x and the weights. */
+typedef struct {
+  int64_t T;
+  int32_t d, E, k, I, n_shared, I_shared;
+  moe_dtype_t dtype;
+} moe_dims_t;
+
+/* Bytes of device workspace that moe_dispatch, moe_grouped_ffn and
+ * moe_layer_fwd need for `dims` (one size serves all three).  Returns 0 for
+ * invalid or unsupported dims. */
+MOE_API size_t moe_workspace_bytes(const moe_dims_t* dims);
+
+/* Static, never-NULL description of a status code. */
+MOE_API const char* moe_status_str(moe_status_t status);
+
+/* Gate: router logits, top-k ids and renormalised softmax weights.
+ *   x [T,d], w_router [E,d] (dtype); bias [E] fp32 or NULL.
+ *   logits_in [T,E] fp32 or NULL: when given, the top-k is taken on these
+ *     logits and x, w_router and bias are not read (may be NULL).
+ *   logits_out [T,E] fp32 or NULL: receives the logits the top-k used.
+ *   topk_ids [T,k] int32, topk_w [T,k] fp32: outputs, slot 0 = largest logit.
+ * bf16 logits: bf16 products accumulated in fp32 on the matrix cores.
+ * fp32 logits: per (t,e), 64 partial sums (partial l takes i = l, l+64, ... in
+ *   ascending i, separate multiply and add), a xor butterfly over 32,16,8,4,2,1,
+ *   then + bias; all in fp32 round-to-nearest. */
+MOE_API moe_status_t moe_route(const moe_dims_t* dims, const void* x, const void* w_router,
+                       const float* bias, const float* logits_in, float* logits_out,
+                       int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* Dispatch: group the R = T*k assignments a = t*k + j by expert, stably.
+ *   topk_ids [T,k] int32 in [0,E).
+ *   counts [E]: assignments per expert.  offsets [E+1]: exclusive prefix sum,
+ *   offsets[E] = R.  perm [R]: perm[i] = assignment at sorted row i.
+ *   inv_perm [R]: inv_perm[a] = sorted row of assignment a.
+ *   x_sorted [R,d] (dtype): x_sorted[i] = x[perm[i] / k].
+ *   ws: workspace of ws_bytes >= moe_workspace_bytes(dims). */
+MOE_API moe_status_t moe_dispatch(const moe_dims_t* dims, const void* x, const int32_t* topk_ids,
+                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                          void* x_sorted, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Routed experts as a grouped GEMM, plus the shared experts.
+ *   x_sorted [R,d] (dtype) and offsets [E+1] as produced by moe_dispatch.
+ *   w_gate, w_up [E,I,d], w_down [E,d,I] (dtype).
+ *   x [T,d] and wsh_* : shared experts; NULL when n_shared == 0.
+ *   y_sorted [R,d] fp32: y_sorted[i] = expert output of sorted row i.
+ *   y_shared [T,d] fp32: sum of the shared experts; NULL when n_shared == 0.
+ *   On return the workspace starts with A [R,I] followed by A_shared
+ *   [T, n_shared*I_shared], the SwiGLU products (bf16 for MOE_BF16, fp32 for
+ *   MOE_F32), each 256-byte aligned. */
+MOE_API moe_status_t moe_grouped_ffn(const moe_dims_t* dims, const void* x_sorted, const int32_t* offsets,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* x, const void* wsh_gate, const void* wsh_up,
+                             const void* wsh_down, float* y_sorted, float* y_shared,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Combine: out[t] = sum_{j<k} topk_w[t,j] * y_sorted[inv_perm[t*k+j]] (+ y_shared[t]),
+ * accumulated in fp32 in ascending j, shared term last.
+ *   y_sorted [R,d], inv_perm [R], topk_w [T,k], y_shared [T,d] or NULL, out [T,d]. */
+MOE_API moe_status_t moe_combine(const moe_dims_t* dims, const float* y_sorted, const int32_t* inv_perm,
+                         const float* topk_w, const float* y_shared, float* out,
+                         hipStream_t stream);
+
+/* The whole layer: route, dispatch, grouped FFN with shared experts, combine.
+ *   Inputs as above (wsh_* NULL when n_shared == 0); out [T,d] fp32.
+ *   topk_ids_out [T,k], topk_w_out [T,k], counts_out [E], offsets_out [E+1],
+ *   perm_out [R]: optional copies of the intermediate results (NULL = skip).
+ *   ws: workspace of ws_bytes >= moe_workspace_bytes(dims). */
+MOE_API moe_status_t moe_layer_fwd(const moe_dims_t* dims, const void* x, const void* w_router,
+                           const float* bias, const void* w_gate, const void* w_up,
+                           const void* w_down, const void* wsh_gate, const void* wsh_up,
+                           const void* wsh_down, float* out, int32_t* topk_ids_out,
+                           float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                           int32_t* perm_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_fwd that also records HIP events on `stream` at its stage
+ * boundaries, for per-stage timing.  events[0..n_events) are caller-created
+ * events; event i is recorded after stage i-1 when i < n_events:
+ *   0 start, 1 after route, 2 after dispatch (count, scan, rank, gather),
+ *   3 after gate/up GEMM, 4 after down GEMM, 5 after combine.
+ * n_events may be 0..6. */
+MOE_API moe_status_t moe_layer_fwd_timed(const moe_dims_t* dims, const void* x, const void* w_router,
+                                 const float* bias, const void* w_gate, const void* w_up,
+                                 const void* w_down, const void* wsh_gate, const void* wsh_up,
+                                 const void* wsh_down, float* out, int32_t* topk_ids_out,
+                                 float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                                 int32_t* perm_out, void* ws, size_t ws_bytes,
+                                 hipEvent_t* events, int n_events, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

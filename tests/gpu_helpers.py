@@ -1,0 +1,191 @@
+"""Helpers for the GPU parity tests: device buffers, calls through the C ABI
+binding, and the comparison rules.
+
+Comparison rules:
+  * integer results (ids, counts, offsets, perm, inv_perm) and copied rows
+    (x_sorted): bit-exact;
+  * gate weights from identical logits: max abs error <= 2e-6;
+  * floating outputs of bf16-in / fp32-accumulate kernels: mean |g - r| <=
+    1e-3 and max_i |g_i - r_i| / max(|r_i|, rms(r)) <= 2e-2 against the fp64
+    oracle;
+  * router logits computed on the GPU: within the float32 dot-product error
+    bound gamma_n * (|x| |W_r|^T) + u |b| + u |L| with u = 2^-24,
+    gamma_n = n u / (1 - n u), n = d + 5 (d products, 4 partial-sum merges,
+    the bias);  a token whose top-k differs from the oracle's must be a
+    certified near tie (two of its leading k+1 oracle logits closer than
+    twice that bound); any other difference fails.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import expert_routing_grouped_route_amd as moe
+
+U32 = 2.0 ** -24
+MEAN_ABS_TOL = 1e-3
+MAX_REL_TOL = 2e-2
+W_ABS_TOL = 2e-6
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.detach().cpu().numpy()
+
+
+def fp_errors(g, r):
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    if r.size == 0:
+        return 0.0, 0.0
+    diff = np.abs(g - r)
+    rms = float(np.sqrt(np.mean(r * r)))
+    floor = np.maximum(np.abs(r), rms if rms > 0 else 1.0)
+    return float(diff.mean()), float((diff / floor).max())
+
+
+def assert_fp_close(g, r, what="", mean_abs=MEAN_ABS_TOL, max_rel=MAX_REL_TOL):
+    ma, mr = fp_errors(g, r)
+    assert np.all(np.isfinite(np.asarray(g))), f"{what}: non-finite values"
+    assert ma <= mean_abs and mr <= max_rel, f"{what}: mean_abs={ma:.3e} max_rel={mr:.3e}"
+    return ma, mr
+
+
+def logits_bound(x, w_router, bias, L_ref):
+    d = x.shape[1]
+    n = d + 5
+    gamma = n * U32 / (1 - n * U32)
+    b = np.abs(np.asarray(bias, np.float64)) if bias is not None else 0.0
+    mag = np.abs(x).astype(np.float64) @ np.abs(w_router).astype(np.float64).T
+    return gamma * mag + U32 * b + U32 * np.abs(L_ref.astype(np.float64))
+
+
+def check_topk_of_own_logits(L, ids, k):
+    """The ids are the top-k of the given logits with the lower-index tie rule
+    (checked directly from the definition, per token)."""
+    T, E = L.shape
+    L = L.astype(np.float64)
+    ids = ids.astype(np.int64)
+    for t in range(T):
+        sel = ids[t]
+        assert len(set(sel.tolist())) == k, f"token {t}: repeated expert"
+        key = [(-L[t, e], e) for e in sel]
+        assert key == sorted(key), f"token {t}: slots not in descending order"
+        last = (-L[t, sel[-1]], sel[-1])
+        rest = np.setdiff1d(np.arange(E), sel)
+        for e in rest:
+            assert (-L[t, e], e) > last, f"token {t}: expert {e} should have been kept"
+
+
+def certify_routing(ids_gpu, ids_ref, L_ref, bound):
+    """Returns the tokens whose routing differs; fails on any that is not a
+    certified near tie of the oracle's logits."""
+    differ = np.nonzero(np.any(ids_gpu != ids_ref, axis=1))[0]
+    k = ids_ref.shape[1]
+    for t in differ:
+        row = L_ref[t].astype(np.float64)
+        order = np.argsort(-row, kind="stable")[: k + 1]
+        lead = row[order]
+        gaps = lead[:-1] - lead[1:] if lead.size > 1 else np.array([np.inf])
+        tol = 2.0 * bound[t].max()
+        assert gaps.min() <= tol, (
+            f"token {t}: routing {ids_gpu[t]} vs oracle {ids_ref[t]} with smallest gap "
+            f"{gaps.min():.3e} > certified tie bound {tol:.3e}")
+    return differ
+
+
+class Layer:
+    """Device copies of one workload's inputs and buffers for every entry point."""
+
+    def __init__(self, cfg, arrays):
+        self.cfg = cfg
+        self.a = arrays
+        self.dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.dims = moe.dims(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.I_shared, cfg.dtype)
+        self.t = {}
+        for name, arr in arrays.items():
+            if arr is None:
+                self.t[name] = None
+                continue
+            dt = torch.float32 if name == "bias" else self.dt
+            self.t[name] = torch.from_numpy(np.ascontiguousarray(arr)).to(dt).cuda()
+        self.ws_bytes = moe.moe_workspace_bytes(self.dims)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        self.R = cfg.T * cfg.k
+        self.es = 2 if cfg.dtype == "bf16" else 4
+
+    def _i32(self, *shape):
+        return torch.empty(shape, dtype=torch.int32, device="cuda")
+
+    def _f32(self, *shape):
+        return torch.empty(shape, dtype=torch.float32, device="cuda")
+
+    def layer(self, w_down_scale=None):
+        c, t = self.cfg, self.t
+        out = self._f32(c.T, c.d)
+        ids, w = self._i32(c.T, c.k), self._f32(c.T, c.k)
+        counts, offsets, perm = self._i32(c.E), self._i32(c.E + 1), self._i32(self.R)
+        wd, wsd = t["w_down"], t.get("wsh_down")
+        if w_down_scale is not None:
+            wd = wd * w_down_scale
+            wsd = wsd * w_down_scale if wsd is not None else None
+        moe.moe_layer_fwd(self.dims, t["x"], t["w_router"], t.get("bias"), t["w_gate"], t["w_up"],
+                          wd, t.get("wsh_gate"), t.get("wsh_up"), wsd, out, ids, w, counts,
+                          offsets, perm, self.ws, self.ws_bytes)
+        torch.cuda.synchronize()
+        return dict(out=to_np(out), ids=to_np(ids), w=to_np(w), counts=to_np(counts),
+                    offsets=to_np(offsets), perm=to_np(perm))
+
+    def route(self, logits_in=None):
+        c, t = self.cfg, self.t
+        ids, w, L = self._i32(c.T, c.k), self._f32(c.T, c.k), self._f32(c.T, c.E)
+        lin = torch.from_numpy(np.ascontiguousarray(logits_in, np.float32)).cuda() if logits_in is not None else None
+        moe.moe_route(self.dims, t["x"], t["w_router"], t.get("bias"), lin, L, ids, w)
+        torch.cuda.synchronize()
+        return to_np(ids), to_np(w), to_np(L)
+
+    def dispatch(self, ids):
+        c, t = self.cfg, self.t
+        counts, offsets = self._i32(c.E), self._i32(c.E + 1)
+        perm, inv = self._i32(self.R), self._i32(self.R)
+        xs = torch.empty((self.R, c.d), dtype=self.dt, device="cuda")
+        ids_t = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
+        moe.moe_dispatch(self.dims, t["x"], ids_t, counts, offsets, perm, inv, xs, self.ws, self.ws_bytes)
+        torch.cuda.synchronize()
+        return dict(counts=to_np(counts), offsets=to_np(offsets), perm=to_np(perm),
+                    inv_perm=to_np(inv), x_sorted=xs)
+
+    def ffn(self, x_sorted, offsets):
+        c, t = self.cfg, self.t
+        xs = x_sorted if isinstance(x_sorted, torch.Tensor) else torch.from_numpy(
+            np.ascontiguousarray(x_sorted)).to(self.dt).cuda()
+        off = torch.from_numpy(np.ascontiguousarray(offsets, np.int32)).cuda()
+        y = self._f32(self.R, c.d)
+        ysh = self._f32(c.T, c.d) if c.n_shared else None
+        moe.moe_grouped_ffn(self.dims, xs, off, t["w_gate"], t["w_up"], t["w_down"],
+                            t["x"] if c.n_shared else None, t.get("wsh_gate"), t.get("wsh_up"),
+                            t.get("wsh_down"), y, ysh, self.ws, self.ws_bytes)
+        torch.cuda.synchronize()
+        a_bytes = self.R * c.I * self.es
+        adt = torch.bfloat16 if self.es == 2 else torch.float32
+        A = self.ws[:a_bytes].view(adt).reshape(self.R, c.I)
+        res = dict(y_sorted=to_np(y), A=to_np(A))
+        if c.n_shared:
+            off_sh = (a_bytes + 255) // 256 * 256
+            sh_bytes = c.T * c.n_shared * c.I_shared * self.es
+            res["A_shared"] = to_np(self.ws[off_sh:off_sh + sh_bytes].view(adt).reshape(
+                c.T, c.n_shared * c.I_shared))
+            res["y_shared"] = to_np(ysh)
+        return res
+
+    def combine(self, y_sorted, inv_perm, w, y_shared):
+        c = self.cfg
+        y = torch.from_numpy(np.ascontiguousarray(y_sorted, np.float32)).cuda()
+        inv = torch.from_numpy(np.ascontiguousarray(inv_perm, np.int32)).cuda()
+        wt = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+        ysh = torch.from_numpy(np.ascontiguousarray(y_shared, np.float32)).cuda() if y_shared is not None else None
+        out = self._f32(c.T, c.d)
+        moe.moe_combine(self.dims, y, inv, wt, ysh, out)
+        torch.cuda.synchronize()
+        return to_np(out)

@@ -1,0 +1,185 @@
+"""The C ABI on the host: the library loads without a GPU, exports every entry
+point include/moe.h declares (and nothing else of its own), and rejects
+invalid arguments with the documented status before any HIP call.
+
+Every call here fails validation, so no kernel is ever launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import expert_routing_grouped_route_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+
+
+def test_header_and_binding_agree():
+    names = declared_entry_points()
+    assert sorted(names) == sorted(moe.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.lib()
+    for name in declared_entry_points():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    ours = {s for s in exported if s.startswith("moe") or "moe" in s}
+    assert ours == set(declared_entry_points())
+
+
+def test_status_strings():
+    for code in range(5):
+        assert moe.moe_status_str(code).startswith(
+            ["MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"][code])
+    assert moe.moe_status_str(99) == "unknown moe_status_t"
+
+
+GOOD = dict(T=1000, d=256, E=16, k=4, I=384, n_shared=1, I_shared=256, dtype="bf16")
+
+
+def dims(**kw):
+    p = dict(GOOD)
+    p.update(kw)
+    return moe.dims(**p)
+
+
+def test_workspace_bytes():
+    d = dims()
+    ws = moe.moe_workspace_bytes(d)
+    R = 1000 * 4
+    # at least A, x_sorted (bf16) and y_sorted (fp32)
+    assert ws >= R * 384 * 2 + R * 256 * 2 + R * 256 * 4
+    assert moe.moe_workspace_bytes(dims(T=2000)) > ws
+    assert moe.moe_workspace_bytes(dims(dtype="f32")) > ws
+    assert moe.moe_workspace_bytes(dims(T=0)) > 0
+    for bad in (dict(E=300), dict(k=17, E=20), dict(d=100), dict(T=-1), dict(n_shared=1, I_shared=0)):
+        assert moe.moe_workspace_bytes(dims(**bad)) == 0, bad
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(d=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_shared=2, I_shared=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_shared=0, I_shared=64), moe.MOE_ERR_INVALID_ARG),
+    (dict(E=257), moe.MOE_ERR_UNSUPPORTED),
+    (dict(k=17, E=32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(k=5, E=4), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d=96), moe.MOE_ERR_UNSUPPORTED),
+    (dict(I=100), moe.MOE_ERR_UNSUPPORTED),
+    (dict(I_shared=96), moe.MOE_ERR_UNSUPPORTED),
+    (dict(dtype=7), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 29, k=4), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_invalid_dims_rejected_by_every_entry_point(bad, code):
+    d = dims(**bad)
+    P = 1 << 40  # never dereferenced: validation fails first
+    lib = moe.lib()
+    assert lib.moe_route(ctypes.byref(d), P, P, None, None, None, P, P, 0) == code
+    assert lib.moe_dispatch(ctypes.byref(d), P, P, P, P, P, P, P, P, 1 << 40, 0) == code
+    assert lib.moe_grouped_ffn(ctypes.byref(d), P, P, P, P, P, P, P, P, P, P, P, P, 1 << 40, 0) == code
+    assert lib.moe_combine(ctypes.byref(d), P, P, P, None, P, 0) == code
+    assert lib.moe_layer_fwd(ctypes.byref(d), P, P, None, P, P, P, P, P, P, P, None, None, None,
+                             None, None, P, 1 << 40, 0) == code
+
+
+def test_null_dims_rejected():
+    lib = moe.lib()
+    assert lib.moe_route(None, 0, 0, None, None, None, 0, 0, 0) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_bytes(None) == 0
+
+
+class Bufs:
+    """Distinct, 256-byte aligned fake device addresses, 4 GiB apart."""
+
+    def __init__(self):
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        return (1 << 40) + (self.n << 32)
+
+
+def layer_args(d, **override):
+    b = Bufs()
+    a = dict(x=b(), w_router=b(), bias=None, w_gate=b(), w_up=b(), w_down=b(), wsh_gate=b(),
+             wsh_up=b(), wsh_down=b(), out=b(), ids=None, w=None, counts=None, offsets=None,
+             perm=None, ws=b(), ws_bytes=moe.moe_workspace_bytes(d))
+    a.update(override)
+    return a
+
+
+def call_layer(d, a):
+    return moe.lib().moe_layer_fwd(ctypes.byref(d), a["x"], a["w_router"], a["bias"], a["w_gate"],
+                                   a["w_up"], a["w_down"], a["wsh_gate"], a["wsh_up"],
+                                   a["wsh_down"], a["out"], a["ids"], a["w"], a["counts"],
+                                   a["offsets"], a["perm"], a["ws"], a["ws_bytes"], 0)
+
+
+@pytest.mark.parametrize("override,code", [
+    (dict(x=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(out=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(ws=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(wsh_down=None), moe.MOE_ERR_INVALID_ARG),
+    (dict(w_gate=(1 << 40) + 8), moe.MOE_ERR_INVALID_ARG),  # misaligned
+    (dict(bias=(1 << 41) + 4), moe.MOE_ERR_INVALID_ARG),    # misaligned optional input
+    (dict(ws_bytes=1024), moe.MOE_ERR_WORKSPACE),
+])
+def test_layer_rejects_bad_buffers(override, code):
+    d = dims()
+    a = layer_args(d)
+    if "w_gate" in override:
+        override = dict(w_gate=a["w_gate"] + 8)
+    a.update(override)
+    assert call_layer(d, a) == code
+
+
+def test_layer_rejects_output_overlapping_input():
+    d = dims()
+    a = layer_args(d)
+    a["out"] = a["x"] + 4096  # inside x [T, d] bf16
+    assert call_layer(d, a) == moe.MOE_ERR_INVALID_ARG
+    a = layer_args(d)
+    a["ids"] = a["ws"] + 256  # an optional output inside the workspace
+    assert call_layer(d, a) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_inputs_may_alias_each_other():
+    d = dims()
+    a = layer_args(d)
+    a["w_up"] = a["w_gate"]  # read-only buffers may be shared
+    a["ws_bytes"] = 1024     # stop at the workspace check, before any launch
+    assert call_layer(d, a) == moe.MOE_ERR_WORKSPACE
+
+
+def test_route_requires_x_only_without_given_logits():
+    d = dims()
+    lib = moe.lib()
+    b = Bufs()
+    ids, w = b(), b()
+    assert lib.moe_route(ctypes.byref(d), None, b(), None, None, None, ids, w, 0) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(d), b(), b(), None, None, None, None, w, 0) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(d), b(), b(), None, None, b() + 4, ids, w, 0) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_timed_layer_rejects_bad_event_list():
+    d = dims()
+    a = layer_args(d)
+    lib = moe.lib()
+    arr = (ctypes.c_void_p * 7)(*([1] * 7))
+    args = [ctypes.byref(d), a["x"], a["w_router"], None, a["w_gate"], a["w_up"], a["w_down"],
+            a["wsh_gate"], a["wsh_up"], a["wsh_down"], a["out"], None, None, None, None, None,
+            a["ws"], a["ws_bytes"]]
+    assert lib.moe_layer_fwd_timed(*args, arr, 7, 0) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_fwd_timed(*args, None, 3, 0) == moe.MOE_ERR_INVALID_ARG
+    zero = (ctypes.c_void_p * 2)(None, None)
+    assert lib.moe_layer_fwd_timed(*args, zero, 2, 0) == moe.MOE_ERR_INVALID_ARG
