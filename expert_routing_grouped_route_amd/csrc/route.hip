@@ -160,10 +160,17 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     for (int e = 0; e < E; ++e) {
       const float* w = wr + (size_t)e * d;
       float s = 0.0f;
-      for (int i = lane; i < d; i += 64) s = __fadd_rn(s, __fmul_rn(xr[i], w[i]));
+      {
+        // separate multiply and add: no fused multiply-add in this order
+#pragma clang fp contract(off)
+        for (int i = lane; i < d; i += 64) {
+          const float p = xr[i] * w[i];
+          s = s + p;
+        }
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) s = __fadd_rn(s, __shfl_xor(s, m));
-      if (bias) s = __fadd_rn(s, bias[e]);
+        for (int m = 32; m >= 1; m >>= 1) s = s + __shfl_xor(s, m);
+        if (bias) s = s + bias[e];
+      }
       if (lane == 0) Ls[wave * 4 + q][e] = s;
     }
   }

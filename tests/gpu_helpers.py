@@ -61,6 +61,38 @@ def logits_bound(x, w_router, bias, L_ref):
     return gamma * mag + U32 * b + U32 * np.abs(L_ref.astype(np.float64))
 
 
+def swiglu_a_bound(X, w_gate, w_up, A_ref):
+    """Allowed |A_gpu - A_ref| for A = bf16(silu(X Wg^T) * (X Wu^T)) made from
+    fp32 dot products: one bf16 ulp of the reference plus the float32
+    dot-product error of G and U carried through the product,
+    |dA| <= 1.1 |U| |dG| + |silu(G)| |dU| <= 2.2 gamma_d (|X||Wg|^T)(|X||Wu|^T),
+    plus a few float32 ulps of A for the exponential and division."""
+    d = X.shape[1]
+    gamma = (d + 1) * U32 / (1 - (d + 1) * U32)
+    ax = np.abs(np.asarray(X, np.float64))
+    mg = ax @ np.abs(np.asarray(w_gate, np.float64)).T
+    mu = ax @ np.abs(np.asarray(w_up, np.float64)).T
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(A_ref), 1e-38))) - 7)
+    return ulp + 2.2 * gamma * mg * mu + 8 * U32 * np.abs(A_ref)
+
+
+def check_swiglu_a(A_gpu, A_ref, X, offsets, w_gate, w_up, what="A"):
+    """bf16 A against the oracle: within the bound above everywhere, and equal
+    to the oracle's correctly rounded value almost everywhere (round to
+    nearest even; truncation would differ on about half of the elements)."""
+    A_gpu = np.asarray(A_gpu, np.float64)
+    for e in range(len(offsets) - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        bound = swiglu_a_bound(X[r0:r1], w_gate[e], w_up[e], A_ref[r0:r1])
+        err = np.abs(A_gpu[r0:r1] - A_ref[r0:r1])
+        assert np.all(err <= bound), f"{what}, expert {e}: error {(err / bound).max():.2f}x the bound"
+    flips = (A_gpu != A_ref).mean()
+    assert flips < 0.01, f"{what}: {flips:.3%} of the elements differ from the oracle's rounding"
+    return flips
+
+
 def check_topk_of_own_logits(L, ids, k):
     """The ids are the top-k of the given logits with the lower-index tie rule
     (checked directly from the definition, per token)."""
