@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
-SOURCES = ("route.hip", "dispatch.hip", "gemm.hip", "combine.hip", "moe_api.hip")
+SOURCES = ("route.hip", "dispatch.hip", "gemm_bf16.hip", "gemm_f32.hip", "combine.hip",
+           "moe_api.hip")
 ARCH = "gfx950"
 
 

@@ -12,7 +12,8 @@
 //   count:  per block of `chunk` assignments, an LDS histogram of expert ids
 //   scan:   one block; per expert, an exclusive scan over the blocks (block
 //           bases), then exclusive scans over experts of the counts
-//           (offsets) and of the M-tiles per expert (tile table of the GEMMs)
+//           (offsets) and of the M-tiles per expert, with the expert of every
+//           M-tile (the tile table of the grouped GEMMs)
 //   rank:   per block, its chunk in order, 256 assignments at a time: the
 //           stable rank within a wave from 8 ballots on the id bits, across
 //           waves from LDS counts; writes perm and inv_perm
@@ -27,6 +28,18 @@ int dispatch_chunk(int64_t R) {
   int64_t c = (R + 255) / 256;
   c = (c + 255) / 256 * 256;
   return (int)(c < kDispatchChunk ? kDispatchChunk : c);
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev]) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
 }
 
 int dispatch_blocks(int64_t R) {
@@ -63,28 +76,39 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* buf) {
   return buf[threadIdx.x];
 }
 
-// Per-expert counts -> offsets [E+1] and the M-tile prefix [E+1].
-__device__ __forceinline__ void write_offsets(int cnt, int E, int32_t* __restrict__ offsets,
-                                              int32_t* __restrict__ tile_off, int* buf) {
+// The GEMM tile table: tiles[0..E] = M-tile prefix per expert (units of kBM
+// rows), followed by tiles[E+1+j] = expert of M-tile j.
+__device__ __forceinline__ void write_tile_table(int cnt, int E, int32_t* __restrict__ tiles,
+                                                 int* buf) {
   const int e = threadIdx.x;
-  const int tiles = (cnt + kBM - 1) / kBM;
+  const int nt = (cnt + kBM - 1) / kBM;
+  const int tincl = block_inclusive_scan(nt, buf);
+  if (e < E) {
+    tiles[e] = tincl - nt;
+    for (int j = tincl - nt; j < tincl; ++j) tiles[E + 1 + j] = e;
+  }
+  if (e == E - 1) tiles[E] = tincl;
+}
+
+// Per-expert counts -> offsets [E+1], and the tile table when asked for.
+__device__ __forceinline__ void write_offsets(int cnt, int E, int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ tiles, int* buf) {
+  const int e = threadIdx.x;
   const int incl = block_inclusive_scan(cnt, buf);
   if (e < E) offsets[e] = incl - cnt;
   if (e == E - 1) offsets[E] = incl;
   __syncthreads();
-  const int tincl = block_inclusive_scan(tiles, buf);
-  if (tile_off) {
-    if (e < E) tile_off[e] = tincl - tiles;
-    if (e == E - 1) tile_off[E] = tincl;
-  }
+  if (tiles) write_tile_table(cnt, E, tiles, buf);
 }
 
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ blk, int nblk,
                                                             int E, int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ tile_off) {
+                                                            int32_t* __restrict__ tiles,
+                                                            int32_t* __restrict__ ctr) {
   __shared__ int buf[256];
   const int e = threadIdx.x;
+  if (ctr && e < kGemmCounters) ctr[e] = 0;
   int run = 0;
   if (e < E) {
     int b = 0;
@@ -104,18 +128,17 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict_
     }
     if (counts) counts[e] = run;
   }
-  write_offsets(e < E ? run : 0, E, offsets, tile_off, buf);
+  write_offsets(e < E ? run : 0, E, offsets, tiles, buf);
 }
 
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
-                                                         int E, int32_t* __restrict__ tile_off) {
+                                                         int E, int32_t* __restrict__ tiles,
+                                                         int32_t* __restrict__ ctr) {
   __shared__ int buf[256];
   const int e = threadIdx.x;
+  if (e < kGemmCounters) ctr[e] = 0;
   const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
-  const int tiles = (cnt + kBM - 1) / kBM;
-  const int tincl = block_inclusive_scan(tiles, buf);
-  if (e < E) tile_off[e] = tincl - tiles;
-  if (e == E - 1) tile_off[E] = tincl;
+  write_tile_table(cnt, E, tiles, buf);
 }
 
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(
@@ -182,7 +205,7 @@ void launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), block, 0, stream, a.ids, (int)R, a.E,
                        chunk, a.blk);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), block, 0, stream, a.blk, nblk, a.E, a.counts,
-                     a.offsets, a.tile_off);
+                     a.offsets, a.tiles, a.ctr);
   if (nblk == 0) return;
   hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nblk), block, 0, stream, a.ids, (int)R, a.E, chunk,
                      a.offsets, a.blk, a.perm, a.inv_perm);
@@ -195,8 +218,9 @@ void launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
   }
 }
 
-void launch_tile_table(const int32_t* offsets, int E, int32_t* tile_off, hipStream_t stream) {
-  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(256), 0, stream, offsets, E, tile_off);
+void launch_tile_table(const int32_t* offsets, int E, int32_t* tiles, int32_t* ctr,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(256), 0, stream, offsets, E, tiles, ctr);
 }
 
 }  // namespace moe

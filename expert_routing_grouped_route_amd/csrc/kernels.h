@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace moe {
 
 struct RouteArgs {
@@ -32,7 +34,9 @@ struct DispatchArgs {
   const int32_t* ids;   // [T,k]
   int32_t* counts;      // [E] or null
   int32_t* offsets;     // [E+1]
-  int32_t* tile_off;    // [E+1] or null: M-tile prefix (units of kBM rows)
+  int32_t* tiles;       // or null: tile table, [E+1] M-tile prefix (units of kBM
+                        // rows) then the expert of each M-tile (tile_table_ints)
+  int32_t* ctr;         // or null: kGemmCounters work counters of the GEMMs, zeroed
   int32_t* perm;        // [R]
   int32_t* inv_perm;    // [R]
   void* x_sorted;       // [R,d] or null (skip the row gather)
@@ -43,8 +47,19 @@ struct DispatchArgs {
 };
 void launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
-// M-tile prefix table from expert offsets (for a grouped FFN call on its own).
-void launch_tile_table(const int32_t* offsets, int E, int32_t* tile_off, hipStream_t stream);
+// Tile table from expert offsets (for a grouped FFN call on its own); also
+// zeroes the GEMM work counters.
+void launch_tile_table(const int32_t* offsets, int E, int32_t* tiles, int32_t* ctr,
+                       hipStream_t stream);
+constexpr int kGemmCounters = 16;  // 8 per grouped GEMM launch (one per XCD)
+// Compute units of the current device (cached per device).
+int device_cu_count();
+// Upper bound of the M-tiles of R rows over E experts, and the table's size.
+inline int64_t routed_mtile_bound(int64_t R, int E) {
+  // sum_e ceil(n_e / kBM) <= floor((R + E * (kBM - 1)) / kBM)
+  return R > 0 ? (R + (int64_t)E * (kBM - 1)) / kBM : 0;
+}
+inline int64_t tile_table_ints(int64_t R, int E) { return E + 1 + routed_mtile_bound(R, E); }
 
 // Grouped SwiGLU FFN: gate/up GEMM with the SiLU product fused, then down GEMM.
 struct FfnArgs {
@@ -53,7 +68,8 @@ struct FfnArgs {
   const void *wg, *wu, *wd;        // routed weights
   const void *wsg, *wsu, *wsd;     // shared weights or null
   const int32_t* offsets; // [E+1]
-  const int32_t* tile_off;// [E+1]
+  const int32_t* tile_off;// tile table: [E+1] M-tile prefix, then expert per M-tile
+  int32_t* ctr;           // kGemmCounters zeroed work counters
   void* a;                // [R,I]
   void* ash;              // [T, ns*Is]
   float* y;               // [R,d]
@@ -62,11 +78,28 @@ struct FfnArgs {
   int d, E, I, ns, Is;
   bool bf16;
 };
-void launch_gate_up(const FfnArgs& a, hipStream_t stream);
-void launch_down(const FfnArgs& a, hipStream_t stream);
-// Upper bounds of the grid sizes (for validation of the 2^31 grid limit).
-int64_t gate_up_grid(const FfnArgs& a);
-int64_t down_grid(const FfnArgs& a);
+void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream);
+void launch_down_bf16(const FfnArgs& a, hipStream_t stream);
+void launch_gate_up_f32(const FfnArgs& a, hipStream_t stream);
+void launch_down_f32(const FfnArgs& a, hipStream_t stream);
+// Grid sizes in blocks (for validation against the 2^31 grid limit).
+int64_t gate_up_grid_bf16(const FfnArgs& a);
+int64_t down_grid_bf16(const FfnArgs& a);
+int64_t gate_up_grid_f32(const FfnArgs& a);
+int64_t down_grid_f32(const FfnArgs& a);
+
+inline void launch_gate_up(const FfnArgs& a, hipStream_t stream) {
+  if (a.bf16) launch_gate_up_bf16(a, stream);
+  else launch_gate_up_f32(a, stream);
+}
+inline void launch_down(const FfnArgs& a, hipStream_t stream) {
+  if (a.bf16) launch_down_bf16(a, stream);
+  else launch_down_f32(a, stream);
+}
+inline int64_t gate_up_grid(const FfnArgs& a) {
+  return a.bf16 ? gate_up_grid_bf16(a) : gate_up_grid_f32(a);
+}
+inline int64_t down_grid(const FfnArgs& a) { return a.bf16 ? down_grid_bf16(a) : down_grid_f32(a); }
 
 struct CombineArgs {
   const float* y;        // [R,d]

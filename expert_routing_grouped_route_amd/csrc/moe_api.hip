@@ -20,7 +20,7 @@ size_t elem_bytes(const moe_dims_t& D) { return D.dtype == MOE_BF16 ? 2 : 4; }
 // Workspace layout.  The grouped FFN's SwiGLU products come first (the
 // documented contents of the workspace after moe_grouped_ffn).
 struct Layout {
-  size_t a, ash, tile_off, blk, ids, wts, counts, offsets, perm, inv, xs, y, ysh, total;
+  size_t a, ash, tile_off, ctr, blk, ids, wts, counts, offsets, perm, inv, xs, y, ysh, total;
 };
 
 Layout layout_of(const moe_dims_t& D) {
@@ -35,7 +35,8 @@ Layout layout_of(const moe_dims_t& D) {
   };
   L.a = take(R * D.I * es);
   L.ash = take(T * (size_t)D.n_shared * D.I_shared * es);
-  L.tile_off = take((E + 1) * 4);
+  L.tile_off = take((size_t)tile_table_ints((int64_t)R, D.E) * 4);
+  L.ctr = take(kGemmCounters * 4);
   L.blk = take((size_t)dispatch_blocks((int64_t)R) * E * 4);
   L.ids = take(R * 4);
   L.wts = take(R * 4);
@@ -172,8 +173,9 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
   launch_route(ra, stream);
   if (!mark(1)) return MOE_ERR_HIP;
 
-  DispatchArgs da = {x, ids, counts, offsets, at<int32_t>(ws, L.tile_off), perm, inv,
-                     at<void>(ws, L.xs), at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k, (int)es};
+  DispatchArgs da = {x, ids, counts, offsets, at<int32_t>(ws, L.tile_off), at<int32_t>(ws, L.ctr),
+                     perm, inv, at<void>(ws, L.xs), at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k,
+                     (int)es};
   launch_dispatch(da, stream);
   if (!mark(2)) return MOE_ERR_HIP;
 
@@ -188,6 +190,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
   fa.wsd = wsh_down;
   fa.offsets = offsets;
   fa.tile_off = at<int32_t>(ws, L.tile_off);
+  fa.ctr = at<int32_t>(ws, L.ctr);
   fa.a = at<void>(ws, L.a);
   fa.ash = at<void>(ws, L.ash);
   fa.y = at<float>(ws, L.y);
@@ -266,7 +269,7 @@ moe_status_t moe_dispatch(const moe_dims_t* dims, const void* x, const int32_t* 
   if (st != MOE_OK) return st;
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   (void)hipGetLastError();
-  DispatchArgs da = {x, topk_ids, counts, offsets, nullptr, perm, inv_perm, x_sorted,
+  DispatchArgs da = {x, topk_ids, counts, offsets, nullptr, nullptr, perm, inv_perm, x_sorted,
                      at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k, (int)es};
   launch_dispatch(da, stream);
   return launched();
@@ -311,11 +314,12 @@ moe_status_t moe_grouped_ffn(const moe_dims_t* dims, const void* x_sorted, const
   fa.wsd = wsh_down;
   fa.offsets = offsets;
   fa.tile_off = at<int32_t>(ws, L.tile_off);
+  fa.ctr = at<int32_t>(ws, L.ctr);
   fa.a = at<void>(ws, L.a);
   fa.ash = at<void>(ws, L.ash);
   fa.y = y_sorted;
   fa.ysh = sh ? y_shared : nullptr;
-  launch_tile_table(offsets, D.E, at<int32_t>(ws, L.tile_off), stream);
+  launch_tile_table(offsets, D.E, at<int32_t>(ws, L.tile_off), at<int32_t>(ws, L.ctr), stream);
   launch_gate_up(fa, stream);
   launch_down(fa, stream);
   return launched();
