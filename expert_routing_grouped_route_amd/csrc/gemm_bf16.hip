@@ -83,9 +83,11 @@ __device__ __forceinline__ void routed_decode(const FfnArgs& p, const GemmGrid& 
 }
 
 struct BTile {
-  const uint8_t* X;       // first A row
+  const uint8_t* X;       // first A row (or the token rows when rmap is set)
   size_t x_ld;            // bytes between A rows
   int rows;               // valid rows
+  const int32_t* rmap;    // or null: A row r is token row rmap[r] / rdiv of X
+  int rdiv;
   const uint8_t* W[2];    // first row of each 128-row weight half
   int wcols[2];           // valid rows of each half
   size_t w_ld;            // bytes between weight rows
@@ -104,7 +106,14 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
     routed_decode(p, g, L, e, m, n);
     const int r0 = p.offsets[e] + m * kBM;
     t.rows = min(kBM, p.offsets[e + 1] - r0);
-    t.X = static_cast<const uint8_t*>(p.xs) + (size_t)r0 * p.d * 2;
+    if (p.xs) {
+      t.X = static_cast<const uint8_t*>(p.xs) + (size_t)r0 * p.d * 2;
+      t.rmap = nullptr;
+    } else {  // gather the token rows of x through the dispatch permutation
+      t.X = static_cast<const uint8_t*>(p.x);
+      t.rmap = p.perm + r0;
+      t.rdiv = p.k;
+    }
     const size_t w_off = ((size_t)e * p.I + (size_t)n * HALF) * p.d * 2;
     t.W[0] = static_cast<const uint8_t*>(p.wg) + w_off;
     t.W[1] = static_cast<const uint8_t*>(p.wu) + w_off;
@@ -119,6 +128,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
     const int r0 = m * kBM;
     t.rows = (int)min((int64_t)kBM, p.T - r0);
     t.X = static_cast<const uint8_t*>(p.x) + (size_t)r0 * p.d * 2;
+    t.rmap = nullptr;
     const size_t w_off = ((size_t)s * p.Is + (size_t)n * HALF) * p.d * 2;
     t.W[0] = static_cast<const uint8_t*>(p.wsg) + w_off;
     t.W[1] = static_cast<const uint8_t*>(p.wsu) + w_off;
@@ -168,6 +178,7 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     t.w_seg = (size_t)p.d * p.Is * 2;
     t.Out = reinterpret_cast<uint8_t*>(p.ysh + (size_t)r0 * p.d + (size_t)n * WROWS);
   }
+  t.rmap = nullptr;
   const int left = p.d - n * WROWS;  // output columns from this tile on
   t.W[0] = w0;
   t.wcols[0] = min(HALF, left);
@@ -197,7 +208,9 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
     for (int q = 0; q < 2; ++q) {
       const int row = wave * 16 + q * 8 + sub;
       const int c = pos ^ chunk_xor(row);
-      src[q] = t.X + (size_t)min(row, t.rows - 1) * t.x_ld + c * 16;
+      const int rr = min(row, t.rows - 1);
+      const size_t xrow = t.rmap ? (size_t)(t.rmap[rr] / t.rdiv) : (size_t)rr;
+      src[q] = t.X + xrow * t.x_ld + c * 16;
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

@@ -14,9 +14,11 @@ constexpr int FBN = 64;   // output columns per tile
 constexpr int FBK = 16;   // K per LDS step
 
 struct F32Tile {
-  const float* X;       // first A row
+  const float* X;       // first A row (or the token rows when rmap is set)
   size_t x_ld;          // floats between A rows
   int rows;             // valid rows
+  const int32_t* rmap;  // or null: A row r is token row rmap[r] / rdiv of X
+  int rdiv;
   const float* W0;      // first weight row (gate, or down)
   const float* W1;      // first up-weight row (gate/up only)
   size_t w_ld;          // floats between weight rows
@@ -36,7 +38,14 @@ __device__ __forceinline__ bool f32_gate_up_tile(const FfnArgs& p, const GemmGri
     if (!routed_tile(L, p.tile_off, p.E, g.nt_r, e, m, n)) return false;
     const int r0 = p.offsets[e] + m * kBM;
     t.rows = min(kBM, p.offsets[e + 1] - r0);
-    t.X = static_cast<const float*>(p.xs) + (size_t)r0 * p.d;
+    if (p.xs) {
+      t.X = static_cast<const float*>(p.xs) + (size_t)r0 * p.d;
+      t.rmap = nullptr;
+    } else {  // gather the token rows of x through the dispatch permutation
+      t.X = static_cast<const float*>(p.x);
+      t.rmap = p.perm + r0;
+      t.rdiv = p.k;
+    }
     const size_t w_off = ((size_t)e * p.I + (size_t)n * FBN) * p.d;
     t.W0 = static_cast<const float*>(p.wg) + w_off;
     t.W1 = static_cast<const float*>(p.wu) + w_off;
@@ -51,6 +60,7 @@ __device__ __forceinline__ bool f32_gate_up_tile(const FfnArgs& p, const GemmGri
     const int r0 = m * kBM;
     t.rows = (int)min((int64_t)kBM, p.T - r0);
     t.X = static_cast<const float*>(p.x) + (size_t)r0 * p.d;
+    t.rmap = nullptr;
     const size_t w_off = ((size_t)s * p.Is + (size_t)n * FBN) * p.d;
     t.W0 = static_cast<const float*>(p.wsg) + w_off;
     t.W1 = static_cast<const float*>(p.wsu) + w_off;
@@ -100,6 +110,7 @@ __device__ __forceinline__ bool f32_down_tile(const FfnArgs& p, const GemmGrid& 
     t.Out = p.ysh + (size_t)r0 * p.d + (size_t)n * FBN;
   }
   t.W1 = nullptr;
+  t.rmap = nullptr;
   t.out_ld = p.d;
   return true;
 }
@@ -116,8 +127,9 @@ __device__ __forceinline__ void f32_tile_loop(const F32Tile& t, float (&acc)[NW]
 #pragma unroll
     for (int q = 0; q < 2; ++q) {  // X: 128 rows x 16 = 512 float4
       const int c = tid + 256 * q, row = c >> 2, k4 = (c & 3) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(
-          t.X + (size_t)min(row, t.rows - 1) * t.x_ld + k0 + k4);
+      const int rr = min(row, t.rows - 1);
+      const size_t xrow = t.rmap ? (size_t)(t.rmap[rr] / t.rdiv) : (size_t)rr;
+      const float4 v = *reinterpret_cast<const float4*>(t.X + xrow * t.x_ld + k0 + k4);
       sX[k4 + 0][row] = v.x;
       sX[k4 + 1][row] = v.y;
       sX[k4 + 2][row] = v.z;

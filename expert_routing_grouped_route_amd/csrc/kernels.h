@@ -63,7 +63,10 @@ inline int64_t tile_table_ints(int64_t R, int E) { return E + 1 + routed_mtile_b
 
 // Grouped SwiGLU FFN: gate/up GEMM with the SiLU product fused, then down GEMM.
 struct FfnArgs {
-  const void* xs;         // [R,d] rows grouped by expert
+  const void* xs;         // [R,d] rows grouped by expert, or null: then row i of the
+                          // routed operand is x[perm[i] / k] (gathered by the GEMM)
+  const int32_t* perm;    // [R] (with xs == null)
+  int k;                  // top-k (with xs == null)
   const void* x;          // [T,d] (shared experts) or null
   const void *wg, *wu, *wd;        // routed weights
   const void *wsg, *wsu, *wsd;     // shared weights or null

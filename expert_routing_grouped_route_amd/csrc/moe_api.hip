@@ -20,7 +20,7 @@ size_t elem_bytes(const moe_dims_t& D) { return D.dtype == MOE_BF16 ? 2 : 4; }
 // Workspace layout.  The grouped FFN's SwiGLU products come first (the
 // documented contents of the workspace after moe_grouped_ffn).
 struct Layout {
-  size_t a, ash, tile_off, ctr, blk, ids, wts, counts, offsets, perm, inv, xs, y, ysh, total;
+  size_t a, ash, tile_off, ctr, blk, ids, wts, counts, offsets, perm, inv, y, ysh, total;
 };
 
 Layout layout_of(const moe_dims_t& D) {
@@ -44,7 +44,6 @@ Layout layout_of(const moe_dims_t& D) {
   L.offsets = take((E + 1) * 4);
   L.perm = take(R * 4);
   L.inv = take(R * 4);
-  L.xs = take(R * D.d * es);
   L.y = take(R * D.d * 4);
   L.ysh = take(D.n_shared ? T * D.d * 4 : 0);
   L.total = o;
@@ -173,14 +172,16 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
   launch_route(ra, stream);
   if (!mark(1)) return MOE_ERR_HIP;
 
+  // no row gather here: the gate/up GEMM reads the token rows through perm
   DispatchArgs da = {x, ids, counts, offsets, at<int32_t>(ws, L.tile_off), at<int32_t>(ws, L.ctr),
-                     perm, inv, at<void>(ws, L.xs), at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k,
-                     (int)es};
+                     perm, inv, nullptr, at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k, (int)es};
   launch_dispatch(da, stream);
   if (!mark(2)) return MOE_ERR_HIP;
 
   FfnArgs fa = ffn_shape(D);
-  fa.xs = at<void>(ws, L.xs);
+  fa.xs = nullptr;
+  fa.perm = perm;
+  fa.k = D.k;
   fa.x = x;
   fa.wg = w_gate;
   fa.wu = w_up;
@@ -305,6 +306,8 @@ moe_status_t moe_grouped_ffn(const moe_dims_t* dims, const void* x_sorted, const
   (void)hipGetLastError();
   FfnArgs fa = ffn_shape(D);
   fa.xs = x_sorted;
+  fa.perm = nullptr;
+  fa.k = D.k;
   fa.x = x;
   fa.wg = w_gate;
   fa.wu = w_up;

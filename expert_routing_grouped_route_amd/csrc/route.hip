@@ -7,11 +7,11 @@
 // FarSkip-Collective review (axiom ledger, Eq. 9).  Softmax, renormalisation
 // over the kept k and the tie rule are readings: the pages name none of them.
 //
-// One block handles 16 tokens.  bf16 logits run on the matrix cores: the four
+// One block handles 16 tokens.  bf16 logits run on the matrix cores: eight
 // waves split the hidden dimension (K-steps of 32 taken round-robin), each
 // wave holding 16 tokens x E experts of fp32 partial sums; the partials meet
 // in LDS in a fixed order.  fp32 logits run on the vector ALUs in a fixed
-// lane order.  Then each wave takes the top-k of 4 tokens, one wave-wide
+// lane order.  Then each wave takes the top-k of its tokens, one wave-wide
 // arg-max per slot.
 #include "common.h"
 #include "kernels.h"
@@ -90,13 +90,19 @@ __device__ __forceinline__ void topk_one_token(const float* L, int E, int k, int
 }
 
 // Logits of 16 tokens x E experts, bf16 in, fp32 accumulate on the matrix cores.
+// Eight waves split the hidden dimension (K-steps of 32 dealt round-robin);
+// each wave issues the loads of four K-steps before their MFMAs, so a block
+// has 32 K-steps of x and W_r in flight.
+constexpr int kRouteWaves = 8;
+constexpr int kRouteBatch = 4;
+
 template <int NET>  // 16-expert column tiles: E <= 16 * NET
-__global__ __launch_bounds__(256) void route_bf16_kernel(
+__global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int T, int d, int E, int k,
     float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ wts) {
   constexpr int EP = NET * 16 + 1;
-  __shared__ float part[4][kRouteTokens][EP];
+  __shared__ float part[kRouteWaves][kRouteTokens][EP];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * kRouteTokens;
   const int r = lane & 15, kq = (lane >> 4) * 8;
@@ -110,12 +116,22 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
 #pragma unroll
   for (int et = 0; et < NET; ++et) acc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nks = d >> 5;
-  for (int s = wave; s < nks; s += 4) {
-    const bf16x8 a = as_bf16x8(ld_u32x4(xp + s * 32));
+  for (int s0 = wave; s0 < nks; s0 += kRouteWaves * kRouteBatch) {
+    u32x4 av[kRouteBatch], bv[kRouteBatch][NET];
 #pragma unroll
-    for (int et = 0; et < NET; ++et) {
-      const bf16x8 b = as_bf16x8(ld_u32x4(wp[et] + s * 32));
-      acc[et] = mfma_16x16x32_bf16(a, b, acc[et]);
+    for (int u = 0; u < kRouteBatch; ++u) {
+      const int s = min(s0 + u * kRouteWaves, nks - 1);  // clamped steps are not used
+      av[u] = ld_u32x4(xp + s * 32);
+#pragma unroll
+      for (int et = 0; et < NET; ++et) bv[u][et] = ld_u32x4(wp[et] + s * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < kRouteBatch; ++u) {
+      if (s0 + u * kRouteWaves < nks) {
+#pragma unroll
+        for (int et = 0; et < NET; ++et)
+          acc[et] = mfma_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u][et]), acc[et]);
+      }
     }
   }
 #pragma unroll
@@ -124,17 +140,19 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     for (int q = 0; q < 4; ++q) part[wave][(lane >> 4) * 4 + q][et * 16 + r] = acc[et][q];
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < kRouteTokens * E; idx += 256) {
+  for (int idx = threadIdx.x; idx < kRouteTokens * E; idx += 64 * kRouteWaves) {
     const int t = idx / E, e = idx - t * E;
-    float v = ((part[0][t][e] + part[1][t][e]) + part[2][t][e]) + part[3][t][e];
+    float v = part[0][t][e];
+#pragma unroll
+    for (int w = 1; w < kRouteWaves; ++w) v += part[w][t][e];
     if (bias) v += bias[e];
     part[0][t][e] = v;
     if (logits_out && t0 + t < T) logits_out[(size_t)(t0 + t) * E + e] = v;
   }
   __syncthreads();
 #pragma unroll 1
-  for (int q = 0; q < 4; ++q) {
-    const int t = wave * 4 + q;
+  for (int q = 0; q < kRouteTokens / kRouteWaves; ++q) {
+    const int t = wave * (kRouteTokens / kRouteWaves) + q;
     if (t0 + t < T)
       topk_one_token(&part[0][t][0], E, k, lane, ids + (size_t)(t0 + t) * k,
                      wts + (size_t)(t0 + t) * k);
@@ -229,8 +247,8 @@ void launch_route(const RouteArgs& a, hipStream_t stream) {
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
 #define MOE_ROUTE_CASE(N)                                                                   \
-  hipLaunchKernelGGL(route_bf16_kernel<N>, dim3(grid), block, 0, stream, x, wr, a.bias,      \
-                     (int)a.T, a.d, a.E, a.k, a.logits_out, a.ids, a.wts)
+  hipLaunchKernelGGL(route_bf16_kernel<N>, dim3(grid), dim3(64 * kRouteWaves), 0, stream, x, wr, \
+                     a.bias, (int)a.T, a.d, a.E, a.k, a.logits_out, a.ids, a.wts)
   if (a.E <= 16) MOE_ROUTE_CASE(1);
   else if (a.E <= 32) MOE_ROUTE_CASE(2);
   else if (a.E <= 64) MOE_ROUTE_CASE(4);
