@@ -14,8 +14,11 @@ steps.  The oracle (fp64 NumPy on the host cores) is timed on a bounded token
 sample of the same workload as a CPU baseline.
 """
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,19 +30,133 @@ METRIC = "MoE-layer tokens/sec + grouped-GEMM % bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 STAGES = ("route", "dispatch", "gate_up", "down", "combine")
+GATE_UP_KERNEL = "grouped_gemm_bf16_kernel<true>"
+PROFILES = os.path.join(ROOT, "profiles")
+# sources of the gate/up kernel: a change to any of them voids stored counter readings
+GEMM_SOURCES = ("gemm_bf16.hip", "grouped_gemm.h", "kernels.h", "common.h")
+
+
+def gemm_source_sha():
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "expert_routing_grouped_route_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_summary_path(workload):
+    return os.path.join(PROFILES, f"hbm_traffic_gate_up_{workload}.md")
+
+
+def load_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary; None
+    when there is none or it was taken on other kernel sources."""
+    path = traffic_summary_path(workload)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha") != gemm_source_sha():
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
+def _dispatches(csv_path, counter):
+    """[(dispatch id, kernel name, value)] of one counter in a rocprofv3 counter CSV."""
+    out = []
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(out)
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_mib, workload, command):
+    """Write the HBM-traffic summary of the gate/up kernel from a FETCH_SIZE and
+    a WRITE_SIZE run (KiB per dispatch), each scaled by what the same counter
+    reads for the plain device copy of copy_mib MiB at the end of the run."""
+    rec = {"kernel": GATE_UP_KERNEL, "workload": workload, "kernel_source_sha": gemm_source_sha(),
+           "copy_calibration_mib": copy_mib}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _dispatches(path, name)
+        gu = [v for _, k, v in rows if GATE_UP_KERNEL in k]
+        last_moe = max(i for i, k, _ in rows if "moe" in k)
+        cp = sum(v for i, k, v in rows if i > last_moe and "copyBuffer" in k)
+        scale = copy_mib * 1024.0 / cp
+        rec[name] = {"kib_per_launch": sum(gu) / len(gu), "launches": len(gu),
+                     "copy_kib": cp, "scale": scale}
+    rec["traffic_bytes_per_launch"] = round(
+        (rec["FETCH_SIZE"]["kib_per_launch"] * rec["FETCH_SIZE"]["scale"] +
+         rec["WRITE_SIZE"]["kib_per_launch"] * rec["WRITE_SIZE"]["scale"]) * 1024)
+    path = traffic_summary_path(workload)
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic of the gate/up grouped GEMM, {workload}\n\n")
+        fh.write("Commands (one counter per run, from the repository root):\n\n")
+        for c in command:
+            fh.write(f"    {c}\n")
+        fh.write("\nFETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by "
+                 f"(copy size) / (the counter's reading for the {copy_mib} MiB device copy "
+                 "at the end of the run).\n\n")
+        fh.write("```json\n" + json.dumps(rec, indent=1) + "\n```\n")
+    print(path)
+
+
+def kernel_label(name):
+    """Demangled kernel name without return type, anonymous namespace and arguments."""
+    name = re.sub(r"^void ", "", name).replace("(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(name):  # cut at the argument list (first '(' outside template brackets)
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def summarize_stats(stats_csv, workload, command, bench_log=None):
+    """Write the rocprofv3 --stats kernel summary (name, calls, average and total
+    time), with the stage times that bench.py measured with HIP events in the
+    same profiled run when its log is given."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    path = os.path.join(PROFILES, f"kernels_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write(f"# Kernel time, {workload} layer (rocprofv3 --kernel-trace --stats)\n\n")
+        fh.write("Command (from the repository root):\n\n")
+        for c in command:
+            fh.write(f"    {c}\n")
+        fh.write("\n| kernel | calls | average us | total ms | share |\n|---|---|---|---|---|\n")
+        for r in rows:
+            fh.write(f"| `{kernel_label(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |\n")
+        if bench_log:
+            for line in open(bench_log):
+                if line.startswith("{"):
+                    rec = json.loads(line)
+                    fh.write("\nThe same profiled run's HIP-event stage times (ms per layer call, "
+                             "averaged over the timed steps): " +
+                             ", ".join(f"{k} {v}" for k, v in rec["stages_ms"].items()) + ".\n")
+    print(path)
 
 
 def stage_bytes(cfg):
-    """Algorithmic HBM bytes of the bandwidth-bound stages."""
+    """Algorithmic HBM bytes of the bandwidth-bound stages of the layer path.
+
+    In moe_layer_fwd the row gather of x is part of the gate/up GEMM's operand
+    loads, so the dispatch kernels move index data only: the ids in, perm and
+    inv_perm out (the standalone moe_dispatch also writes x_sorted)."""
     es = 2 if cfg.dtype == "bf16" else 4
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     R = T * k
     return {
         # x and W_r read, bias read, ids and weights written
         "route": T * d * es + E * d * es + E * 4 + R * 8,
-        # ids read, x read once, x_sorted written, perm and inv_perm written
-        "dispatch": T * d * es + R * 4 + R * d * es + 2 * R * 4,
-        # y_sorted gathered, ids/weights read, shared output read, out written
+        # ids read, perm and inv_perm written, counts and offsets written
+        "dispatch": R * 4 + 2 * R * 4 + (2 * E + 1) * 4,
+        # y_sorted gathered, inv_perm and weights read, shared output read, out written
         "combine": R * d * 4 + R * 8 + (T * d * 4 if cfg.n_shared else 0) + T * d * 4,
     }
 
@@ -51,27 +168,38 @@ def gemm_flops(cfg):
     return gate_up, down
 
 
-def cpu_baseline(cfg, arrays, budget_s=10.0):
+def cpu_baseline(cfg, arrays, budget_s=10.0, max_runs=7):
     """Time the oracle on the first Ts tokens, doubling Ts until one run takes
-    at least budget_s or covers the whole workload."""
+    at least budget_s or covers the whole workload; when the whole workload
+    takes less than budget_s, repeat it until budget_s of work is done and
+    report the median run."""
     import oracle
     from threadpoolctl import threadpool_limits
 
     cores = len(os.sched_getaffinity(0))
+
+    def run(Ts):
+        t0 = time.perf_counter()
+        oracle.moe_layer(arrays["x"][:Ts], arrays["w_router"], arrays["bias"], arrays["w_gate"],
+                         arrays["w_up"], arrays["w_down"], cfg.k, arrays["wsh_gate"],
+                         arrays["wsh_up"], arrays["wsh_down"], round_a=cfg.dtype == "bf16")
+        return time.perf_counter() - t0
+
     Ts = min(512, cfg.T)
     with threadpool_limits(limits=cores):
         while True:
-            t0 = time.perf_counter()
-            oracle.moe_layer(arrays["x"][:Ts], arrays["w_router"], arrays["bias"], arrays["w_gate"],
-                             arrays["w_up"], arrays["w_down"], cfg.k, arrays["wsh_gate"],
-                             arrays["wsh_up"], arrays["wsh_down"], round_a=cfg.dtype == "bf16")
-            el = time.perf_counter() - t0
+            el = run(Ts)
             if el >= budget_s or Ts >= cfg.T:
                 break
             Ts = min(cfg.T, Ts * 2)
-    return {"value": Ts / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        times = [el]
+        while sum(times) < budget_s and len(times) < max_runs:
+            times.append(run(Ts))
+    med = sorted(times)[len(times) // 2]
+    return {"value": Ts / med, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {Ts} of {cfg.T} tokens, all {cfg.E} experts"
-                      f"{' + shared' if cfg.n_shared else ''}, fp64 NumPy oracle, {el:.1f} s"}
+                      f"{' + shared' if cfg.n_shared else ''}, fp64 NumPy oracle; median of "
+                      f"{len(times)} run(s) of {med:.2f} s"}
 
 
 def main():
@@ -85,7 +213,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter scale)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the gate/up HBM-traffic summary from two rocprofv3 counter CSVs")
+    ap.add_argument("--summarize-stats", metavar="STATS_CSV",
+                    help="write the kernel-time summary from a rocprofv3 kernel_stats CSV")
+    ap.add_argument("--bench-log", help="bench.py output of the profiled run (for --summarize-stats)")
+    ap.add_argument("--command", action="append", default=[],
+                    help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.copy_calibration_mib, args.workload, args.command)
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.workload, args.command, args.bench_log)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share of tokens; --gpus {args.gpus} "
@@ -174,9 +315,10 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k,
                    "I": cfg.I, "n_shared": cfg.n_shared, "I_shared": cfg.I_shared,
                    "router_bias": cfg.bias, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "gate_up_bf16_kernel",
+        "roofline": {"bound": "mfma", "kernel": GATE_UP_KERNEL,
                      "achieved": round(gu_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(cfg.name),
                      "flops_per_launch": fl_gu, "avg_launch_ms": round(stage_ms["gate_up"], 4)},
         "grouped_gemm": {"tflops": round(gemm_tflops, 1),
                          "frac_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
