@@ -11,24 +11,56 @@
 // waves split the hidden dimension (K-steps of 32 taken round-robin), each
 // wave holding 16 tokens x E experts of fp32 partial sums; the partials meet
 // in LDS in a fixed order.  fp32 logits run on the vector ALUs in a fixed
-// lane order.  Then each wave takes the top-k of its tokens, one wave-wide
-// arg-max per slot.
+// lane order.  The top-k then takes one token per 16-lane row, each slot a
+// row-wide arg-max through the VALU's cross-lane data-parallel moves.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-// Top-k of one token whose E logits sit in LDS at `L`.  All 64 lanes take
-// part; lane j < k writes slot j.
-__device__ __forceinline__ void topk_one_token(const float* L, int E, int k, int lane,
-                                               int32_t* __restrict__ ids_out,
-                                               float* __restrict__ w_out) {
-  constexpr int NV = 4;  // E <= 256 = 4 * 64 logits per token
+// Row-wide exchange within each group of 16 lanes on the VALU's data-parallel
+// primitives: CTRL 0xB1 swaps neighbours (quad_perm 1,0,3,2), 0x4E swaps lane
+// pairs (quad_perm 2,3,0,1), 0x141 mirrors each half row of 8, 0x140 mirrors
+// the row of 16.  Applied in that order, a symmetric pairwise rule leaves
+// every lane of the row with the row's result.
+template <int CTRL>
+__device__ __forceinline__ int row16_swap(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+// Keep the larger of (bv, bi) and (ov, oi): larger value first, then the lower
+// index; bi == kNone marks no candidate.
+constexpr int kNone = 0x7fffffff;
+__device__ __forceinline__ void keep_better(float& bv, int& bi, float ov, int oi) {
+  const bool take = oi != kNone && (bi == kNone || ov > bv || (ov == bv && oi < bi));
+  if (take) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void row16_step(float& bv, int& bi) {
+  const float ov = __int_as_float(row16_swap<CTRL>(__float_as_int(bv)));
+  const int oi = row16_swap<CTRL>(bi);
+  keep_better(bv, bi, ov, oi);
+}
+
+// Top-k of one token per 16-lane row.  The token's E logits sit in LDS at `L`;
+// lane c of the row considers experts c, c+16, ... (ascending, so a strict '>'
+// keeps the lowest index among equal values), and each slot is one row-wide
+// arg-max.  Lane c < k of the row writes slot c.  All 16 lanes of a row call
+// this together; `valid` false (a row past T) writes nothing.
+__device__ __forceinline__ void topk_row16(const float* L, int E, int k, bool valid,
+                                           int32_t* __restrict__ ids_out,
+                                           float* __restrict__ w_out) {
+  constexpr int NV = 16;  // E <= 256 = 16 * 16 logits per token
+  const int c = threadIdx.x & 15;
   float v[NV];
   bool live[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
+    const int e = c + 16 * i;
     live[i] = e < E;
     v[i] = live[i] ? L[e] : 0.0f;
   }
@@ -40,32 +72,22 @@ __device__ __forceinline__ void topk_one_token(const float* L, int E, int k, int
     seli[j] = 0;
     if (j < k) {
       float bv = 0.0f;
-      int bi = 0x7fffffff;  // none yet
+      int bi = kNone;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        // within a lane the index grows with i, so a strict '>' keeps the
-        // lowest index among equal values
-        if (live[i] && (bi == 0x7fffffff || v[i] > bv)) {
+      for (int i = 0; i < NV; ++i)
+        if (live[i] && (bi == kNone || v[i] > bv)) {
           bv = v[i];
-          bi = lane + 64 * i;
+          bi = c + 16 * i;
         }
-      }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(bv, m);
-        const int oi = __shfl_xor(bi, m);
-        const bool take = oi != 0x7fffffff &&
-                          (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
-        if (take) {
-          bv = ov;
-          bi = oi;
-        }
-      }
+      row16_step<0xB1>(bv, bi);
+      row16_step<0x4E>(bv, bi);
+      row16_step<0x141>(bv, bi);
+      row16_step<0x140>(bv, bi);
       selv[j] = bv;
       seli[j] = bi;
 #pragma unroll
       for (int i = 0; i < NV; ++i)
-        if (bi == lane + 64 * i) live[i] = false;
+        if (bi == c + 16 * i) live[i] = false;
     }
   }
   // w_j = exp(L_j - L_0) / sum_j' exp(L_j' - L_0): the softmax over all E
@@ -82,7 +104,7 @@ __device__ __forceinline__ void topk_one_token(const float* L, int E, int k, int
   }
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    if (j < k && lane == j) {
+    if (valid && j < k && c == j) {
       ids_out[j] = seli[j];
       w_out[j] = z[j] / s;
     }
@@ -150,12 +172,10 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
     if (logits_out && t0 + t < T) logits_out[(size_t)(t0 + t) * E + e] = v;
   }
   __syncthreads();
-#pragma unroll 1
-  for (int q = 0; q < kRouteTokens / kRouteWaves; ++q) {
-    const int t = wave * (kRouteTokens / kRouteWaves) + q;
-    if (t0 + t < T)
-      topk_one_token(&part[0][t][0], E, k, lane, ids + (size_t)(t0 + t) * k,
-                     wts + (size_t)(t0 + t) * k);
+  if (wave < kRouteTokens / 4) {  // one token per 16-lane row: 4 rows per wave
+    const int t = wave * 4 + (lane >> 4);
+    const size_t tg = (size_t)min(t0 + t, T - 1);
+    topk_row16(&part[0][t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
   }
 }
 
@@ -197,11 +217,10 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     const int t = idx / E, e = idx - t * E;
     if (logits_out && t0 + t < T) logits_out[(size_t)(t0 + t) * E + e] = Ls[t][e];
   }
-#pragma unroll 1
-  for (int q = 0; q < 4; ++q) {
-    const int t = wave * 4 + q;
-    if (t0 + t < T)
-      topk_one_token(&Ls[t][0], E, k, lane, ids + (size_t)(t0 + t) * k, wts + (size_t)(t0 + t) * k);
+  {  // one token per 16-lane row: 4 waves x 4 rows = the block's 16 tokens
+    const int t = wave * 4 + (lane >> 4);
+    const size_t tg = (size_t)min(t0 + t, T - 1);
+    topk_row16(&Ls[t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
   }
 }
 
@@ -221,11 +240,10 @@ __global__ __launch_bounds__(256) void route_from_logits_kernel(
     }
   }
   __syncthreads();
-#pragma unroll 1
-  for (int q = 0; q < 4; ++q) {
-    const int t = wave * 4 + q;
-    if (t0 + t < T)
-      topk_one_token(&Ls[t][0], E, k, lane, ids + (size_t)(t0 + t) * k, wts + (size_t)(t0 + t) * k);
+  {  // one token per 16-lane row: 4 waves x 4 rows = the block's 16 tokens
+    const int t = wave * 4 + (lane >> 4);
+    const size_t tg = (size_t)min(t0 + t, T - 1);
+    topk_row16(&Ls[t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
   }
 }
 
