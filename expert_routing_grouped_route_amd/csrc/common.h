@@ -7,9 +7,9 @@
 
 namespace moe {
 
-// Rows per M-tile of both grouped GEMMs; the dispatch scan builds the
+// Rows per M-tile of the grouped GEMMs; the dispatch scan builds the
 // per-expert M-tile prefix table in units of this.
-constexpr int kBM = 128;
+constexpr int kBM = 256;
 // Assignments handled per block of the dispatch count/rank kernels (minimum).
 constexpr int kDispatchChunk = 1024;
 // Tokens per block of the router.
@@ -19,6 +19,7 @@ constexpr int kMaxK = 16;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
@@ -45,6 +46,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
 // (l / 16); D comes back with column (l % 16), rows 4*(l/16) + 0..3.
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A(32x16) * B(16x32) + C.  Lane l supplies row (l % 32) of A and column
+// (l % 32) of B, each with the 8 K-elements of group (l / 32); D comes back
+// with column (l % 32), value v at row 8*(v/4) + 4*(l/32) + v%4.
+__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float silu_times(float g, float u) {

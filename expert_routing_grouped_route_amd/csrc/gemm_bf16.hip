@@ -9,51 +9,58 @@
 // (SwiGLU without biases, A rounded to bf16) is a reading; the pages do not
 // spell it out.
 //
-// One kernel template serves both products.  A block computes a 128-row x
-// 256-column tile with 8 waves (two per SIMD, so one wave's MFMAs issue while
-// the other waits on LDS) in a 2 x 4 arrangement: 64 x 64 per wave, 4 x 4
-// MFMA 16x16x32 fragments, fp32 accumulators:
-//   gate/up: the 256 columns are 128 gate and the same 128 up columns of W_g
-//            and W_u; a wave holds 32 gate and the matching 32 up columns,
-//            so the epilogue forms bf16(silu(g) * u) in registers;
+// One kernel template serves both products.  What bounds it is the number of
+// 128-byte cache lines a CU can have in flight between its L1 and L2, so the
+// block tile is the largest square the accumulators allow: 256 rows x 256
+// weight rows, 8 waves (two per SIMD) in a 2 x 4 arrangement, each wave 128
+// rows x 64 weight rows as 4 x 2 MFMA 32x32x16 tiles with fp32 accumulators.
+// The weight fragment is the MFMA's first operand, so a lane ends with four
+// consecutive output columns of one row:
+//   gate/up: the 256 weight rows are 128 gate and the same 128 up rows of
+//            W_g and W_u; a wave holds 32 gate and the matching 32 up
+//            columns, so the epilogue forms bf16(silu(g) * u) in registers;
 //   down:    256 output columns of y, fp32.
-// Operands stream global -> LDS with the gfx950 direct 16-byte LDS loads
-// (no register staging) through a ring of 3 K-steps of 64, two steps ahead
-// of the MFMAs, one barrier per step.  Each 128-byte LDS row holds its eight 16-byte
-// K-chunks in an order permuted by (row mod 8), which keeps the fragment
-// reads at the full LDS rate.  The compiler places the LDS waits and
-// interleaves fragment reads with MFMAs.  The epilogue stages the tile
-// through LDS and writes whole rows with 16-byte stores.
+// Operands stream global -> LDS with the gfx950 direct 16-byte LDS loads (no
+// register staging) through two K-stages of 64 (64 KB each), one barrier per
+// stage.  The loads of the next stage are spread between the MFMAs of the
+// current one, so no wave stalls on a full memory queue while its matrix core
+// idles; fragment reads run one K-sub-step ahead of the MFMAs that use them.
+// Each 128-byte LDS row holds its eight 16-byte K-chunks in an order permuted
+// by (row / 2 mod 8), which keeps the 32-row fragment reads free of bank
+// conflicts.  The epilogue stores straight from registers.
 //
 // Work order: the routed tiles of expert 0, 1, ... (within an expert n-tile
 // outer, m-tile inner, so consecutive tiles share a weight slice), then the
 // shared experts' tiles; the expert of a routed tile is one lookup in the tile
 // table the dispatch scan wrote.
 #include <algorithm>
+#include <type_traits>
 
 #include "grouped_gemm.h"
 
 namespace moe {
 namespace {
 
-constexpr int BK = 64;                     // K per stage
-constexpr int WROWS = 256;                 // weight rows per tile
-constexpr int HALF = 128;                  // rows of each weight half
-constexpr int STAGES = 3;
-constexpr int ROW_BYTES = BK * 2;          // one LDS row: 64 bf16
-constexpr int X_BYTES = kBM * ROW_BYTES;   // 16 KB
-constexpr int W_BYTES = WROWS * ROW_BYTES; // 32 KB
-constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;  // 144 KB
+static_assert(kBM == 256, "the bf16 tile is 256 rows");
+constexpr int BK = 64;                          // K per stage
+constexpr int BN = 256;                         // weight rows per tile
+constexpr int GU_COLS = BN / 2;                 // gate/up: output columns per tile
+constexpr int ROW_BYTES = BK * 2;               // one LDS row: 64 bf16
+constexpr int X_BYTES = kBM * ROW_BYTES;        // 32 KB
+constexpr int STAGE_BYTES = (kBM + BN) * ROW_BYTES;  // 64 KB
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;      // 128 KB
+
+constexpr int NWAVES = 8;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int XLOADS = kBM / 8 / NWAVES;        // 1 KB direct loads per wave per stage: 4 of X
+constexpr int WLOADS = BN / 8 / NWAVES;         // and 4 of weights
+constexpr int LOADS = XLOADS + WLOADS;          // 8
+constexpr int XCD_RUN = 8;                      // consecutive work indices per XCD
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 
-constexpr int NWAVES = 8;
-constexpr int XCD_RUN = 8;  // consecutive work indices per XCD
-constexpr int NTHREADS = 64 * NWAVES;
-
 // Position permutation of the 16-byte chunks of LDS row `row`.
-__device__ __forceinline__ int chunk_xor(int row) { return row & 7; }
+__device__ __forceinline__ int chunk_xor(int row) { return (row >> 1) & 7; }
 
 // Hardware barrier with compiler-only fences: the waits that make LDS data
 // visible are issued explicitly before it.
@@ -63,11 +70,8 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding; expcnt untouched).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 0x3) << 14) | (0x7 << 4) | (0x0 << 8));
-}
+// s_waitcnt vmcnt(0) lgkmcnt(0) (gfx9 encoding; expcnt untouched).
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x70); }
 
 // Routed tile t (experts in order; within an expert n-tile outer, m-tile
 // inner) -> expert e, m-tile m, n-tile n.  The expert comes from the tile
@@ -88,15 +92,15 @@ struct BTile {
   int rows;               // valid rows
   const int32_t* rmap;    // or null: A row r is token row rmap[r] / rdiv of X
   int rdiv;
-  const uint8_t* W[2];    // first row of each 128-row weight half
-  int wcols[2];           // valid rows of each half
+  const uint8_t* W[2];    // gate/up: first gate and first up row; down: first row (both)
+  int wrows;              // valid weight rows of each half (gate/up) or of the tile (down)
   size_t w_ld;            // bytes between weight rows
   int nk;                 // K-steps
   int kps;                // shared down tiles: K-steps per shared expert (0: one segment)
   size_t w_seg;           // bytes between shared experts' weight blocks
-  uint8_t* Out;
+  uint8_t* Out;           // element (0, 0) of the tile
   size_t out_ld;          // elements between output rows
-  int out_cols;           // valid output columns
+  int out_cols;           // valid output columns (a multiple of 64)
 };
 
 __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g, int L, int n_routed,
@@ -114,11 +118,11 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
       t.rmap = p.perm + r0;
       t.rdiv = p.k;
     }
-    const size_t w_off = ((size_t)e * p.I + (size_t)n * HALF) * p.d * 2;
+    const size_t w_off = ((size_t)e * p.I + (size_t)n * GU_COLS) * p.d * 2;
     t.W[0] = static_cast<const uint8_t*>(p.wg) + w_off;
     t.W[1] = static_cast<const uint8_t*>(p.wu) + w_off;
-    t.wcols[0] = t.wcols[1] = min(HALF, p.I - n * HALF);
-    t.Out = static_cast<uint8_t*>(p.a) + ((size_t)r0 * p.I + (size_t)n * HALF) * 2;
+    t.wrows = min(GU_COLS, p.I - n * GU_COLS);
+    t.Out = static_cast<uint8_t*>(p.a) + ((size_t)r0 * p.I + (size_t)n * GU_COLS) * 2;
     t.out_ld = p.I;
   } else {
     const int sb = L - n_routed;
@@ -129,12 +133,12 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
     t.rows = (int)min((int64_t)kBM, p.T - r0);
     t.X = static_cast<const uint8_t*>(p.x) + (size_t)r0 * p.d * 2;
     t.rmap = nullptr;
-    const size_t w_off = ((size_t)s * p.Is + (size_t)n * HALF) * p.d * 2;
+    const size_t w_off = ((size_t)s * p.Is + (size_t)n * GU_COLS) * p.d * 2;
     t.W[0] = static_cast<const uint8_t*>(p.wsg) + w_off;
     t.W[1] = static_cast<const uint8_t*>(p.wsu) + w_off;
-    t.wcols[0] = t.wcols[1] = min(HALF, p.Is - n * HALF);
+    t.wrows = min(GU_COLS, p.Is - n * GU_COLS);
     const size_t ld = (size_t)p.ns * p.Is;
-    t.Out = static_cast<uint8_t*>(p.ash) + ((size_t)r0 * ld + (size_t)s * p.Is + (size_t)n * HALF) * 2;
+    t.Out = static_cast<uint8_t*>(p.ash) + ((size_t)r0 * ld + (size_t)s * p.Is + (size_t)n * GU_COLS) * 2;
     t.out_ld = ld;
   }
   t.x_ld = (size_t)p.d * 2;
@@ -142,7 +146,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
   t.nk = p.d / BK;
   t.kps = 0;
   t.w_seg = 0;
-  t.out_cols = t.wcols[0];
+  t.out_cols = t.wrows;
 }
 
 __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, int L, int n_routed,
@@ -156,12 +160,12 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     t.rows = min(kBM, p.offsets[e + 1] - r0);
     t.X = static_cast<const uint8_t*>(p.a) + (size_t)r0 * p.I * 2;
     t.x_ld = (size_t)p.I * 2;
-    w0 = static_cast<const uint8_t*>(p.wd) + ((size_t)e * p.d + (size_t)n * WROWS) * p.I * 2;
+    w0 = static_cast<const uint8_t*>(p.wd) + ((size_t)e * p.d + (size_t)n * BN) * p.I * 2;
     t.w_ld = (size_t)p.I * 2;
     t.nk = p.I / BK;
     t.kps = 0;
     t.w_seg = 0;
-    t.Out = reinterpret_cast<uint8_t*>(p.y + (size_t)r0 * p.d + (size_t)n * WROWS);
+    t.Out = reinterpret_cast<uint8_t*>(p.y + (size_t)r0 * p.d + (size_t)n * BN);
   } else {
     const int sb = L - n_routed;
     n = sb / g.mt_s;
@@ -171,168 +175,209 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     const size_t ld = (size_t)p.ns * p.Is;
     t.X = static_cast<const uint8_t*>(p.ash) + (size_t)r0 * ld * 2;
     t.x_ld = ld * 2;
-    w0 = static_cast<const uint8_t*>(p.wsd) + (size_t)n * WROWS * p.Is * 2;
+    w0 = static_cast<const uint8_t*>(p.wsd) + (size_t)n * BN * p.Is * 2;
     t.w_ld = (size_t)p.Is * 2;
     t.nk = (int)(ld / BK);
     t.kps = p.Is / BK;
     t.w_seg = (size_t)p.d * p.Is * 2;
-    t.Out = reinterpret_cast<uint8_t*>(p.ysh + (size_t)r0 * p.d + (size_t)n * WROWS);
+    t.Out = reinterpret_cast<uint8_t*>(p.ysh + (size_t)r0 * p.d + (size_t)n * BN);
   }
   t.rmap = nullptr;
-  const int left = p.d - n * WROWS;  // output columns from this tile on
-  t.W[0] = w0;
-  t.wcols[0] = min(HALF, left);
-  if (left > HALF) {
-    t.W[1] = w0 + (size_t)HALF * t.w_ld;
-    t.wcols[1] = min(HALF, left - HALF);
-  } else {  // no second half: load valid rows of the first, results are dropped
-    t.W[1] = w0;
-    t.wcols[1] = t.wcols[0];
-  }
+  t.W[0] = t.W[1] = w0;
+  t.wrows = min(BN, p.d - n * BN);
   t.out_ld = p.d;
-  t.out_cols = min(WROWS, left);
+  t.out_cols = t.wrows;
 }
 
-// One tile: pipeline fill, K loop and epilogue.  Ends with the LDS free.
+// One tile: pipeline fill, K loop and epilogue.
 template <bool GATE_UP>
 __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
 
-
-  // ---- loader: 2 X and 4 W direct-to-LDS loads of 1 KB (8 rows) per wave per step
-  const uint8_t* src[6];
-  {
-    const int sub = lane >> 3, pos = lane & 7;
+  // ---- loader.  Direct load q of a wave fills 8 LDS rows (1 KB): lane L
+  // writes row (L / 8), position L % 8, which holds K-chunk (L % 8) ^ chunk_xor(row).
+  // X: LDS rows wave*32 + q*8 + L/8 (q < 4).  Weights: LDS rows 256 + wave*32 +
+  // q*8 + L/8 (q < 4): gate/up waves 0..3 load gate rows, waves 4..7 up rows.
+  const int sub = lane >> 3, pos = lane & 7;
+  const uint8_t* xsrc[XLOADS];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = wave * 16 + q * 8 + sub;
-      const int c = pos ^ chunk_xor(row);
-      const int rr = min(row, t.rows - 1);
-      const size_t xrow = t.rmap ? (size_t)(t.rmap[rr] / t.rdiv) : (size_t)rr;
-      src[q] = t.X + xrow * t.x_ld + c * 16;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = wave * 32 + q * 8 + sub;  // 0..255
-      const bool hi = row >= HALF;
-      const int r = row & (HALF - 1);
-      const int c = pos ^ chunk_xor(row);
-      const uint8_t* base = hi ? t.W[1] : t.W[0];
-      const int valid = hi ? t.wcols[1] : t.wcols[0];
-      src[2 + q] = base + (size_t)min(r, valid - 1) * t.w_ld + c * 16;
-    }
+  for (int q = 0; q < XLOADS; ++q) {
+    const int row = wave * (8 * XLOADS) + q * 8 + sub;
+    const int rr = min(row, t.rows - 1);
+    const size_t xrow = t.rmap ? (size_t)(t.rmap[rr] / t.rdiv) : (size_t)rr;
+    xsrc[q] = t.X + xrow * t.x_ld + ((pos ^ chunk_xor(row)) << 4);
   }
-  auto issue = [&](int kt) {
-    uint8_t* st = smem + (kt % STAGES) * STAGE_BYTES;
-    const size_t xo = (size_t)kt * ROW_BYTES;
-    const size_t wo = t.kps ? (size_t)(kt / t.kps) * t.w_seg + (size_t)(kt % t.kps) * ROW_BYTES
-                            : (size_t)kt * ROW_BYTES;
+  const uint8_t* wbase;  // wave-uniform
+  int wfirst;            // first weight row of this wave within its half (gate/up) or tile (down)
+  if (GATE_UP) {
+    wbase = wave < 4 ? t.W[0] : t.W[1];
+    wfirst = (wave & 3) * (8 * WLOADS);
+  } else {
+    wbase = t.W[0];
+    wfirst = wave * (8 * WLOADS);
+  }
+  uint32_t woff[WLOADS];  // byte offsets from wbase, rows clamped to the valid ones
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      __builtin_amdgcn_global_load_lds(src[q] + xo, (lds_void_t)(st + (wave * 16 + q * 8) * ROW_BYTES),
+  for (int q = 0; q < WLOADS; ++q) {
+    const int r = wfirst + q * 8 + sub;  // its LDS row kBM + wave*32 + q*8 + sub has the same row mod 16
+    woff[q] = (uint32_t)((size_t)min(r, t.wrows - 1) * t.w_ld) + ((pos ^ chunk_xor(r)) << 4);
+  }
+  // weight byte offset of K-step kt (the shared down tiles' K runs over the
+  // shared experts' blocks one after the other)
+  auto w_step = [&](int kt) -> size_t {
+    return t.kps ? (size_t)(kt / t.kps) * t.w_seg + (size_t)(kt % t.kps) * ROW_BYTES
+                 : (size_t)kt * ROW_BYTES;
+  };
+  // direct load q (0..LOADS-1) of K-step kt; wstep = w_step(kt)
+  auto issue = [&](int kt, size_t wstep, int q) {
+    uint8_t* st = smem + (kt & 1) * STAGE_BYTES;
+    if (q < XLOADS) {
+      __builtin_amdgcn_global_load_lds(xsrc[q] + (size_t)kt * ROW_BYTES,
+                                       (lds_void_t)(st + (wave * (8 * XLOADS) + q * 8) * ROW_BYTES), 16, 0, 0);
+    } else {
+      const int w = q - XLOADS;
+      __builtin_amdgcn_global_load_lds(wbase + wstep + woff[w],
+                                       (lds_void_t)(st + X_BYTES + (wave * (8 * WLOADS) + w * 8) * ROW_BYTES),
                                        16, 0, 0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds(src[2 + q] + wo,
-                                       (lds_void_t)(st + X_BYTES + (wave * 32 + q * 8) * ROW_BYTES),
-                                       16, 0, 0);
+    }
   };
 
-  // ---- fragment addresses (bytes within a stage)
-  const int r16 = lane & 15, kg = lane >> 4;
-  const int lane_off = r16 * ROW_BYTES + ((kg ^ chunk_xor(r16)) << 4);  // K-chunk kg; +32 K: ^64
-  int a_off[4], b_off[4];
+  // ---- fragments (bytes within a stage).  MFMA 32x32x16: lane l reads row
+  // (l % 32) with K-chunk 2s + l/32 of sub-step s.  First operand: 32 weight
+  // rows (output columns); second: 32 A rows.
+  const int r32 = lane & 31, kg = lane >> 5;
+  const int cx = chunk_xor(r32);
+  int a_off[4], b_off[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_off[i] = (wm * 64 + i * 16) * ROW_BYTES + lane_off;
+  for (int i = 0; i < 4; ++i) a_off[i] = (wm * 128 + i * 32 + r32) * ROW_BYTES;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int wrow = GATE_UP ? (j < 2 ? wn * 32 + j * 16 : HALF + wn * 32 + (j - 2) * 16)
-                             : wn * 64 + j * 16;
-    b_off[j] = X_BYTES + wrow * ROW_BYTES + lane_off;
+  for (int j = 0; j < 2; ++j) {
+    const int wrow = GATE_UP ? j * GU_COLS + wn * 32 : wn * 64 + j * 32;
+    b_off[j] = X_BYTES + (wrow + r32) * ROW_BYTES;
   }
 
-  f32x4 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // One K-step out of the stage of kt; with MORE, the loads of step kt+1 are
+  // spread between its MFMAs (2 per sub-step, one after every fourth MFMA).
+  // XL: this wave's 32 A rows hold valid rows, so it loads them; MM: its 128
+  // output rows hold valid rows, so it computes.  Rows past the tile's valid
+  // ones cost neither loads nor, in 128-row halves, matrix-core time.
+  auto step = [&](int kt, auto more_c, auto xl_c, auto mm_c) {
+    constexpr bool MORE = decltype(more_c)::value;
+    constexpr bool XL = decltype(xl_c)::value;
+    constexpr bool MM = decltype(mm_c)::value;
+    const size_t wnext = MORE ? w_step(kt + 1) : 0;
+    wait_all_loads();  // this wave's loads of step kt have landed, and its reads of step kt-1
+    block_barrier();   // everyone's: stage kt & 1 is full and stage (kt+1) & 1 is free
+    const uint8_t* st = smem + (kt & 1) * STAGE_BYTES;
+    bf16x8 F[2][6];
+    auto rd = [&](int ks, bf16x8 (&f)[6]) {
+      const int c = (((ks * 2 + kg) ^ cx) << 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = as_bf16x8(ld_u32x4(st + a_off[i] + c));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) f[4 + j] = as_bf16x8(ld_u32x4(st + b_off[j] + c));
+    };
+    if (MM) rd(0, F[0]);
+    __builtin_amdgcn_sched_barrier(0);  // sub-step 0's reads issue before any prefetch
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (MM) {
+        if (ks < 3) rd(ks + 1, F[(ks + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = mfma_32x32x16_bf16(F[ks & 1][4 + j], F[ks & 1][i], acc[i][j]);
+      }
+      if (MORE) {
+#pragma unroll
+        for (int u = 0; u < LOADS / 4; ++u) {
+          const int q = ks * (LOADS / 4) + u;
+          if (XL || q >= XLOADS) issue(kt + 1, wnext, q);
+        }
+      }
+      // schedule: the next sub-step's fragment reads first, then the MFMAs with
+      // a load after every fourth
+      if (MM) {
+        if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (MORE && m % 4 == 0 && (XL || ks * (LOADS / 4) + m / 4 >= XLOADS))
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+    }
+  };
 
   const int nk = t.nk;
-  issue(0);
-  if (nk > 1) issue(1);
-  for (int kt = 0; kt < nk; ++kt) {
-    // this step's loads have landed (the next step's 6 may still be in flight)
-    if (kt + 1 < nk) wait_vm_lgkm0<6>();
-    else wait_vm_lgkm0<0>();
-    block_barrier();
-    if (kt + 2 < nk) issue(kt + 2);  // into the stage of step kt-1, read by everyone now
-    const uint8_t* st = smem + (kt % STAGES) * STAGE_BYTES;
+  auto k_loop = [&](auto xl_c, auto mm_c) {
+    constexpr bool XL = decltype(xl_c)::value;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kx = ks * 64;  // second half of the step: K-chunks 4..7
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = as_bf16x8(ld_u32x4(st + (a_off[i] ^ kx)));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = as_bf16x8(ld_u32x4(st + (b_off[j] ^ kx)));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32_bf16(a[i], b[j], acc[i][j]);
-    }
-  }
+    for (int q = 0; q < LOADS; ++q)
+      if (XL || q >= XLOADS) issue(0, 0, q);
+    for (int kt = 0; kt + 1 < nk; ++kt) step(kt, std::true_type{}, xl_c, mm_c);
+    step(nk - 1, std::false_type{}, xl_c, mm_c);
+  };
+  const bool mm = wm * 128 < t.rows;  // wave-uniform
+  if (wave * (8 * XLOADS) < t.rows) k_loop(std::true_type{}, std::true_type{});
+  else if (mm) k_loop(std::false_type{}, std::true_type{});
+  else k_loop(std::false_type{}, std::false_type{});
+  if (!mm) return;  // no valid rows in this wave's outputs
 
-  // ---- epilogue through LDS
-  wait_vm_lgkm0<0>();
-  block_barrier();
+  // ---- epilogue from registers.  Lane l holds, for A-block i and weight block
+  // j, row wm*128 + i*32 + l%32 and the four columns 8q + 4(l/32) + 0..3 of the
+  // block in acc[i][j][4q..4q+3].
   if (GATE_UP) {
-    constexpr int LD = HALF + 8;  // bf16 per staged row
-    uint16_t* stg = reinterpret_cast<uint16_t*>(smem);
+    if (wn * 32 >= t.out_cols) return;  // a partial last n-tile: this wave's columns are past I
+    uint16_t* out = reinterpret_cast<uint16_t*>(t.Out);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + r32;
+      if (row >= t.rows) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wn * 32 + 8 * q + 4 * kg;
+        uint32_t h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          h[r] = f32_to_bf16_bits(silu_times(acc[i][0][4 * q + r], acc[i][1][4 * q + r]));
+        uint2 v;
+        v.x = h[0] | (h[1] << 16);
+        v.y = h[2] | (h[3] << 16);
+        *reinterpret_cast<uint2*>(out + (size_t)row * t.out_ld + col) = v;
+      }
+    }
+  } else {
+    if (wn * 64 >= t.out_cols) return;
+    float* out = reinterpret_cast<float*>(t.Out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + r32;
+      if (row >= t.rows) continue;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int row = wm * 64 + i * 16 + kg * 4 + q;
-          const int col = wn * 32 + j * 16 + r16;
-          stg[row * LD + col] = f32_to_bf16_bits(silu_times(acc[i][j][q], acc[i][j + 2][q]));
+          const int col = wn * 64 + j * 32 + 8 * q + 4 * kg;
+          float4 v;
+          v.x = acc[i][j][4 * q + 0];
+          v.y = acc[i][j][4 * q + 1];
+          v.z = acc[i][j][4 * q + 2];
+          v.w = acc[i][j][4 * q + 3];
+          *reinterpret_cast<float4*>(out + (size_t)row * t.out_ld + col) = v;
         }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    block_barrier();
-    uint16_t* out = reinterpret_cast<uint16_t*>(t.Out);
-    for (int c = tid; c < kBM * (HALF / 8); c += NTHREADS) {
-      const int row = c >> 4, ch = c & 15;
-      if (row < t.rows && ch * 8 < t.out_cols)
-        *reinterpret_cast<u32x4*>(out + (size_t)row * t.out_ld + ch * 8) =
-            *reinterpret_cast<const u32x4*>(stg + row * LD + ch * 8);
-    }
-  } else {
-    constexpr int LD = WROWS + 4;  // floats per staged row
-    float* stg = reinterpret_cast<float*>(smem);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = wm * 64 + i * 16 + kg * 4 + q;
-          const int col = wn * 64 + j * 16 + r16;
-          stg[row * LD + col] = acc[i][j][q];
-        }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    block_barrier();
-    float* out = reinterpret_cast<float*>(t.Out);
-    for (int c = tid; c < kBM * (WROWS / 4); c += NTHREADS) {
-      const int row = c >> 6, ch = c & 63;
-      if (row < t.rows && ch * 4 < t.out_cols)
-        *reinterpret_cast<u32x4*>(out + (size_t)row * t.out_ld + ch * 4) =
-            *reinterpret_cast<const u32x4*>(stg + row * LD + ch * 4);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staged reads done before the LDS is reused
-  block_barrier();
 }
 
 // Launch slot -> work index: blocks are dealt to the 8 XCDs round-robin, so
@@ -360,8 +405,8 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, 
 GemmGrid bf16_gate_up_grid(const FfnArgs& a) {
   GemmGrid g;
   g.mtb = (int)routed_mtile_bound(a.R, a.E);
-  g.nt_r = (a.I + HALF - 1) / HALF;
-  g.nt_s = a.ns ? (a.Is + HALF - 1) / HALF : 0;
+  g.nt_r = (a.I + GU_COLS - 1) / GU_COLS;
+  g.nt_s = a.ns ? (a.Is + GU_COLS - 1) / GU_COLS : 0;
   g.mt_s = (int)((a.T + kBM - 1) / kBM);
   g.n_shared = a.ns * g.nt_s * g.mt_s;
   g.routed = (int64_t)g.mtb * g.nt_r;
@@ -374,7 +419,7 @@ int64_t pad_slots(int64_t n) { return (n + 8 * XCD_RUN - 1) / (8 * XCD_RUN) * (8
 GemmGrid bf16_down_grid(const FfnArgs& a) {
   GemmGrid g;
   g.mtb = (int)routed_mtile_bound(a.R, a.E);
-  g.nt_r = (a.d + WROWS - 1) / WROWS;
+  g.nt_r = (a.d + BN - 1) / BN;
   g.nt_s = g.nt_r;
   g.mt_s = (int)((a.T + kBM - 1) / kBM);
   g.n_shared = a.ns ? g.nt_r * g.mt_s : 0;

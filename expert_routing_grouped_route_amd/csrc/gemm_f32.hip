@@ -1,16 +1,19 @@
 // Grouped SwiGLU experts for float32 workloads, on the vector ALUs.
 //
-// Same layer and tile space as the bf16 matrix-core kernels (see
+// Same layer and tile table as the bf16 matrix-core kernels (see
 // gemm_bf16.hip for the pages these steps follow); A stays in fp32.  Tiles are
-// 128 rows x 64 columns, K-steps of 16 staged through LDS, each thread
-// accumulating 8 rows x 4 columns with fused multiply-adds.  These kernels
-// serve small float32 layers; large layers are bf16.
+// 128 rows x 64 columns (each M-tile of the table is taken in two halves),
+// K-steps of 16 staged through LDS, each thread accumulating 8 rows x 4
+// columns with fused multiply-adds.  These kernels serve small float32
+// layers; large layers are bf16.
 #include "grouped_gemm.h"
 
 namespace moe {
 namespace {
 
+constexpr int FBM = 128;  // rows per tile (half an M-tile of the table)
 constexpr int FBN = 64;   // output columns per tile
+constexpr int HALVES = kBM / FBM;
 constexpr int FBK = 16;   // K per LDS step
 
 struct F32Tile {
@@ -35,9 +38,10 @@ __device__ __forceinline__ bool f32_gate_up_tile(const FfnArgs& p, const GemmGri
                                                  F32Tile& t) {
   if (L < g.routed) {
     int e, m, n;
-    if (!routed_tile(L, p.tile_off, p.E, g.nt_r, e, m, n)) return false;
-    const int r0 = p.offsets[e] + m * kBM;
-    t.rows = min(kBM, p.offsets[e + 1] - r0);
+    if (!routed_tile(L / HALVES, p.tile_off, p.E, g.nt_r, e, m, n)) return false;
+    const int r0 = p.offsets[e] + m * kBM + (L % HALVES) * FBM;
+    t.rows = min(FBM, p.offsets[e + 1] - r0);
+    if (t.rows <= 0) return false;
     if (p.xs) {
       t.X = static_cast<const float*>(p.xs) + (size_t)r0 * p.d;
       t.rmap = nullptr;
@@ -57,8 +61,8 @@ __device__ __forceinline__ bool f32_gate_up_tile(const FfnArgs& p, const GemmGri
     const int per_s = g.mt_s * g.nt_s;
     const int s = sb / per_s, rem = sb - s * per_s;
     const int n = rem / g.mt_s, m = rem - n * g.mt_s;
-    const int r0 = m * kBM;
-    t.rows = (int)min((int64_t)kBM, p.T - r0);
+    const int r0 = m * FBM;
+    t.rows = (int)min((int64_t)FBM, p.T - r0);
     t.X = static_cast<const float*>(p.x) + (size_t)r0 * p.d;
     t.rmap = nullptr;
     const size_t w_off = ((size_t)s * p.Is + (size_t)n * FBN) * p.d;
@@ -81,9 +85,10 @@ __device__ __forceinline__ bool f32_down_tile(const FfnArgs& p, const GemmGrid& 
                                               F32Tile& t) {
   if (L < g.routed) {
     int e, m, n;
-    if (!routed_tile(L, p.tile_off, p.E, g.nt_r, e, m, n)) return false;
-    const int r0 = p.offsets[e] + m * kBM;
-    t.rows = min(kBM, p.offsets[e + 1] - r0);
+    if (!routed_tile(L / HALVES, p.tile_off, p.E, g.nt_r, e, m, n)) return false;
+    const int r0 = p.offsets[e] + m * kBM + (L % HALVES) * FBM;
+    t.rows = min(FBM, p.offsets[e + 1] - r0);
+    if (t.rows <= 0) return false;
     t.X = static_cast<const float*>(p.a) + (size_t)r0 * p.I;
     t.x_ld = p.I;
     t.W0 = static_cast<const float*>(p.wd) + ((size_t)e * p.d + (size_t)n * FBN) * p.I;
@@ -96,8 +101,8 @@ __device__ __forceinline__ bool f32_down_tile(const FfnArgs& p, const GemmGrid& 
   } else {
     const int sb = L - (int)g.routed;
     const int n = sb / g.mt_s, m = sb - n * g.mt_s;
-    const int r0 = m * kBM;
-    t.rows = (int)min((int64_t)kBM, p.T - r0);
+    const int r0 = m * FBM;
+    t.rows = (int)min((int64_t)FBM, p.T - r0);
     const size_t ld = (size_t)p.ns * p.Is;
     t.X = static_cast<const float*>(p.ash) + (size_t)r0 * ld;
     t.x_ld = ld;
@@ -117,7 +122,7 @@ __device__ __forceinline__ bool f32_down_tile(const FfnArgs& p, const GemmGrid& 
 
 template <int NW>
 __device__ __forceinline__ void f32_tile_loop(const F32Tile& t, float (&acc)[NW][8][4]) {
-  __shared__ float sX[FBK][kBM + 4];
+  __shared__ float sX[FBK][FBM + 4];
   __shared__ float sW[NW][FBK][FBN + 4];
   const int tid = threadIdx.x;
   const int tn = tid & 15, tm = tid >> 4;
@@ -202,8 +207,8 @@ GemmGrid f32_gate_up_grid(const FfnArgs& a) {
   GemmGrid g;
   g.nt_r = (a.I + FBN - 1) / FBN;
   g.nt_s = a.ns ? (a.Is + FBN - 1) / FBN : 0;
-  g.mt_s = (int)((a.T + kBM - 1) / kBM);
-  g.routed = routed_mtile_bound(a.R, a.E) * g.nt_r;
+  g.mt_s = (int)((a.T + FBM - 1) / FBM);
+  g.routed = routed_mtile_bound(a.R, a.E) * HALVES * g.nt_r;
   g.total = g.routed + (int64_t)a.ns * g.nt_s * g.mt_s;
   return g;
 }
@@ -212,8 +217,8 @@ GemmGrid f32_down_grid(const FfnArgs& a) {
   GemmGrid g;
   g.nt_r = (a.d + FBN - 1) / FBN;
   g.nt_s = g.nt_r;
-  g.mt_s = (int)((a.T + kBM - 1) / kBM);
-  g.routed = routed_mtile_bound(a.R, a.E) * g.nt_r;
+  g.mt_s = (int)((a.T + FBM - 1) / FBM);
+  g.routed = routed_mtile_bound(a.R, a.E) * HALVES * g.nt_r;
   g.total = g.routed + (a.ns ? (int64_t)g.nt_r * g.mt_s : 0);
   return g;
 }

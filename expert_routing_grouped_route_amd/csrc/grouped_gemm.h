@@ -1,6 +1,6 @@
 // Tile space shared by the grouped GEMM kernels (bf16 and fp32).
 //
-// M-tiles of kBM = 128 rows per expert come from the tile table that the
+// M-tiles of kBM = 256 rows per expert come from the tile table that the
 // dispatch scan writes (tile_off[e] = M-tiles of the experts before e).
 // Within an expert the tiles run n-tile outer, m-tile inner, so the tiles
 // that share a weight slice are adjacent.  The grid is sized by an upper

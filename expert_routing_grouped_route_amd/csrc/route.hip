@@ -51,10 +51,10 @@ __device__ __forceinline__ void row16_step(float& bv, int& bi) {
 // keeps the lowest index among equal values), and each slot is one row-wide
 // arg-max.  Lane c < k of the row writes slot c.  All 16 lanes of a row call
 // this together; `valid` false (a row past T) writes nothing.
+template <int NV>  // E <= 16 * NV
 __device__ __forceinline__ void topk_row16(const float* L, int E, int k, bool valid,
                                            int32_t* __restrict__ ids_out,
                                            float* __restrict__ w_out) {
-  constexpr int NV = 16;  // E <= 256 = 16 * 16 logits per token
   const int c = threadIdx.x & 15;
   float v[NV];
   bool live[NV];
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
   if (wave < kRouteTokens / 4) {  // one token per 16-lane row: 4 rows per wave
     const int t = wave * 4 + (lane >> 4);
     const size_t tg = (size_t)min(t0 + t, T - 1);
-    topk_row16(&part[0][t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
+    topk_row16<NET>(&part[0][t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
   }
 }
 
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
   {  // one token per 16-lane row: 4 waves x 4 rows = the block's 16 tokens
     const int t = wave * 4 + (lane >> 4);
     const size_t tg = (size_t)min(t0 + t, T - 1);
-    topk_row16(&Ls[t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
+    topk_row16<16>(&Ls[t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
   }
 }
 
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void route_from_logits_kernel(
   {  // one token per 16-lane row: 4 waves x 4 rows = the block's 16 tokens
     const int t = wave * 4 + (lane >> 4);
     const size_t tg = (size_t)min(t0 + t, T - 1);
-    topk_row16(&Ls[t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
+    topk_row16<16>(&Ls[t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
   }
 }
 
