@@ -27,7 +27,8 @@
 // idles; fragment reads run one K-sub-step ahead of the MFMAs that use them.
 // Each 128-byte LDS row holds its eight 16-byte K-chunks in an order permuted
 // by (row / 2 mod 8), which keeps the 32-row fragment reads free of bank
-// conflicts.  The epilogue stores straight from registers.
+// conflicts.  The gate/up epilogue stores from registers; the down epilogue
+// stages its fp32 tile through LDS and stores whole rows.
 //
 // Work order: the routed tiles of expert 0, 1, ... (within an expert n-tile
 // outer, m-tile inner, so consecutive tiles share a weight slice), then the
@@ -332,13 +333,18 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
   if (wave * (8 * XLOADS) < t.rows) k_loop(std::true_type{}, std::true_type{});
   else if (mm) k_loop(std::false_type{}, std::true_type{});
   else k_loop(std::false_type{}, std::false_type{});
-  if (!mm) return;  // no valid rows in this wave's outputs
 
-  // ---- epilogue from registers.  Lane l holds, for A-block i and weight block
-  // j, row wm*128 + i*32 + l%32 and the four columns 8q + 4(l/32) + 0..3 of the
-  // block in acc[i][j][4q..4q+3].
+  // ---- epilogue.  Lane l holds, for A-block i and weight block j, row
+  // wm*128 + i*32 + l%32 and the four columns 8q + 4(l/32) + 0..3 of the block
+  // in acc[i][j][4q..4q+3].  The fp32 output of the down product goes through
+  // LDS (free once every wave's fragment reads are done), so that each store
+  // instruction writes a whole row; staged rows keep their 16-byte pieces at
+  // position (piece ^ row), which spreads both the column writes and the row
+  // reads over the banks.  Waves without valid rows write nothing but take
+  // part in every barrier.
   if (GATE_UP) {
-    if (wn * 32 >= t.out_cols) return;  // a partial last n-tile: this wave's columns are past I
+    // bf16 output is small: each lane stores its four columns (8 bytes) directly
+    if (!mm || wn * 32 >= t.out_cols) return;  // no valid rows, or columns past I
     uint16_t* out = reinterpret_cast<uint16_t*>(t.Out);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -358,24 +364,40 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
       }
     }
   } else {
-    if (wn * 64 >= t.out_cols) return;
+    // fp32 [128 rows][256 columns] per half: 64 pieces of 4 columns per row
+    block_barrier();  // every wave's fragment reads are done: the LDS is free
+    float* sm = reinterpret_cast<float*>(smem);
     float* out = reinterpret_cast<float*>(t.Out);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 128 + i * 32 + r32;
-      if (row >= t.rows) continue;
+    for (int h = 0; h < 2; ++h) {
+      if (wm == h && mm) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < 4; ++i) {
+          const int row = i * 32 + r32;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = wn * 64 + j * 32 + 8 * q + 4 * kg;
-          float4 v;
-          v.x = acc[i][j][4 * q + 0];
-          v.y = acc[i][j][4 * q + 1];
-          v.z = acc[i][j][4 * q + 2];
-          v.w = acc[i][j][4 * q + 3];
-          *reinterpret_cast<float4*>(out + (size_t)row * t.out_ld + col) = v;
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int piece = wn * 16 + j * 8 + 2 * q + kg;
+              f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                         acc[i][j][4 * q + 3]};
+              *reinterpret_cast<f32x4*>(sm + row * 256 + ((piece ^ (row & 63)) << 2)) = v;
+            }
         }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      block_barrier();
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {  // one row per instruction, 16 rows per wave
+        const int row = wave * 16 + u, grow = h * 128 + row;
+        if (grow < t.rows && lane * 4 < t.out_cols)
+          *reinterpret_cast<f32x4*>(out + (size_t)grow * t.out_ld + lane * 4) =
+              *reinterpret_cast<const f32x4*>(sm + row * 256 + ((lane ^ (row & 63)) << 2));
+      }
+      if (h == 0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // staged reads done before the second half
+        block_barrier();
+      }
     }
   }
 }
