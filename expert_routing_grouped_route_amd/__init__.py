@@ -25,7 +25,8 @@ MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
 
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
-                "moe_grouped_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_fwd_timed")
+                "moe_grouped_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_fwd_timed",
+                "moe_layer_fwd_overlap")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -66,6 +67,8 @@ _SIGS = {
     "moe_layer_fwd_timed": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                            _P, _P, _P, _P, ctypes.c_size_t,
                                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, _P]),
+    "moe_layer_fwd_overlap": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _P]),
 }
 
 
@@ -168,3 +171,18 @@ def moe_layer_fwd_timed(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_down, 
                                    _ptr(perm_out), _ptr(ws), int(ws_bytes), arr, len(events),
                                    _stream(stream))
     _check("moe_layer_fwd_timed", st)
+
+
+def moe_layer_fwd_overlap(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_down, wsh_gate,
+                          wsh_up, wsh_down, out, topk_ids_out, topk_w_out, counts_out, offsets_out,
+                          perm_out, ws, ws_bytes, side, fork, join, stream=None):
+    """Shared experts on ``side`` (a torch.cuda.Stream or raw handle); ``fork`` and
+    ``join`` are torch.cuda.Event objects or raw hipEvent_t handles."""
+    ev = lambda e: int(e) if isinstance(e, int) else int(e.cuda_event)
+    st = lib().moe_layer_fwd_overlap(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(bias),
+                                     _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(wsh_gate),
+                                     _ptr(wsh_up), _ptr(wsh_down), _ptr(out), _ptr(topk_ids_out),
+                                     _ptr(topk_w_out), _ptr(counts_out), _ptr(offsets_out),
+                                     _ptr(perm_out), _ptr(ws), int(ws_bytes), _stream(stream),
+                                     _stream(side), ev(fork), ev(join))
+    _check("moe_layer_fwd_overlap", st)

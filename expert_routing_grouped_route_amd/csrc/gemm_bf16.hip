@@ -411,13 +411,17 @@ __device__ __forceinline__ int xcd_remap(int bid) {
   return base + (w & 7) * XCD_RUN + (w >> 3);
 }
 
-// One block per work slot; slots past the device-side tile count return.
+// One block per work slot; slots past the device-side tile count return.  A
+// launch of the shared experts' tiles alone reads nothing the dispatch writes
+// (it may run before the dispatch); a launch of the routed tiles alone stops
+// before the shared ones.
 template <bool GATE_UP>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, GemmGrid g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
-  const int n_routed = p.tile_off[p.E] * g.nt_r;
+  const int n_routed = p.part == kSharedTiles ? 0 : p.tile_off[p.E] * g.nt_r;
   const int L = xcd_remap(blockIdx.x);
-  if (L >= n_routed + g.n_shared) return;
+  const int end = p.part == kRoutedTiles ? n_routed : n_routed + g.n_shared;
+  if (L >= end) return;
   BTile t;
   if (GATE_UP) gate_up_tile(p, g, L, n_routed, t);
   else down_tile(p, g, L, n_routed, t);
@@ -455,18 +459,26 @@ GemmGrid bf16_down_grid(const FfnArgs& a) {
 int64_t gate_up_grid_bf16(const FfnArgs& a) { return pad_slots(bf16_gate_up_grid(a).total); }
 int64_t down_grid_bf16(const FfnArgs& a) { return pad_slots(bf16_down_grid(a).total); }
 
+// Slots of one launch: all tiles, the routed tiles (an upper bound) or the
+// shared experts' tiles.
+int64_t launch_slots(const FfnArgs& a, const GemmGrid& g) {
+  const int64_t n = a.part == kRoutedTiles ? g.routed
+                  : a.part == kSharedTiles ? (int64_t)g.n_shared : g.total;
+  return n ? pad_slots(n) : 0;
+}
+
 void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream) {
-  const GemmGrid g = bf16_gate_up_grid(a);
-  if (g.total == 0) return;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3((unsigned)pad_slots(g.total)),
-                     dim3(NTHREADS), 0, stream, a, g);
+  const int64_t slots = launch_slots(a, bf16_gate_up_grid(a));
+  if (slots == 0) return;
+  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3((unsigned)slots), dim3(NTHREADS), 0,
+                     stream, a, bf16_gate_up_grid(a));
 }
 
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream) {
-  const GemmGrid g = bf16_down_grid(a);
-  if (g.total == 0) return;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3((unsigned)pad_slots(g.total)),
-                     dim3(NTHREADS), 0, stream, a, g);
+  const int64_t slots = launch_slots(a, bf16_down_grid(a));
+  if (slots == 0) return;
+  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3((unsigned)slots), dim3(NTHREADS), 0,
+                     stream, a, bf16_down_grid(a));
 }
 
 }  // namespace moe

@@ -172,9 +172,14 @@ __device__ __forceinline__ void f32_tile_loop(const F32Tile& t, float (&acc)[NW]
   }
 }
 
+// A launch of the shared experts' tiles alone starts after the routed slots.
+__device__ __forceinline__ int f32_slot(const FfnArgs& p, const GemmGrid& g) {
+  return (int)blockIdx.x + (p.part == kSharedTiles ? (int)g.routed : 0);
+}
+
 __global__ __launch_bounds__(256) void gate_up_f32_kernel(FfnArgs p, GemmGrid g) {
   F32Tile t;
-  if (!f32_gate_up_tile(p, g, blockIdx.x, t)) return;
+  if (!f32_gate_up_tile(p, g, f32_slot(p, g), t)) return;
   float acc[2][8][4] = {};
   f32_tile_loop<2>(t, acc);
   const int tn = threadIdx.x & 15, tm = threadIdx.x >> 4;
@@ -190,7 +195,7 @@ __global__ __launch_bounds__(256) void gate_up_f32_kernel(FfnArgs p, GemmGrid g)
 
 __global__ __launch_bounds__(256) void down_f32_kernel(FfnArgs p, GemmGrid g) {
   F32Tile t;
-  if (!f32_down_tile(p, g, blockIdx.x, t)) return;
+  if (!f32_down_tile(p, g, f32_slot(p, g), t)) return;
   float acc[1][8][4] = {};
   f32_tile_loop<1>(t, acc);
   const int tn = threadIdx.x & 15, tm = threadIdx.x >> 4;
@@ -228,16 +233,23 @@ GemmGrid f32_down_grid(const FfnArgs& a) {
 int64_t gate_up_grid_f32(const FfnArgs& a) { return f32_gate_up_grid(a).total; }
 int64_t down_grid_f32(const FfnArgs& a) { return f32_down_grid(a).total; }
 
+// Blocks of one launch: all tiles, the routed slots or the shared tiles.
+int64_t f32_blocks(const FfnArgs& a, const GemmGrid& g) {
+  return a.part == kRoutedTiles ? g.routed : a.part == kSharedTiles ? g.total - g.routed : g.total;
+}
+
 void launch_gate_up_f32(const FfnArgs& a, hipStream_t stream) {
   const GemmGrid g = f32_gate_up_grid(a);
-  if (g.total == 0) return;
-  hipLaunchKernelGGL(gate_up_f32_kernel, dim3((unsigned)g.total), dim3(256), 0, stream, a, g);
+  const int64_t n = f32_blocks(a, g);
+  if (n == 0) return;
+  hipLaunchKernelGGL(gate_up_f32_kernel, dim3((unsigned)n), dim3(256), 0, stream, a, g);
 }
 
 void launch_down_f32(const FfnArgs& a, hipStream_t stream) {
   const GemmGrid g = f32_down_grid(a);
-  if (g.total == 0) return;
-  hipLaunchKernelGGL(down_f32_kernel, dim3((unsigned)g.total), dim3(256), 0, stream, a, g);
+  const int64_t n = f32_blocks(a, g);
+  if (n == 0) return;
+  hipLaunchKernelGGL(down_f32_kernel, dim3((unsigned)n), dim3(256), 0, stream, a, g);
 }
 
 }  // namespace moe

@@ -80,7 +80,9 @@ struct FfnArgs {
   int64_t T, R;
   int d, E, I, ns, Is;
   bool bf16;
+  int part;               // tiles launched: 0 all, 1 routed experts only, 2 shared experts only
 };
+constexpr int kAllTiles = 0, kRoutedTiles = 1, kSharedTiles = 2;
 void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream);
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream);
 void launch_gate_up_f32(const FfnArgs& a, hipStream_t stream);

@@ -123,11 +123,14 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
                        const void* wsh_down, float* out, int32_t* topk_ids_out,
                        float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
                        int32_t* perm_out, void* ws, size_t ws_bytes, hipEvent_t* events,
-                       int n_events, hipStream_t stream) {
+                       int n_events, hipStream_t stream, hipStream_t side = nullptr,
+                       hipEvent_t fork = nullptr, hipEvent_t join = nullptr) {
   moe_status_t st = check_dims(dims);
   if (st != MOE_OK) return st;
   const moe_dims_t& D = *dims;
   if (n_events < 0 || n_events > 6 || (n_events > 0 && !events)) return MOE_ERR_INVALID_ARG;
+  const bool two_streams = side || fork || join;
+  if (two_streams && (!side || !fork || !join || n_events)) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i < n_events; ++i)
     if (!events[i]) return MOE_ERR_INVALID_ARG;
   const Layout L = layout_of(D);
@@ -160,6 +163,37 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
   };
   if (!mark(0)) return MOE_ERR_HIP;
 
+  FfnArgs fa = ffn_shape(D);
+  fa.xs = nullptr;
+  fa.k = D.k;
+  fa.x = x;
+  fa.wg = w_gate;
+  fa.wu = w_up;
+  fa.wd = w_down;
+  fa.wsg = wsh_gate;
+  fa.wsu = wsh_up;
+  fa.wsd = wsh_down;
+  fa.tile_off = at<int32_t>(ws, L.tile_off);
+  fa.ctr = at<int32_t>(ws, L.ctr);
+  fa.a = at<void>(ws, L.a);
+  fa.ash = at<void>(ws, L.ash);
+  fa.y = at<float>(ws, L.y);
+  fa.ysh = sh ? at<float>(ws, L.ysh) : nullptr;
+  if (two_streams) {
+    // the shared experts depend on x alone: they run on the side stream from
+    // the start, beside the gate, the dispatch and the routed experts
+    if (hipEventRecord(fork, stream) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (sh) {
+      FfnArgs fs = fa;
+      fs.part = kSharedTiles;
+      launch_gate_up(fs, side);
+      launch_down(fs, side);
+    }
+    if (hipEventRecord(join, side) != hipSuccess) return MOE_ERR_HIP;
+    fa.part = kRoutedTiles;
+  }
+
   int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
   float* wts = topk_w_out ? topk_w_out : at<float>(ws, L.wts);
   int32_t* counts = counts_out ? counts_out : at<int32_t>(ws, L.counts);
@@ -178,28 +212,13 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
   launch_dispatch(da, stream);
   if (!mark(2)) return MOE_ERR_HIP;
 
-  FfnArgs fa = ffn_shape(D);
-  fa.xs = nullptr;
   fa.perm = perm;
-  fa.k = D.k;
-  fa.x = x;
-  fa.wg = w_gate;
-  fa.wu = w_up;
-  fa.wd = w_down;
-  fa.wsg = wsh_gate;
-  fa.wsu = wsh_up;
-  fa.wsd = wsh_down;
   fa.offsets = offsets;
-  fa.tile_off = at<int32_t>(ws, L.tile_off);
-  fa.ctr = at<int32_t>(ws, L.ctr);
-  fa.a = at<void>(ws, L.a);
-  fa.ash = at<void>(ws, L.ash);
-  fa.y = at<float>(ws, L.y);
-  fa.ysh = sh ? at<float>(ws, L.ysh) : nullptr;
   launch_gate_up(fa, stream);
   if (!mark(3)) return MOE_ERR_HIP;
   launch_down(fa, stream);
   if (!mark(4)) return MOE_ERR_HIP;
+  if (two_streams && hipStreamWaitEvent(stream, join, 0) != hipSuccess) return MOE_ERR_HIP;
 
   CombineArgs ca = {fa.y, inv, wts, fa.ysh, out, D.T, D.d, D.k};
   launch_combine(ca, stream);
@@ -369,6 +388,20 @@ moe_status_t moe_layer_fwd_timed(const moe_dims_t* dims, const void* x, const vo
   return layer_fwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down, out,
                    topk_ids_out, topk_w_out, counts_out, offsets_out, perm_out, ws, ws_bytes,
                    events, n_events, stream);
+}
+
+moe_status_t moe_layer_fwd_overlap(const moe_dims_t* dims, const void* x, const void* w_router,
+                                   const float* bias, const void* w_gate, const void* w_up,
+                                   const void* w_down, const void* wsh_gate, const void* wsh_up,
+                                   const void* wsh_down, float* out, int32_t* topk_ids_out,
+                                   float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                                   int32_t* perm_out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream, hipStream_t side, hipEvent_t fork,
+                                   hipEvent_t join) {
+  if (!side || !fork || !join) return MOE_ERR_INVALID_ARG;
+  return layer_fwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down, out,
+                   topk_ids_out, topk_w_out, counts_out, offsets_out, perm_out, ws, ws_bytes,
+                   nullptr, 0, stream, side, fork, join);
 }
 
 }  // extern "C"

@@ -170,6 +170,31 @@ MOE_API moe_status_t moe_layer_fwd_timed(const moe_dims_t* dims, const void* x, 
                                  int32_t* perm_out, void* ws, size_t ws_bytes,
                                  hipEvent_t* events, int n_events, hipStream_t stream);
 
+/* moe_layer_fwd with the shared experts on a second stream.  The shared
+ * experts depend on x alone, so their two GEMMs run on `side` from the start,
+ * beside the gate, the dispatch and the routed experts on `stream`; the
+ * combine on `stream` waits for them.  This is the one-GPU form of running
+ * the always-on shared expert concurrently with the routed path (the
+ * FarSkip-Collective review: Fig. 11 caption, the shared expert beside
+ * Combine; its second hardware queue in "What carries the argument").
+ * Results are bit-identical to moe_layer_fwd (same kernels, same tiles).
+ *   side: a stream other than `stream`, of the same device.
+ *   fork, join: caller-owned events (timing may be disabled); `fork` is
+ *     recorded on `stream` at entry, `join` on `side` after the shared
+ *     experts.  Both are re-recorded on every call.
+ * All other arguments and the workspace are those of moe_layer_fwd; the side
+ * stream uses parts of the same workspace, so two calls that share a
+ * workspace must not overlap.  NULL side, fork or join: MOE_ERR_INVALID_ARG.
+ * Returns once both streams have their work enqueued. */
+MOE_API moe_status_t moe_layer_fwd_overlap(const moe_dims_t* dims, const void* x, const void* w_router,
+                                   const float* bias, const void* w_gate, const void* w_up,
+                                   const void* w_down, const void* wsh_gate, const void* wsh_up,
+                                   const void* wsh_down, float* out, int32_t* topk_ids_out,
+                                   float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                                   int32_t* perm_out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream, hipStream_t side, hipEvent_t fork,
+                                   hipEvent_t join);
+
 #ifdef __cplusplus
 }
 #endif

@@ -169,6 +169,25 @@ class Layer:
         return dict(out=to_np(out), ids=to_np(ids), w=to_np(w), counts=to_np(counts),
                     offsets=to_np(offsets), perm=to_np(perm))
 
+    def layer_overlap(self):
+        """moe_layer_fwd_overlap: shared experts on a second stream."""
+        c, t = self.cfg, self.t
+        out = self._f32(c.T, c.d)
+        ids, w = self._i32(c.T, c.k), self._f32(c.T, c.k)
+        counts, offsets, perm = self._i32(c.E), self._i32(c.E + 1), self._i32(self.R)
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        fork.record(main)  # creates the underlying events
+        join.record(main)
+        moe.moe_layer_fwd_overlap(self.dims, t["x"], t["w_router"], t.get("bias"), t["w_gate"],
+                                  t["w_up"], t["w_down"], t.get("wsh_gate"), t.get("wsh_up"),
+                                  t.get("wsh_down"), out, ids, w, counts, offsets, perm, self.ws,
+                                  self.ws_bytes, side, fork, join, stream=main)
+        torch.cuda.synchronize()
+        return dict(out=to_np(out), ids=to_np(ids), w=to_np(w), counts=to_np(counts),
+                    offsets=to_np(offsets), perm=to_np(perm))
+
     def route(self, logits_in=None):
         c, t = self.cfg, self.t
         ids, w, L = self._i32(c.T, c.k), self._f32(c.T, c.k), self._f32(c.T, c.E)

@@ -90,6 +90,8 @@ def test_invalid_dims_rejected_by_every_entry_point(bad, code):
     assert lib.moe_combine(ctypes.byref(d), P, P, P, None, P, 0) == code
     assert lib.moe_layer_fwd(ctypes.byref(d), P, P, None, P, P, P, P, P, P, P, None, None, None,
                              None, None, P, 1 << 40, 0) == code
+    assert lib.moe_layer_fwd_overlap(ctypes.byref(d), P, P, None, P, P, P, P, P, P, P, None, None,
+                                     None, None, None, P, 1 << 40, 0, P, P, P) == code
 
 
 def test_null_dims_rejected():
@@ -169,6 +171,23 @@ def test_route_requires_x_only_without_given_logits():
     assert lib.moe_route(ctypes.byref(d), None, b(), None, None, None, ids, w, 0) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(d), b(), b(), None, None, None, None, w, 0) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(d), b(), b(), None, None, b() + 4, ids, w, 0) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_overlap_layer_requires_side_stream_and_events():
+    d = dims()
+    a = layer_args(d)
+    lib = moe.lib()
+    args = [ctypes.byref(d), a["x"], a["w_router"], None, a["w_gate"], a["w_up"], a["w_down"],
+            a["wsh_gate"], a["wsh_up"], a["wsh_down"], a["out"], None, None, None, None, None,
+            a["ws"], a["ws_bytes"], 0]
+    b = Bufs()
+    side, fork, join = b(), b(), b()  # never dereferenced: validation fails first
+    assert lib.moe_layer_fwd_overlap(*args, None, fork, join) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_fwd_overlap(*args, side, None, join) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_fwd_overlap(*args, side, fork, None) == moe.MOE_ERR_INVALID_ARG
+    bad = list(args)
+    bad[-2] = 1024  # workspace too small: rejected before any event or launch
+    assert lib.moe_layer_fwd_overlap(*bad, side, fork, join) == moe.MOE_ERR_WORKSPACE
 
 
 def test_timed_layer_rejects_bad_event_list():

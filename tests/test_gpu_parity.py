@@ -199,6 +199,18 @@ def test_layer_is_deterministic(name):
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
 
 
+@pytest.mark.parametrize("name", ALL)
+def test_layer_overlap_matches_single_stream(name):
+    """The shared experts on a second stream give bit-identical results (same
+    kernels and tiles, only the launch streams differ), on two calls in a row."""
+    cfg, arrays, ref, lay = case(name)
+    a = lay.layer()
+    for _ in range(2):
+        b = lay.layer_overlap()
+        for key in a:
+            np.testing.assert_array_equal(b[key], a[key], err_msg=key)
+
+
 def test_down_projection_scaling_is_exact():
     cfg, arrays, ref, lay = case("med_bf16_shared")
     a = lay.layer()
