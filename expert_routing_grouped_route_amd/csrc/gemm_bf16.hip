@@ -21,10 +21,12 @@
 //            columns, so the epilogue forms bf16(silu(g) * u) in registers;
 //   down:    256 output columns of y, fp32.
 // Operands stream global -> LDS with the gfx950 direct 16-byte LDS loads (no
-// register staging) through two K-stages of 64 (64 KB each), one barrier per
-// stage.  The loads of the next stage are spread between the MFMAs of the
-// current one, so no wave stalls on a full memory queue while its matrix core
-// idles; fragment reads run one K-sub-step ahead of the MFMAs that use them.
+// register staging) in K-steps of 64, one barrier per step: the A rows through
+// three 32 KB buffers, loaded two steps ahead, the weight rows through two,
+// loaded one step ahead (160 KB of LDS in all).  The loads are spread between
+// the MFMAs of the current step, so no wave stalls on a full memory queue
+// while its matrix core idles; fragment reads run one K-sub-step ahead of the
+// MFMAs that use them.
 // Each 128-byte LDS row holds its eight 16-byte K-chunks in an order permuted
 // by (row / 2 mod 8), which keeps the 32-row fragment reads free of bank
 // conflicts.  The gate/up epilogue stores from registers; the down epilogue
@@ -48,8 +50,14 @@ constexpr int BN = 256;                         // weight rows per tile
 constexpr int GU_COLS = BN / 2;                 // gate/up: output columns per tile
 constexpr int ROW_BYTES = BK * 2;               // one LDS row: 64 bf16
 constexpr int X_BYTES = kBM * ROW_BYTES;        // 32 KB
-constexpr int STAGE_BYTES = (kBM + BN) * ROW_BYTES;  // 64 KB
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;      // 128 KB
+// The A rows (X) are the deep operand: three buffers, loaded two K-steps
+// ahead; the weight rows have two buffers and are loaded one step ahead.
+constexpr bool DEEP_X = true;
+constexpr int W_BYTES = BN * ROW_BYTES;         // 32 KB
+constexpr int NXB = DEEP_X ? 3 : 2;             // buffers of the A rows (X) ...
+constexpr int NWB = DEEP_X ? 2 : 3;             // ... and of the weight rows
+constexpr int W_BASE = NXB * X_BYTES;
+constexpr int LDS_BYTES = NXB * X_BYTES + NWB * W_BYTES;  // 160 KB
 
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
@@ -230,18 +238,16 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
     return t.kps ? (size_t)(kt / t.kps) * t.w_seg + (size_t)(kt % t.kps) * ROW_BYTES
                  : (size_t)kt * ROW_BYTES;
   };
-  // direct load q (0..LOADS-1) of K-step kt; wstep = w_step(kt)
-  auto issue = [&](int kt, size_t wstep, int q) {
-    uint8_t* st = smem + (kt & 1) * STAGE_BYTES;
-    if (q < XLOADS) {
-      __builtin_amdgcn_global_load_lds(xsrc[q] + (size_t)kt * ROW_BYTES,
-                                       (lds_void_t)(st + (wave * (8 * XLOADS) + q * 8) * ROW_BYTES), 16, 0, 0);
-    } else {
-      const int w = q - XLOADS;
-      __builtin_amdgcn_global_load_lds(wbase + wstep + woff[w],
-                                       (lds_void_t)(st + X_BYTES + (wave * (8 * WLOADS) + w * 8) * ROW_BYTES),
-                                       16, 0, 0);
-    }
+  // direct loads of K-step kt: X load q (0..XLOADS-1), weight load q (0..WLOADS-1)
+  auto issue_x = [&](int kt, int q) {
+    __builtin_amdgcn_global_load_lds(xsrc[q] + (size_t)kt * ROW_BYTES,
+                                     (lds_void_t)(smem + (kt % NXB) * X_BYTES +
+                                                  (wave * (8 * XLOADS) + q * 8) * ROW_BYTES), 16, 0, 0);
+  };
+  auto issue_w = [&](int kt, size_t wstep, int q) {
+    __builtin_amdgcn_global_load_lds(wbase + wstep + woff[q],
+                                     (lds_void_t)(smem + W_BASE + (kt % NWB) * W_BYTES +
+                                                  (wave * (8 * WLOADS) + q * 8) * ROW_BYTES), 16, 0, 0);
   };
 
   // ---- fragments (bytes within a stage).  MFMA 32x32x16: lane l reads row
@@ -255,7 +261,7 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int wrow = GATE_UP ? j * GU_COLS + wn * 32 : wn * 64 + j * 32;
-    b_off[j] = X_BYTES + (wrow + r32) * ROW_BYTES;
+    b_off[j] = (wrow + r32) * ROW_BYTES;
   }
 
   f32x16 acc[4][2];
@@ -266,26 +272,35 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // One K-step out of the stage of kt; with MORE, the loads of step kt+1 are
-  // spread between its MFMAs (2 per sub-step, one after every fourth MFMA).
+  // One K-step.  The deep operand (three buffers) is loaded two steps ahead,
+  // the other (two buffers) one step ahead; during step kt this wave issues
+  // the shallow loads of step kt+1 first (MS), then the deep loads of step
+  // kt+2 (MD), spread between its MFMAs.  WD: the deep loads of step kt+1 may
+  // still be in flight at the top of step kt.
   // XL: this wave's 32 A rows hold valid rows, so it loads them; MM: its 128
   // output rows hold valid rows, so it computes.  Rows past the tile's valid
   // ones cost neither loads nor, in 128-row halves, matrix-core time.
-  auto step = [&](int kt, auto more_c, auto xl_c, auto mm_c) {
-    constexpr bool MORE = decltype(more_c)::value;
+  constexpr int NS_LOADS = DEEP_X ? WLOADS : XLOADS;  // shallow loads per wave and step
+  auto step = [&](int kt, auto ms_c, auto md_c, auto wd_c, auto xl_c, auto mm_c) {
+    constexpr bool MS = decltype(ms_c)::value;
+    constexpr bool MD = decltype(md_c)::value;
+    constexpr bool WD = decltype(wd_c)::value;
     constexpr bool XL = decltype(xl_c)::value;
     constexpr bool MM = decltype(mm_c)::value;
-    const size_t wnext = MORE ? w_step(kt + 1) : 0;
-    wait_all_loads();  // this wave's loads of step kt have landed, and its reads of step kt-1
-    block_barrier();   // everyone's: stage kt & 1 is full and stage (kt+1) & 1 is free
-    const uint8_t* st = smem + (kt & 1) * STAGE_BYTES;
+    constexpr int NDEEP = DEEP_X ? (XL ? XLOADS : 0) : WLOADS;  // this wave's deep loads per step
+    const size_t wnext = (DEEP_X ? MS : MD) ? w_step(kt + (DEEP_X ? 1 : 2)) : 0;
+    if (WD) __builtin_amdgcn_s_waitcnt((NDEEP & 0xF) | (0x7 << 4));  // vmcnt(NDEEP) lgkmcnt(0)
+    else wait_all_loads();
+    block_barrier();  // everyone's loads of step kt have landed; step kt-1's buffers are free
+    const uint8_t* xs_ = smem + (kt % NXB) * X_BYTES;
+    const uint8_t* ws_ = smem + W_BASE + (kt % NWB) * W_BYTES;
     bf16x8 F[2][6];
     auto rd = [&](int ks, bf16x8 (&f)[6]) {
       const int c = (((ks * 2 + kg) ^ cx) << 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = as_bf16x8(ld_u32x4(st + a_off[i] + c));
+      for (int i = 0; i < 4; ++i) f[i] = as_bf16x8(ld_u32x4(xs_ + a_off[i] + c));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) f[4 + j] = as_bf16x8(ld_u32x4(st + b_off[j] + c));
+      for (int j = 0; j < 2; ++j) f[4 + j] = as_bf16x8(ld_u32x4(ws_ + b_off[j] + c));
     };
     if (MM) rd(0, F[0]);
     __builtin_amdgcn_sched_barrier(0);  // sub-step 0's reads issue before any prefetch
@@ -299,22 +314,29 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
           for (int j = 0; j < 2; ++j)
             acc[i][j] = mfma_32x32x16_bf16(F[ks & 1][4 + j], F[ks & 1][i], acc[i][j]);
       }
-      if (MORE) {
+      // sub-steps 0, 1: the shallow loads; 2, 3: the deep loads (two each)
+      bool has[2] = {false, false};
 #pragma unroll
-        for (int u = 0; u < LOADS / 4; ++u) {
-          const int q = ks * (LOADS / 4) + u;
-          if (XL || q >= XLOADS) issue(kt + 1, wnext, q);
+      for (int u = 0; u < 2; ++u) {
+        const int q = (ks & 1) * 2 + u;
+        if (ks < 2) {
+          if (MS) {
+            if (DEEP_X) { issue_w(kt + 1, wnext, q); has[u] = true; }
+            else if (XL) { issue_x(kt + 1, q); has[u] = true; }
+          }
+        } else {
+          if (MD) {
+            if (DEEP_X) { if (XL) { issue_x(kt + 2, q); has[u] = true; } }
+            else { issue_w(kt + 2, wnext, q); has[u] = true; }
+          }
         }
       }
-      // schedule: the next sub-step's fragment reads first, then the MFMAs with
-      // a load after every fourth
       if (MM) {
         if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (MORE && m % 4 == 0 && (XL || ks * (LOADS / 4) + m / 4 >= XLOADS))
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          if (m % 4 == 0 && has[m / 4]) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
       }
     }
@@ -323,11 +345,27 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
   const int nk = t.nk;
   auto k_loop = [&](auto xl_c, auto mm_c) {
     constexpr bool XL = decltype(xl_c)::value;
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    // prologue: shallow loads of step 0, deep loads of steps 0 and 1 (last)
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q)
-      if (XL || q >= XLOADS) issue(0, 0, q);
-    for (int kt = 0; kt + 1 < nk; ++kt) step(kt, std::true_type{}, xl_c, mm_c);
-    step(nk - 1, std::false_type{}, xl_c, mm_c);
+    for (int q = 0; q < NS_LOADS; ++q) {
+      if (DEEP_X) issue_w(0, 0, q);
+      else if (XL) issue_x(0, q);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      if (s2 == 1 && nk < 2) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (DEEP_X) { if (XL) issue_x(s2, q); }
+        else issue_w(s2, w_step(s2), q);
+      }
+    }
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) step(kt, T_{}, T_{}, T_{}, xl_c, mm_c);
+    if (kt + 1 < nk) { step(kt, T_{}, F_{}, T_{}, xl_c, mm_c); ++kt; }
+    step(kt, F_{}, F_{}, F_{}, xl_c, mm_c);
   };
   const bool mm = wm * 128 < t.rows;  // wave-uniform
   if (wave * (8 * XLOADS) < t.rows) k_loop(std::true_type{}, std::true_type{});
