@@ -213,6 +213,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="deepseek_v2_lite", choices=list(moe_synth.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="time only the one-stream layer (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter scale)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -290,16 +292,18 @@ def main():
                                   dev["wsh_down"], out, None, None, None, None, None, ws, ws_bytes,
                                   side, fork, join, stream)
 
-    for _ in range(args.warmup):
-        step_overlap()
-    torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps, shared experts on a second stream",
-          file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step_overlap()
-    torch.cuda.synchronize()
-    wall_overlap = time.perf_counter() - t0
+    wall_overlap = float("inf")
+    if not args.no_overlap:
+        for _ in range(args.warmup):
+            step_overlap()
+        torch.cuda.synchronize()
+        print(f"[bench] timing {args.steps} steps, shared experts on a second stream",
+              file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step_overlap()
+        torch.cuda.synchronize()
+        wall_overlap = time.perf_counter() - t0
 
     stage_ms = {s: 0.0 for s in STAGES}
     for ev in events:
@@ -307,9 +311,10 @@ def main():
             stage_ms[s] += ev[j].elapsed_time(ev[j + 1]) / args.steps
     single = {"ms_per_step": round(wall * 1e3 / args.steps, 4),
               "tokens_per_s": round(cfg.T / (wall / args.steps), 1)}
-    overlap = {"ms_per_step": round(wall_overlap * 1e3 / args.steps, 4),
-               "tokens_per_s": round(cfg.T / (wall_overlap / args.steps), 1)}
-    best = overlap if wall_overlap < wall else single
+    overlap = None if args.no_overlap else {
+        "ms_per_step": round(wall_overlap * 1e3 / args.steps, 4),
+        "tokens_per_s": round(cfg.T / (wall_overlap / args.steps), 1)}
+    best = overlap if overlap and wall_overlap < wall else single
     ms_per_step = best["ms_per_step"]
     tokens_per_s = best["tokens_per_s"]
 
