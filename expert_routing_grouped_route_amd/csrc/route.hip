@@ -111,58 +111,69 @@ __device__ __forceinline__ void topk_row16(const float* L, int E, int k, bool va
   }
 }
 
-// Logits of 16 tokens x E experts, bf16 in, fp32 accumulate on the matrix cores.
-// Eight waves split the hidden dimension (K-steps of 32 dealt round-robin);
-// each wave issues the loads of four K-steps before their MFMAs, so a block
-// has 32 K-steps of x and W_r in flight.
+// Logits of 16 * NTT tokens x E experts, bf16 in, fp32 accumulate on the
+// matrix cores.  Eight waves split the hidden dimension (K-steps of 32 dealt
+// round-robin); each wave issues the loads of its next few K-steps before
+// their MFMAs.  A block reads all of W_r once, so larger token blocks (NTT)
+// cut the router-weight traffic on long inputs.
 constexpr int kRouteWaves = 8;
-constexpr int kRouteBatch = 4;
 
-template <int NET>  // 16-expert column tiles: E <= 16 * NET
+template <int NET, int NTT>  // 16-expert column tiles (E <= 16 * NET); 16-token row tiles
 __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int T, int d, int E, int k,
     float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ wts) {
+  constexpr int TB = 16 * NTT;                  // tokens per block
   constexpr int EP = NET * 16 + 1;
-  __shared__ float part[kRouteWaves][kRouteTokens][EP];
+  constexpr int BATCH = NTT >= 4 ? 1 : 4 / NTT;  // K-steps in flight per wave
+  __shared__ float part[kRouteWaves][TB][EP];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * kRouteTokens;
+  const int t0 = blockIdx.x * TB;
   const int r = lane & 15, kq = (lane >> 4) * 8;
   // rows past T and experts past E read a valid row; their results are dropped
-  const uint16_t* xp = x + (size_t)min(t0 + r, T - 1) * d + kq;
+  const uint16_t* xp[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) xp[tt] = x + (size_t)min(t0 + tt * 16 + r, T - 1) * d + kq;
   const uint16_t* wp[NET];
 #pragma unroll
   for (int et = 0; et < NET; ++et) wp[et] = wr + (size_t)min(et * 16 + r, E - 1) * d + kq;
 
-  f32x4 acc[NET];
+  f32x4 acc[NTT][NET];
 #pragma unroll
-  for (int et = 0; et < NET; ++et) acc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+    for (int et = 0; et < NET; ++et) acc[tt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nks = d >> 5;
-  for (int s0 = wave; s0 < nks; s0 += kRouteWaves * kRouteBatch) {
-    u32x4 av[kRouteBatch], bv[kRouteBatch][NET];
+  for (int s0 = wave; s0 < nks; s0 += kRouteWaves * BATCH) {
+    u32x4 av[BATCH][NTT], bv[BATCH][NET];
 #pragma unroll
-    for (int u = 0; u < kRouteBatch; ++u) {
+    for (int u = 0; u < BATCH; ++u) {
       const int s = min(s0 + u * kRouteWaves, nks - 1);  // clamped steps are not used
-      av[u] = ld_u32x4(xp + s * 32);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) av[u][tt] = ld_u32x4(xp[tt] + s * 32);
 #pragma unroll
       for (int et = 0; et < NET; ++et) bv[u][et] = ld_u32x4(wp[et] + s * 32);
     }
 #pragma unroll
-    for (int u = 0; u < kRouteBatch; ++u) {
+    for (int u = 0; u < BATCH; ++u) {
       if (s0 + u * kRouteWaves < nks) {
 #pragma unroll
-        for (int et = 0; et < NET; ++et)
-          acc[et] = mfma_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u][et]), acc[et]);
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+          for (int et = 0; et < NET; ++et)
+            acc[tt][et] = mfma_16x16x32_bf16(as_bf16x8(av[u][tt]), as_bf16x8(bv[u][et]), acc[tt][et]);
       }
     }
   }
 #pragma unroll
-  for (int et = 0; et < NET; ++et)
+  for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) part[wave][(lane >> 4) * 4 + q][et * 16 + r] = acc[et][q];
+    for (int et = 0; et < NET; ++et)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) part[wave][tt * 16 + (lane >> 4) * 4 + q][et * 16 + r] = acc[tt][et][q];
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < kRouteTokens * E; idx += 64 * kRouteWaves) {
+  for (int idx = threadIdx.x; idx < TB * E; idx += 64 * kRouteWaves) {
     const int t = idx / E, e = idx - t * E;
     float v = part[0][t][e];
 #pragma unroll
@@ -172,10 +183,14 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
     if (logits_out && t0 + t < T) logits_out[(size_t)(t0 + t) * E + e] = v;
   }
   __syncthreads();
-  if (wave < kRouteTokens / 4) {  // one token per 16-lane row: 4 rows per wave
-    const int t = wave * 4 + (lane >> 4);
-    const size_t tg = (size_t)min(t0 + t, T - 1);
-    topk_row16<NET>(&part[0][t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
+  // one token per 16-lane row: 32 tokens per pass of the 8 waves
+#pragma unroll
+  for (int p0 = 0; p0 < TB; p0 += 4 * kRouteWaves) {
+    const int t = p0 + wave * 4 + (lane >> 4);
+    if (t < TB) {  // wave-uniform
+      const size_t tg = (size_t)min(t0 + t, T - 1);
+      topk_row16<NET>(&part[0][t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
+    }
   }
 }
 
@@ -264,14 +279,28 @@ void launch_route(const RouteArgs& a, hipStream_t stream) {
   }
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
-#define MOE_ROUTE_CASE(N)                                                                   \
-  hipLaunchKernelGGL(route_bf16_kernel<N>, dim3(grid), dim3(64 * kRouteWaves), 0, stream, x, wr, \
-                     a.bias, (int)a.T, a.d, a.E, a.k, a.logits_out, a.ids, a.wts)
-  if (a.E <= 16) MOE_ROUTE_CASE(1);
-  else if (a.E <= 32) MOE_ROUTE_CASE(2);
-  else if (a.E <= 64) MOE_ROUTE_CASE(4);
-  else if (a.E <= 128) MOE_ROUTE_CASE(8);
-  else MOE_ROUTE_CASE(16);
+  // tokens per block: 16 while that still gives a block per CU, more on long
+  // inputs (each block reads all of W_r), within the LDS of the partial sums
+  const int net = a.E <= 16 ? 1 : a.E <= 32 ? 2 : a.E <= 64 ? 4 : a.E <= 128 ? 8 : 16;
+  int ntt = a.T <= 4096 ? 1 : a.T <= 16384 ? 2 : 4;
+  if (net == 8) ntt = ntt < 2 ? ntt : 2;
+  if (net == 16) ntt = 1;
+  const int grid_tb = (int)((a.T + 16 * ntt - 1) / (16 * ntt));
+#define MOE_ROUTE_CASE(N, M)                                                                     \
+  hipLaunchKernelGGL((route_bf16_kernel<N, M>), dim3(grid_tb), dim3(64 * kRouteWaves), 0, stream, \
+                     x, wr, a.bias, (int)a.T, a.d, a.E, a.k, a.logits_out, a.ids, a.wts)
+#define MOE_ROUTE_NTT(N)                   \
+  if (ntt == 1) MOE_ROUTE_CASE(N, 1);      \
+  else if (ntt == 2) MOE_ROUTE_CASE(N, 2); \
+  else MOE_ROUTE_CASE(N, 4)
+  if (net == 1) { MOE_ROUTE_NTT(1); }
+  else if (net == 2) { MOE_ROUTE_NTT(2); }
+  else if (net == 4) { MOE_ROUTE_NTT(4); }
+  else if (net == 8) {
+    if (ntt == 1) MOE_ROUTE_CASE(8, 1);
+    else MOE_ROUTE_CASE(8, 2);
+  } else MOE_ROUTE_CASE(16, 1);
+#undef MOE_ROUTE_NTT
 #undef MOE_ROUTE_CASE
 }
 
