@@ -3,16 +3,22 @@
 
 A step is one whole layer: route, dispatch, grouped gate/up GEMM with the
 SwiGLU epilogue, grouped down GEMM (routed and shared experts), combine, with
-inputs already resident in HBM.  It is timed two ways: all on one stream
-through ``moe_layer_fwd_timed`` (which also gives the per-stage times), and
-with the shared experts on a second stream through ``moe_layer_fwd_overlap``;
-``value`` is the faster of the two, and both are reported.  The default workload is the DeepSeek-V2-Lite-shaped
-layer (T=4096, d=2048, 64 experts top-6 + 2 shared, I=1408), bf16 inputs with
-fp32 accumulation, synthetic seeded data.
+inputs already resident in HBM.  After an untimed device warm-up of at least
+0.5 s (the GPU's clocks ramp up after the host-side set-up), it is timed in
+three passes of the same number of steps:
+- all on one stream through ``moe_layer_fwd``;
+- with the shared experts on a second stream through ``moe_layer_fwd_overlap``
+  (only for layers that have shared experts);
+- on one stream through ``moe_layer_fwd_timed``, which records HIP events
+  between the stages.
+``value`` is the faster of the first two, which carry no instrumentation; all
+three are reported.  The default workload is the DeepSeek-V2-Lite-shaped layer
+(T=4096, d=2048, 64 experts top-6 + 2 shared, I=1408), bf16 inputs with fp32
+accumulation, synthetic seeded data.
 
-Prints one JSON line.  Per-stage times come from HIP events that the library
-records on the layer's stream between its kernels, averaged over the timed
-steps.  The oracle (fp64 NumPy on the host cores) is timed on a bounded token
+Prints one JSON line.  Per-stage times come from the third pass: HIP events
+that the library records on the layer's stream between its kernels, averaged
+over its timed steps.  The oracle (fp64 NumPy on the host cores) is timed on a bounded token
 sample of the same workload as a CPU baseline.
 """
 import argparse
@@ -263,22 +269,16 @@ def main():
         for e in step_ev:
             e.record(stream)  # creates the underlying hipEvent_t
 
-    def step(ev):
+    def step_timed(ev):
         moe.moe_layer_fwd_timed(d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
                                 dev["w_down"], dev["wsh_gate"], dev["wsh_up"], dev["wsh_down"], out,
                                 None, None, None, None, None, ws, ws_bytes,
                                 [e.cuda_event for e in ev], stream)
 
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step(events[0])
-    torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    def step_single():
+        moe.moe_layer_fwd(d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
+                          dev["w_down"], dev["wsh_gate"], dev["wsh_up"], dev["wsh_down"], out,
+                          None, None, None, None, None, ws, ws_bytes, stream)
 
     # the same layer with the shared experts on a second stream (moe_layer_fwd_overlap)
     side = torch.cuda.Stream()
@@ -292,28 +292,48 @@ def main():
                                   dev["wsh_down"], out, None, None, None, None, None, ws, ws_bytes,
                                   side, fork, join, stream)
 
-    wall_overlap = float("inf")
-    if not args.no_overlap:
+    def timed(label, fn):
+        # args.warmup untimed calls, then args.steps calls between two synchronisations
         for _ in range(args.warmup):
-            step_overlap()
+            fn(0)
         torch.cuda.synchronize()
-        print(f"[bench] timing {args.steps} steps, shared experts on a second stream",
-              file=sys.stderr, flush=True)
+        print(f"[bench] timing {args.steps} steps: {label}", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step_overlap()
+        for i in range(args.steps):
+            fn(i)
         torch.cuda.synchronize()
-        wall_overlap = time.perf_counter() - t0
+        return time.perf_counter() - t0
+
+    # The GPU's clocks ramp up over tens of milliseconds after the host-side set-up,
+    # so the passes start from a steady state: the layer runs untimed for at least
+    # 0.5 s first (each pass still does its own W warm-up steps).
+    print("[bench] device warm-up (0.5 s of layer calls, untimed)", file=sys.stderr, flush=True)
+    n_dev_warm, t_w = 0, time.perf_counter()
+    while time.perf_counter() - t_w < 0.5:
+        for _ in range(10):
+            step_single()
+        torch.cuda.synchronize()
+        n_dev_warm += 10
+
+    # 1. the layer on one stream, no instrumentation
+    wall = timed("moe_layer_fwd", lambda i: step_single())
+    # 2. shared experts on a second stream (only where there are shared experts:
+    #    otherwise the two entry points do the same work)
+    wall_overlap = float("inf")
+    if not args.no_overlap and cfg.n_shared:
+        wall_overlap = timed("moe_layer_fwd_overlap", lambda i: step_overlap())
+    # 3. one stream with HIP events between the stages (stage times, roofline)
+    wall_timed = timed("moe_layer_fwd_timed (stage events)", lambda i: step_timed(events[i]))
 
     stage_ms = {s: 0.0 for s in STAGES}
     for ev in events:
         for j, s in enumerate(STAGES):
             stage_ms[s] += ev[j].elapsed_time(ev[j + 1]) / args.steps
-    single = {"ms_per_step": round(wall * 1e3 / args.steps, 4),
-              "tokens_per_s": round(cfg.T / (wall / args.steps), 1)}
-    overlap = None if args.no_overlap else {
-        "ms_per_step": round(wall_overlap * 1e3 / args.steps, 4),
-        "tokens_per_s": round(cfg.T / (wall_overlap / args.steps), 1)}
+    def rate(w):
+        return {"ms_per_step": round(w * 1e3 / args.steps, 4),
+                "tokens_per_s": round(cfg.T / (w / args.steps), 1)}
+    single = rate(wall)
+    overlap = rate(wall_overlap) if wall_overlap < float("inf") else None
     best = overlap if overlap and wall_overlap < wall else single
     ms_per_step = best["ms_per_step"]
     tokens_per_s = best["tokens_per_s"]
@@ -358,7 +378,9 @@ def main():
         "grouped_gemm": {"tflops": round(gemm_tflops, 1),
                          "frac_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                          "down_tflops": round(fl_dn / dn_s / 1e12, 1)},
+        "device_warmup_steps": n_dev_warm,
         "layer_variants": {"single_stream": single, "shared_on_second_stream": overlap,
+                           "single_stream_with_stage_events": rate(wall_timed),
                            "value_from": "shared_on_second_stream" if best is overlap
                            else "single_stream"},
         "stages_ms": {s: round(v, 4) for s, v in stage_ms.items()},

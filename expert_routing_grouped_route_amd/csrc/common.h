@@ -26,13 +26,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float(uint32_t(h) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
 __device__ __forceinline__ u32x4 ld_u32x4(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -57,6 +50,25 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 
 
 __device__ __forceinline__ float silu_times(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
+}
+
+// silu(g) * u with the hardware reciprocal (1 ulp) in place of an IEEE
+// division, for products that are rounded to bf16 next.  For large negative g
+// the reciprocal of +inf is 0, so the result is a signed zero, as with the
+// division.
+__device__ __forceinline__ float silu_times_rcp(float g, float u) {
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> two bf16 in one 32-bit word (lo in bits 0..15), rounded
+// to nearest, ties to even, by the gfx950 packed convert (checked against the
+// integer sequence u + 0x7FFF + ((u >> 16) & 1) on all 2^32 non-NaN inputs).
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 }  // namespace moe

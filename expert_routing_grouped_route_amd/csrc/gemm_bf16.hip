@@ -391,13 +391,12 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col = wn * 32 + 8 * q + 4 * kg;
-        uint32_t h[4];
+        float h[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          h[r] = f32_to_bf16_bits(silu_times(acc[i][0][4 * q + r], acc[i][1][4 * q + r]));
+        for (int r = 0; r < 4; ++r) h[r] = silu_times_rcp(acc[i][0][4 * q + r], acc[i][1][4 * q + r]);
         uint2 v;
-        v.x = h[0] | (h[1] << 16);
-        v.y = h[2] | (h[3] << 16);
+        v.x = pack_bf16x2_rne(h[0], h[1]);
+        v.y = pack_bf16x2_rne(h[2], h[3]);
         *reinterpret_cast<uint2*>(out + (size_t)row * t.out_ld + col) = v;
       }
     }
