@@ -8,15 +8,16 @@
 // The order inside a segment (ascending assignment index t*k + j) is a
 // reading; the pages do not fix it.
 //
-// Four kernels, no atomics on results and no host round trip:
+// Three kernels, no atomics on results and no host round trip:
 //   count:  per block of `chunk` assignments, an LDS histogram of expert ids
-//   scan:   one block; per expert, an exclusive scan over the blocks (block
-//           bases), then exclusive scans over experts of the counts
-//           (offsets) and of the M-tiles per expert, with the expert of every
-//           M-tile (the tile table of the grouped GEMMs)
-//   rank:   per block, its chunk in order, 256 assignments at a time: the
-//           stable rank within a wave from 8 ballots on the id bits, across
-//           waves from LDS counts; writes perm and inv_perm
+//   rank:   per block of the same chunk: from the histograms of all blocks
+//           (at most 256 x E ints), each expert's total and this block's base
+//           (the sum over earlier blocks), the offsets as an exclusive scan
+//           of the totals; then its chunk in order, 256 assignments at a
+//           time: the stable rank within a wave from ballots on the id bits,
+//           across waves from LDS counts; writes perm and inv_perm.  Block 0
+//           also writes counts, offsets and the M-tile table of the grouped
+//           GEMMs (M-tile prefix per expert and the expert of every M-tile).
 //   gather: one wave per sorted row, 16-byte vector copies of the token row
 #include "common.h"
 #include "kernels.h"
@@ -90,47 +91,6 @@ __device__ __forceinline__ void write_tile_table(int cnt, int E, int32_t* __rest
   if (e == E - 1) tiles[E] = tincl;
 }
 
-// Per-expert counts -> offsets [E+1], and the tile table when asked for.
-__device__ __forceinline__ void write_offsets(int cnt, int E, int32_t* __restrict__ offsets,
-                                              int32_t* __restrict__ tiles, int* buf) {
-  const int e = threadIdx.x;
-  const int incl = block_inclusive_scan(cnt, buf);
-  if (e < E) offsets[e] = incl - cnt;
-  if (e == E - 1) offsets[E] = incl;
-  __syncthreads();
-  if (tiles) write_tile_table(cnt, E, tiles, buf);
-}
-
-__global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ blk, int nblk,
-                                                            int E, int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ tiles,
-                                                            int32_t* __restrict__ ctr) {
-  __shared__ int buf[256];
-  const int e = threadIdx.x;
-  if (ctr && e < kGemmCounters) ctr[e] = 0;
-  int run = 0;
-  if (e < E) {
-    int b = 0;
-    for (; b + 4 <= nblk; b += 4) {  // four independent loads in flight
-      const int c0 = blk[(size_t)(b + 0) * E + e], c1 = blk[(size_t)(b + 1) * E + e];
-      const int c2 = blk[(size_t)(b + 2) * E + e], c3 = blk[(size_t)(b + 3) * E + e];
-      blk[(size_t)(b + 0) * E + e] = run;
-      blk[(size_t)(b + 1) * E + e] = run + c0;
-      blk[(size_t)(b + 2) * E + e] = run + c0 + c1;
-      blk[(size_t)(b + 3) * E + e] = run + c0 + c1 + c2;
-      run += c0 + c1 + c2 + c3;
-    }
-    for (; b < nblk; ++b) {
-      const int c = blk[(size_t)b * E + e];
-      blk[(size_t)b * E + e] = run;
-      run += c;
-    }
-    if (counts) counts[e] = run;
-  }
-  write_offsets(e < E ? run : 0, E, offsets, tiles, buf);
-}
-
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
                                                          int E, int32_t* __restrict__ tiles,
                                                          int32_t* __restrict__ ctr) {
@@ -142,13 +102,42 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
 }
 
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(
-    const int32_t* __restrict__ ids, int R, int E, int chunk, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ base, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm) {
+    const int32_t* __restrict__ ids, int R, int E, int chunk, const int32_t* __restrict__ blk,
+    int nblk, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ ctr, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv_perm) {
   __shared__ int run[256];     // next free row per expert for this block
   __shared__ int wc[4][256];   // per-wave counts of the current 256 assignments
+  __shared__ int buf[256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int a0 = blockIdx.x * chunk, a1 = min(R, a0 + chunk);
-  for (int e = tid; e < E; e += 256) run[e] = offsets[e] + base[(size_t)blockIdx.x * E + e];
+  // expert e's total over all blocks and its count in the blocks before this one
+  int total = 0, before = 0;
+  if (tid < E) {
+    int b = 0;
+    for (; b + 4 <= nblk; b += 4) {  // four independent loads in flight
+      const int c0 = blk[(size_t)(b + 0) * E + tid], c1 = blk[(size_t)(b + 1) * E + tid];
+      const int c2 = blk[(size_t)(b + 2) * E + tid], c3 = blk[(size_t)(b + 3) * E + tid];
+      before += (b + 0 < (int)blockIdx.x ? c0 : 0) + (b + 1 < (int)blockIdx.x ? c1 : 0) +
+                (b + 2 < (int)blockIdx.x ? c2 : 0) + (b + 3 < (int)blockIdx.x ? c3 : 0);
+      total += c0 + c1 + c2 + c3;
+    }
+    for (; b < nblk; ++b) {
+      const int c = blk[(size_t)b * E + tid];
+      before += b < (int)blockIdx.x ? c : 0;
+      total += c;
+    }
+  }
+  const int incl = block_inclusive_scan(tid < E ? total : 0, buf);
+  if (tid < E) run[tid] = incl - total + before;
+  if (blockIdx.x == 0) {
+    if (ctr && tid < kGemmCounters) ctr[tid] = 0;
+    if (counts && tid < E) counts[tid] = total;
+    if (tid < E) offsets[tid] = incl - total;
+    if (tid == E - 1) offsets[E] = incl;
+    __syncthreads();
+    if (tiles) write_tile_table(tid < E ? total : 0, E, tiles, buf);
+  }
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
   const uint64_t below = (1ull << lane) - 1ull;
   for (int p = a0; p < a1; p += 256) {
@@ -204,11 +193,11 @@ void launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
   if (nblk > 0)
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), block, 0, stream, a.ids, (int)R, a.E,
                        chunk, a.blk);
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), block, 0, stream, a.blk, nblk, a.E, a.counts,
-                     a.offsets, a.tiles, a.ctr);
+  // at least one block, so that R == 0 still writes zero counts and offsets
+  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nblk > 0 ? nblk : 1), block, 0, stream, a.ids,
+                     (int)R, a.E, chunk, a.blk, nblk, a.counts, a.offsets, a.tiles, a.ctr, a.perm,
+                     a.inv_perm);
   if (nblk == 0) return;
-  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nblk), block, 0, stream, a.ids, (int)R, a.E, chunk,
-                     a.offsets, a.blk, a.perm, a.inv_perm);
   if (a.x_sorted) {
     const int vec = (int)((size_t)a.d * a.elem_bytes / 16);
     const int64_t grid = (R + 3) / 4;

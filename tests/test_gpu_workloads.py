@@ -7,8 +7,12 @@ Checked on every workload:
   * dispatch: counts, offsets and perm are a stable counting sort of the
     GPU's ids (bit-exact against the oracle whenever routing agrees fully);
   * output: sampled token rows (random ones, the first and last token, tokens
-    of the rarest experts, tokens in the ragged last tile of the busiest
-    expert) against the oracle computed one token at a time.
+    of the rarest experts, and rows of the busiest expert's ragged last
+    256-row GEMM tile: its first rows, the rows around its 128-row half and
+    its last 32-row group, and its last rows) against the oracle computed one
+    token at a time;
+  * the two-stream entry point gives the same output bit for bit (layers with
+    shared experts).
 The fp32 workload is small enough for a full comparison."""
 import numpy as np
 import pytest
@@ -19,6 +23,9 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
+M_TILE = 256  # rows per M-tile of the bf16 grouped GEMM
+
+
 def sample_tokens(ids_ref, E, k, rng, n_random=40):
     T = ids_ref.shape[0]
     counts = np.bincount(ids_ref.ravel(), minlength=E)
@@ -27,9 +34,15 @@ def sample_tokens(ids_ref, E, k, rng, n_random=40):
     for e in nz[np.argsort(counts[nz])][:3]:  # rarest non-empty experts
         toks |= set(np.nonzero(np.any(ids_ref == e, axis=1))[0][:2].tolist())
     hot = int(np.argmax(counts))
-    rows = np.nonzero(np.any(ids_ref == hot, axis=1))[0]
-    tail = (len(rows) // 128) * 128  # first row of the busiest expert's last tile
-    toks |= set(rows[tail:tail + 3].tolist()) | set(rows[-2:].tolist())
+    rows = np.nonzero(np.any(ids_ref == hot, axis=1))[0]  # the expert's rows, in order
+    n = len(rows)
+    tail = (n - 1) // M_TILE * M_TILE  # first row of its last (ragged) M-tile
+    picks = list(range(tail, min(n, tail + 3)))          # first rows of the last tile
+    picks += [tail + 127, tail + 128]                    # around the 128-row half
+    last32 = (n - 1) // 32 * 32
+    picks += [last32 - 1, last32]                        # around the last 32-row group
+    picks += [n - 2, n - 1]                              # its last rows
+    toks |= {int(rows[i]) for i in picks if 0 <= i < n}
     return np.array(sorted(toks))
 
 
@@ -91,3 +104,9 @@ def test_workload(name):
     tol = dict(mean_abs=1e-5, max_rel=1e-4) if cfg.dtype == "f32" else {}
     ma, mr = gh.assert_fp_close(got["out"][toks], ref_out, f"{name} out", **tol)
     print(f"[workload {name}] {toks.size} rows: mean_abs={ma:.2e} max_rel={mr:.2e}", flush=True)
+
+    if cfg.n_shared:
+        got2 = lay.layer_overlap()
+        np.testing.assert_array_equal(got2["out"], got["out"])
+        np.testing.assert_array_equal(got2["ids"], got["ids"])
+        print(f"[workload {name}] two-stream output identical", flush=True)
