@@ -37,6 +37,7 @@
 // shared experts' tiles; the expert of a routed tile is one lookup in the tile
 // table the dispatch scan wrote.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "grouped_gemm.h"
@@ -67,6 +68,12 @@ constexpr int LOADS = XLOADS + WLOADS;          // 8
 constexpr int XCD_RUN = 8;                      // consecutive work indices per XCD
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
+
+// Raw buffer descriptor for an operand: base address, no stride, the full
+// 32-bit range (offsets are checked on the host), default data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, -1, 0x00020000);
+}
 
 // Position permutation of the 16-byte chunks of LDS row `row`.
 __device__ __forceinline__ int chunk_xor(int row) { return (row >> 1) & 7; }
@@ -199,7 +206,11 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
 }
 
 // One tile: pipeline fill, K loop and epilogue.
-template <bool GATE_UP>
+// BUF: the operands stream in through buffer loads (a descriptor per operand
+// and 32-bit lane offsets), which cost the address path less than 64-bit
+// global addresses; the launcher uses them when every operand offset fits in
+// 32 bits.
+template <bool GATE_UP, bool BUF>
 __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
@@ -209,13 +220,13 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
   // X: LDS rows wave*32 + q*8 + L/8 (q < 4).  Weights: LDS rows 256 + wave*32 +
   // q*8 + L/8 (q < 4): gate/up waves 0..3 load gate rows, waves 4..7 up rows.
   const int sub = lane >> 3, pos = lane & 7;
-  const uint8_t* xsrc[XLOADS];
+  size_t xoff[XLOADS];  // byte offsets from t.X (below 2^32 with BUF)
 #pragma unroll
   for (int q = 0; q < XLOADS; ++q) {
     const int row = wave * (8 * XLOADS) + q * 8 + sub;
     const int rr = min(row, t.rows - 1);
     const size_t xrow = t.rmap ? (size_t)(t.rmap[rr] / t.rdiv) : (size_t)rr;
-    xsrc[q] = t.X + xrow * t.x_ld + ((pos ^ chunk_xor(row)) << 4);
+    xoff[q] = xrow * t.x_ld + ((pos ^ chunk_xor(row)) << 4);
   }
   const uint8_t* wbase;  // wave-uniform
   int wfirst;            // first weight row of this wave within its half (gate/up) or tile (down)
@@ -239,15 +250,24 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
                  : (size_t)kt * ROW_BYTES;
   };
   // direct loads of K-step kt: X load q (0..XLOADS-1), weight load q (0..WLOADS-1)
+  const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(t.X);
+  const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(wbase);
   auto issue_x = [&](int kt, int q) {
-    __builtin_amdgcn_global_load_lds(xsrc[q] + (size_t)kt * ROW_BYTES,
-                                     (lds_void_t)(smem + (kt % NXB) * X_BYTES +
-                                                  (wave * (8 * XLOADS) + q * 8) * ROW_BYTES), 16, 0, 0);
+    const lds_void_t dst =
+        (lds_void_t)(smem + (kt % NXB) * X_BYTES + (wave * (8 * XLOADS) + q * 8) * ROW_BYTES);
+    if (BUF)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, dst, 16, (uint32_t)xoff[q],
+                                               (uint32_t)(kt * ROW_BYTES), 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(t.X + xoff[q] + (size_t)kt * ROW_BYTES, dst, 16, 0, 0);
   };
   auto issue_w = [&](int kt, size_t wstep, int q) {
-    __builtin_amdgcn_global_load_lds(wbase + wstep + woff[q],
-                                     (lds_void_t)(smem + W_BASE + (kt % NWB) * W_BYTES +
-                                                  (wave * (8 * WLOADS) + q * 8) * ROW_BYTES), 16, 0, 0);
+    const lds_void_t dst = (lds_void_t)(smem + W_BASE + (kt % NWB) * W_BYTES +
+                                        (wave * (8 * WLOADS) + q * 8) * ROW_BYTES);
+    if (BUF)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 16, woff[q], (uint32_t)wstep, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(wbase + wstep + woff[q], dst, 16, 0, 0);
   };
 
   // ---- fragments (bytes within a stage).  MFMA 32x32x16: lane l reads row
@@ -452,7 +472,7 @@ __device__ __forceinline__ int xcd_remap(int bid) {
 // launch of the shared experts' tiles alone reads nothing the dispatch writes
 // (it may run before the dispatch); a launch of the routed tiles alone stops
 // before the shared ones.
-template <bool GATE_UP>
+template <bool GATE_UP, bool BUF>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, GemmGrid g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int n_routed = p.part == kSharedTiles ? 0 : p.tile_off[p.E] * g.nt_r;
@@ -462,7 +482,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, 
   BTile t;
   if (GATE_UP) gate_up_tile(p, g, L, n_routed, t);
   else down_tile(p, g, L, n_routed, t);
-  run_tile<GATE_UP>(t, smem);
+  run_tile<GATE_UP, BUF>(t, smem);
 }
 
 GemmGrid bf16_gate_up_grid(const FfnArgs& a) {
@@ -504,18 +524,37 @@ int64_t launch_slots(const FfnArgs& a, const GemmGrid& g) {
   return n ? pad_slots(n) : 0;
 }
 
+// Whether every byte offset a tile adds to its operand bases fits in 32 bits:
+// the gathered token rows span all of x (T*d*2 bytes); other A and weight
+// tiles span at most 256 rows of d, I or n_s*I_s elements plus one row; the
+// shared experts' down tiles walk across all their down weights.
+// MOE_GEMM_GLOBAL_LOADS=1 in the environment forces the global-load variant
+// (read at every launch, so that a test can compare both variants).
+bool buffer_offsets_fit(const FfnArgs& a) {
+  const char* force = std::getenv("MOE_GEMM_GLOBAL_LOADS");
+  if (force && force[0] == '1') return false;
+  const uint64_t lim = 1ull << 32;
+  const uint64_t w = (uint64_t)std::max(std::max(a.d, a.I), a.ns * a.Is);
+  const uint64_t tile = 514 * w;  // a tile's rows plus the K offset, with margin
+  return (uint64_t)a.T * a.d * 2 + tile < lim && (uint64_t)a.ns * a.d * a.Is * 2 + tile < lim;
+}
+
 void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream) {
   const int64_t slots = launch_slots(a, bf16_gate_up_grid(a));
   if (slots == 0) return;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3((unsigned)slots), dim3(NTHREADS), 0,
-                     stream, a, bf16_gate_up_grid(a));
+  auto kern = buffer_offsets_fit(a) ? grouped_gemm_bf16_kernel<true, true>
+                                    : grouped_gemm_bf16_kernel<true, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a,
+                     bf16_gate_up_grid(a));
 }
 
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream) {
   const int64_t slots = launch_slots(a, bf16_down_grid(a));
   if (slots == 0) return;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3((unsigned)slots), dim3(NTHREADS), 0,
-                     stream, a, bf16_down_grid(a));
+  auto kern = buffer_offsets_fit(a) ? grouped_gemm_bf16_kernel<false, true>
+                                    : grouped_gemm_bf16_kernel<false, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a,
+                     bf16_down_grid(a));
 }
 
 }  // namespace moe

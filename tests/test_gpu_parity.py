@@ -13,7 +13,8 @@ from moe_synth import MoEShape
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    # several 128-row tiles per expert, 3 column tiles, one shared expert
+    # about 175 rows per expert (one ragged 256-row tile each), 3 column tiles,
+    # one shared expert
     "med_bf16_shared": MoEShape("med_bf16_shared", T=700, d=256, E=16, k=4, I=384, n_shared=1,
                                 I_shared=256, seed=11, bias="normal"),
     # column counts that end half way through a 128-wide tile, two shared experts
@@ -197,6 +198,23 @@ def test_layer_is_deterministic(name):
     b = lay.layer()
     for key in a:
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+@pytest.mark.parametrize("name", ["med_bf16_shared", "med_bf16_zipf", "one_expert"])
+def test_gemm_load_variants_agree(name, monkeypatch):
+    """The bf16 grouped GEMMs have two operand-load variants: buffer loads with
+    32-bit offsets (used whenever every offset fits) and 64-bit global loads
+    (otherwise; forced here through MOE_GEMM_GLOBAL_LOADS=1).  Both give the
+    same layer and grouped-FFN outputs bit for bit."""
+    cfg, arrays, ref, lay = case(name)
+    a, fa = lay.layer(), lay.ffn(ref["x_sorted"], ref["offsets"])
+    monkeypatch.setenv("MOE_GEMM_GLOBAL_LOADS", "1")
+    b, fb = lay.layer(), lay.ffn(ref["x_sorted"], ref["offsets"])
+    monkeypatch.delenv("MOE_GEMM_GLOBAL_LOADS")
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    for key in fa:
+        np.testing.assert_array_equal(fa[key], fb[key], err_msg=key)
 
 
 @pytest.mark.parametrize("name", ALL)
