@@ -22,10 +22,12 @@ takes these readings:
     key is set when its projection onto caller-given hyperplane b is >= 0
     (sign random projections; the hyperplanes are an input, like any random
     draw of the method);
-  * representative: c(t) is the smallest t' <= t with key(t') == key(t) and
-    cos(x_t, x_t') >= h (t itself when there is none); then rep(t) = c(t)
-    when c(c(t)) == c(t), else t, so that every condensed token maps to a
-    token that is computed;
+  * representative: the members of a key bucket in ascending token order
+    m_0 < m_1 < ...; for t = m_i, c(t) is the first m_j with j < min(i, C)
+    and cos(x_t, x_{m_j}) >= h (t itself when there is none), where C = 32
+    bounds the similarity checks per token; then rep(t) = c(t) when
+    c(c(t)) == c(t), else t, so that every condensed token maps to a token
+    that is computed;
   * an assignment (t, j) is condensed when rep(t) != t and rep(t) is routed to
     the same expert; it then reuses the expert output of that assignment of
     rep(t).  Its own gate weight still applies, and the shared experts run on
@@ -41,9 +43,11 @@ import numpy as np
 from . import moe_oracle as _m
 
 KEY_BITS = 16
+CANDIDATES = 32  # only the first CANDIDATES members of a key bucket can be representatives
 
 __all__ = [
     "KEY_BITS",
+    "CANDIDATES",
     "projections",
     "condense_keys",
     "cosine",
@@ -79,7 +83,8 @@ def cosine(a, b) -> float:
     return float(a @ b / (na * nb))
 
 
-def condense_reps(x, keys, cos_threshold: float, cos_fn=None) -> np.ndarray:
+def condense_reps(x, keys, cos_threshold: float, cos_fn=None,
+                  candidates: int = CANDIDATES) -> np.ndarray:
     """rep[t] by the two-step rule of the module docstring.  ``cos_fn(t, t2)``
     overrides the cosine (for tests that fix similarities by hand)."""
     x = np.asarray(x)
@@ -90,8 +95,9 @@ def condense_reps(x, keys, cos_threshold: float, cos_fn=None) -> np.ndarray:
             return cosine(x[t], x[t2])
     cand = np.arange(T)
     for t in range(T):
-        for t2 in range(t):  # the smallest qualifying t2 wins
-            if keys[t2] == keys[t] and cos_fn(t, t2) >= cos_threshold:
+        earlier = [t2 for t2 in range(t) if keys[t2] == keys[t]]  # ascending
+        for t2 in earlier[:candidates]:  # the first qualifying member wins
+            if cos_fn(t, t2) >= cos_threshold:
                 cand[t] = t2
                 break
     rep = np.where(cand[cand] == cand, cand, np.arange(T))

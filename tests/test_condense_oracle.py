@@ -82,6 +82,20 @@ def test_chain_is_cut():
     assert rep.tolist() == [0, 0, 2]
 
 
+def test_only_the_first_32_bucket_members_can_be_representatives():
+    # 34 mutually orthogonal rows share a key; row 34 copies member 33 (past
+    # the first 32) and stays its own representative, row 35 copies member 31
+    assert oc.CANDIDATES == 32
+    d = 40
+    x = np.zeros((36, d))
+    x[np.arange(34), np.arange(34)] = 1.0
+    x[34] = x[33]
+    x[35] = x[31]
+    rep = oc.condense_reps(x, np.zeros(36, np.int64), 0.9)
+    assert rep[:34].tolist() == list(range(34))
+    assert rep[34] == 34 and rep[35] == 31
+
+
 def test_different_keys_never_condense_and_zero_rows_stay():
     x = np.ones((4, 3))
     x[3] = 0.0
