@@ -26,7 +26,8 @@ MOE_ERR_HIP = 4
 
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
                 "moe_grouped_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_fwd_timed",
-                "moe_layer_fwd_overlap")
+                "moe_layer_fwd_overlap", "moe_condensed_workspace_bytes",
+                "moe_layer_fwd_condensed")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -69,6 +70,10 @@ _SIGS = {
                                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, _P]),
     "moe_layer_fwd_overlap": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _P]),
+    "moe_condensed_workspace_bytes": (ctypes.c_size_t, [_DIMS]),
+    "moe_layer_fwd_condensed": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                               ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P,
+                                               ctypes.c_size_t, _P]),
 }
 
 
@@ -186,3 +191,22 @@ def moe_layer_fwd_overlap(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_down
                                      _ptr(perm_out), _ptr(ws), int(ws_bytes), _stream(stream),
                                      _stream(side), ev(fork), ev(join))
     _check("moe_layer_fwd_overlap", st)
+
+
+def moe_condensed_workspace_bytes(d: moe_dims_t) -> int:
+    return int(lib().moe_condensed_workspace_bytes(ctypes.byref(d)))
+
+
+def moe_layer_fwd_condensed(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_down, wsh_gate,
+                            wsh_up, wsh_down, hyperplanes, cos_threshold, out, topk_ids_out,
+                            topk_w_out, counts_out, offsets_out, perm_out, rep_out, ws, ws_bytes,
+                            stream=None):
+    """The layer with token condensation; ``hyperplanes`` is [16, d] in the dtype of x."""
+    st = lib().moe_layer_fwd_condensed(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(bias),
+                                       _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(wsh_gate),
+                                       _ptr(wsh_up), _ptr(wsh_down), _ptr(hyperplanes),
+                                       float(cos_threshold), _ptr(out), _ptr(topk_ids_out),
+                                       _ptr(topk_w_out), _ptr(counts_out), _ptr(offsets_out),
+                                       _ptr(perm_out), _ptr(rep_out), _ptr(ws), int(ws_bytes),
+                                       _stream(stream))
+    _check("moe_layer_fwd_condensed", st)

@@ -48,8 +48,21 @@ int dispatch_blocks(int64_t R) {
   return (int)((R + c - 1) / c);
 }
 
+// Token condensation: assignment a = t*k + j (expert e) is condensed when the
+// token's representative is another token that is also routed to e.
+__device__ __forceinline__ bool is_condensed(const int32_t* __restrict__ ids,
+                                             const int32_t* __restrict__ rep, int k, int a, int e) {
+  if (!rep) return false;
+  const int t = a / k, r = rep[t];
+  if (r == t) return false;
+  for (int j = 0; j < k; ++j)
+    if (ids[(size_t)r * k + j] == e) return true;
+  return false;
+}
+
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ ids,
                                                              int R, int E, int chunk,
+                                                             const int32_t* __restrict__ rep, int k,
                                                              int32_t* __restrict__ blk) {
   __shared__ int h[256];
   for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
@@ -57,7 +70,7 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   const int a0 = blockIdx.x * chunk, a1 = min(R, a0 + chunk);
   for (int a = a0 + threadIdx.x; a < a1; a += 256) {
     const int e = ids[a];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+    if ((unsigned)e < (unsigned)E && !is_condensed(ids, rep, k, a, e)) atomicAdd(&h[e], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) blk[(size_t)blockIdx.x * E + e] = h[e];
@@ -102,7 +115,8 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
 }
 
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(
-    const int32_t* __restrict__ ids, int R, int E, int chunk, const int32_t* __restrict__ blk,
+    const int32_t* __restrict__ ids, int R, int E, int chunk, const int32_t* __restrict__ rep,
+    int k, const int32_t* __restrict__ blk,
     int nblk, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tiles, int32_t* __restrict__ ctr, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv_perm) {
@@ -145,7 +159,7 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(
     __syncthreads();
     const int a = p + tid;
     const int e = a < a1 ? ids[a] : -1;
-    const bool ok = (unsigned)e < (unsigned)E;
+    const bool ok = (unsigned)e < (unsigned)E && !is_condensed(ids, rep, k, a, e);
     uint64_t peers = __ballot(ok);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = ok && ((e >> b) & 1);
@@ -192,10 +206,10 @@ void launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
   const dim3 block(256);
   if (nblk > 0)
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), block, 0, stream, a.ids, (int)R, a.E,
-                       chunk, a.blk);
+                       chunk, a.rep, a.k, a.blk);
   // at least one block, so that R == 0 still writes zero counts and offsets
   hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nblk > 0 ? nblk : 1), block, 0, stream, a.ids,
-                     (int)R, a.E, chunk, a.blk, nblk, a.counts, a.offsets, a.tiles, a.ctr, a.perm,
+                     (int)R, a.E, chunk, a.rep, a.k, a.blk, nblk, a.counts, a.offsets, a.tiles, a.ctr, a.perm,
                      a.inv_perm);
   if (nblk == 0) return;
   if (a.x_sorted) {

@@ -44,6 +44,10 @@ struct DispatchArgs {
   int64_t T;
   int d, E, k;
   int elem_bytes;
+  const int32_t* rep;   // or null: token condensation, [T] representative of each token;
+                        // an assignment (t, j) with rep[t] != t whose expert is among
+                        // rep[t]'s gets no row (its inv_perm entry is left for
+                        // launch_condense_inv)
 };
 void launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
@@ -105,6 +109,33 @@ inline int64_t gate_up_grid(const FfnArgs& a) {
   return a.bf16 ? gate_up_grid_bf16(a) : gate_up_grid_f32(a);
 }
 inline int64_t down_grid(const FfnArgs& a) { return a.bf16 ? down_grid_bf16(a) : down_grid_f32(a); }
+
+// Token condensation (see condense.hip): keys from 16 hyperplanes, a stable
+// radix sort of the keys, and the representative of every token.
+constexpr int kCondenseBits = 16;        // hyperplanes, key bits
+constexpr int kCondenseCandidates = 32;  // bucket members a token is compared with
+struct CondenseArgs {
+  const void* x;            // [T,d]
+  const void* hyperplanes;  // [16,d], the dtype of x
+  int64_t T;
+  int d;
+  bool bf16;
+  float cos_threshold;
+  // scratch
+  float* proj;                         // [T,16]
+  int32_t* pids;                       // [T]
+  float* pwts;                         // [T]
+  int32_t *key, *key_lo, *key_hi;      // [T] each
+  int32_t *off1, *off2;                // [257] each
+  int32_t *perm1, *inv1, *perm2, *inv2;// [T] each
+  int32_t* blk;                        // [dispatch_blocks(T), 256]
+  int32_t *tok, *skey, *cand;          // [T] each
+  int32_t* rep;                        // [T] output
+};
+void launch_condense(const CondenseArgs& a, hipStream_t stream);
+// inv_perm of every condensed assignment := the row of its source.
+void launch_condense_inv(const int32_t* ids, const int32_t* rep, int64_t R, int k, int32_t* inv,
+                         hipStream_t stream);
 
 struct CombineArgs {
   const float* y;        // [R,d]

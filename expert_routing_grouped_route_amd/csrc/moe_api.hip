@@ -50,6 +50,49 @@ Layout layout_of(const moe_dims_t& D) {
   return L;
 }
 
+// Scratch of token condensation, after the layer's own workspace.
+struct CLayout {
+  size_t proj, pids, pwts, key, key_lo, key_hi, off1, off2, perm1, inv1, perm2, inv2, blk, tok,
+      skey, cand, rep, total;
+};
+
+CLayout condense_layout_of(const moe_dims_t& D) {
+  const size_t T = (size_t)D.T;
+  CLayout C;
+  size_t o = layout_of(D).total;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  C.proj = take(T * kCondenseBits * 4);
+  C.pids = take(T * 4);
+  C.pwts = take(T * 4);
+  C.key = take(T * 4);
+  C.key_lo = take(T * 4);
+  C.key_hi = take(T * 4);
+  C.off1 = take(257 * 4);
+  C.off2 = take(257 * 4);
+  C.perm1 = take(T * 4);
+  C.inv1 = take(T * 4);
+  C.perm2 = take(T * 4);
+  C.inv2 = take(T * 4);
+  C.blk = take((size_t)dispatch_blocks((int64_t)T) * 256 * 4);
+  C.tok = take(T * 4);
+  C.skey = take(T * 4);
+  C.cand = take(T * 4);
+  C.rep = take(T * 4);
+  C.total = o;
+  return C;
+}
+
+// Token condensation inputs of a layer call.
+struct CondenseIn {
+  const void* hyperplanes;
+  float cos_threshold;
+  int32_t* rep_out;
+};
+
 FfnArgs ffn_shape(const moe_dims_t& D) {
   FfnArgs f = {};
   f.T = D.T;
@@ -124,7 +167,8 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
                        float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
                        int32_t* perm_out, void* ws, size_t ws_bytes, hipEvent_t* events,
                        int n_events, hipStream_t stream, hipStream_t side = nullptr,
-                       hipEvent_t fork = nullptr, hipEvent_t join = nullptr) {
+                       hipEvent_t fork = nullptr, hipEvent_t join = nullptr,
+                       const CondenseIn* cond = nullptr) {
   moe_status_t st = check_dims(dims);
   if (st != MOE_OK) return st;
   const moe_dims_t& D = *dims;
@@ -138,6 +182,9 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
   const size_t T = (size_t)D.T, R = T * D.k, E = D.E, d = D.d;
   const bool sh = D.n_shared > 0;
   const size_t wsh_in = (size_t)D.n_shared * D.I_shared * d * es;
+  if (cond && cond->cos_threshold != cond->cos_threshold) return MOE_ERR_INVALID_ARG;  // NaN
+  const CLayout C = cond ? condense_layout_of(D) : CLayout{};
+  const size_t ws_need = cond ? C.total : L.total;
   st = check_bufs({{x, T * d * es, true, false},
                    {w_router, E * d * es, true, false},
                    {bias, E * 4, false, false},
@@ -153,9 +200,12 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
                    {counts_out, E * 4, false, true},
                    {offsets_out, (E + 1) * 4, false, true},
                    {perm_out, R * 4, false, true},
-                   {ws, L.total, true, true}});
+                   {cond ? cond->hyperplanes : nullptr, (size_t)kCondenseBits * d * es, cond != nullptr,
+                    false},
+                   {cond ? cond->rep_out : nullptr, T * 4, false, true},
+                   {ws, ws_need, true, true}});
   if (st != MOE_OK) return st;
-  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < ws_need) return MOE_ERR_WORKSPACE;
 
   (void)hipGetLastError();
   auto mark = [&](int i) -> bool {
@@ -206,10 +256,24 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
   launch_route(ra, stream);
   if (!mark(1)) return MOE_ERR_HIP;
 
+  int32_t* rep = nullptr;
+  if (cond) {
+    rep = cond->rep_out ? cond->rep_out : at<int32_t>(ws, C.rep);
+    CondenseArgs cn = {x, cond->hyperplanes, D.T, D.d, D.dtype == MOE_BF16, cond->cos_threshold,
+                       at<float>(ws, C.proj), at<int32_t>(ws, C.pids), at<float>(ws, C.pwts),
+                       at<int32_t>(ws, C.key), at<int32_t>(ws, C.key_lo), at<int32_t>(ws, C.key_hi),
+                       at<int32_t>(ws, C.off1), at<int32_t>(ws, C.off2), at<int32_t>(ws, C.perm1),
+                       at<int32_t>(ws, C.inv1), at<int32_t>(ws, C.perm2), at<int32_t>(ws, C.inv2),
+                       at<int32_t>(ws, C.blk), at<int32_t>(ws, C.tok), at<int32_t>(ws, C.skey),
+                       at<int32_t>(ws, C.cand), rep};
+    launch_condense(cn, stream);
+  }
+
   // no row gather here: the gate/up GEMM reads the token rows through perm
   DispatchArgs da = {x, ids, counts, offsets, at<int32_t>(ws, L.tile_off), at<int32_t>(ws, L.ctr),
-                     perm, inv, nullptr, at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k, (int)es};
+                     perm, inv, nullptr, at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k, (int)es, rep};
   launch_dispatch(da, stream);
+  if (rep) launch_condense_inv(ids, rep, (int64_t)R, D.k, inv, stream);
   if (!mark(2)) return MOE_ERR_HIP;
 
   fa.perm = perm;
@@ -402,6 +466,25 @@ moe_status_t moe_layer_fwd_overlap(const moe_dims_t* dims, const void* x, const 
   return layer_fwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down, out,
                    topk_ids_out, topk_w_out, counts_out, offsets_out, perm_out, ws, ws_bytes,
                    nullptr, 0, stream, side, fork, join);
+}
+
+size_t moe_condensed_workspace_bytes(const moe_dims_t* dims) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  return condense_layout_of(*dims).total;
+}
+
+moe_status_t moe_layer_fwd_condensed(const moe_dims_t* dims, const void* x, const void* w_router,
+                                     const float* bias, const void* w_gate, const void* w_up,
+                                     const void* w_down, const void* wsh_gate, const void* wsh_up,
+                                     const void* wsh_down, const void* hyperplanes,
+                                     float cos_threshold, float* out, int32_t* topk_ids_out,
+                                     float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                                     int32_t* perm_out, int32_t* rep_out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  const CondenseIn cond = {hyperplanes, cos_threshold, rep_out};
+  return layer_fwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down, out,
+                   topk_ids_out, topk_w_out, counts_out, offsets_out, perm_out, ws, ws_bytes,
+                   nullptr, 0, stream, nullptr, nullptr, nullptr, &cond);
 }
 
 }  // extern "C"

@@ -195,6 +195,47 @@ MOE_API moe_status_t moe_layer_fwd_overlap(const moe_dims_t* dims, const void* x
                                    hipStream_t stream, hipStream_t side, hipEvent_t fork,
                                    hipEvent_t join);
 
+/* Workspace of moe_layer_fwd_condensed: moe_workspace_bytes plus the
+ * condensation scratch (about 100 bytes per token).  0 for invalid dims. */
+MOE_API size_t moe_condensed_workspace_bytes(const moe_dims_t* dims);
+
+/* moe_layer_fwd with token condensation: a routed assignment whose token is
+ * a near-duplicate of an earlier token routed to the same expert gets no row
+ * of its own and reuses that token's expert output (the Luffy review, "Core
+ * claim" and "What carries the argument": similar tokens bound for one
+ * expert send one representative, whose expert output is reused).  The
+ * result is an approximation of moe_layer_fwd; with cos_threshold > 1 it is
+ * the same computation.
+ *   Similar tokens are found in one pass (a reading; the pages' own
+ *   measurement uses training history): each token gets a 16-bit key, bit b
+ *   set when its projection onto hyperplane b is >= 0; tokens with equal keys
+ *   form a bucket in ascending token order; token t's representative is the
+ *   first of the bucket's first 32 members before t whose plain cosine with t
+ *   is >= cos_threshold (computed in fp32), unless that member is itself
+ *   condensed (then t stays).  Assignment (t, j) is condensed when t's
+ *   representative is another token routed to the same expert.
+ *   hyperplanes: [16, d], the dtype of x, device memory (the method's random
+ *     draws, passed in); required.
+ *   cos_threshold: the plain cosine bound (a [0,1]-normalised bound h is
+ *     2h - 1); NaN: MOE_ERR_INVALID_ARG.
+ *   rep_out: [T] int32 or NULL: each token's representative (itself when it
+ *     is not condensed).
+ *   counts_out, offsets_out, perm_out: the rows that exist, i.e. the
+ *     assignments that are not condensed; perm_out is written up to
+ *     offsets[E] only.  topk_ids_out, topk_w_out: as in moe_layer_fwd.
+ *   ws: ws_bytes >= moe_condensed_workspace_bytes(dims).
+ * All other arguments, errors and the asynchrony are those of moe_layer_fwd;
+ * the shared experts run on every token, uncondensed. */
+MOE_API moe_status_t moe_layer_fwd_condensed(const moe_dims_t* dims, const void* x,
+                                     const void* w_router, const float* bias,
+                                     const void* w_gate, const void* w_up, const void* w_down,
+                                     const void* wsh_gate, const void* wsh_up,
+                                     const void* wsh_down, const void* hyperplanes,
+                                     float cos_threshold, float* out, int32_t* topk_ids_out,
+                                     float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                                     int32_t* perm_out, int32_t* rep_out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

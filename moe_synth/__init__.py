@@ -49,6 +49,7 @@ _TAGS = {
     "wsh_gate": 8,
     "wsh_up": 9,
     "wsh_down": 10,
+    "condense_hyperplanes": 11,
 }
 
 WEIGHT_NAMES = ("w_gate", "w_up", "w_down")
@@ -225,6 +226,17 @@ def generate(cfg: MoEShape, names=None, workers: int = 8) -> dict:
         else:
             raise KeyError(name)
     return out
+
+
+def condense_hyperplanes(cfg: MoEShape, bits: int = 16) -> np.ndarray:
+    """The random hyperplanes of token condensation's keys: [bits, d] float32
+    draws of N(0, 1), rounded to bf16 for bf16 workloads, from a stream of
+    their own (the other inputs of ``cfg`` are unchanged by drawing them)."""
+    p = np.empty((bits, cfg.d), np.float32)
+    _normal_into(p, _rng(cfg.seed, "condense_hyperplanes"), 1.0)
+    if cfg.dtype == "bf16":
+        _round_bf16_inplace(p)
+    return p
 
 
 def to_device(arrays: dict, cfg: MoEShape, device="cuda"):

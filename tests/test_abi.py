@@ -202,3 +202,31 @@ def test_timed_layer_rejects_bad_event_list():
     assert lib.moe_layer_fwd_timed(*args, None, 3, 0) == moe.MOE_ERR_INVALID_ARG
     zero = (ctypes.c_void_p * 2)(None, None)
     assert lib.moe_layer_fwd_timed(*args, zero, 2, 0) == moe.MOE_ERR_INVALID_ARG
+
+
+def _call_condensed(d, a, hyper, thr, rep, ws_bytes):
+    return moe.lib().moe_layer_fwd_condensed(
+        ctypes.byref(d), a["x"], a["w_router"], None, a["w_gate"], a["w_up"], a["w_down"],
+        a["wsh_gate"], a["wsh_up"], a["wsh_down"], hyper, thr, a["out"], None, None, None, None,
+        None, rep, a["ws"], ws_bytes, 0)
+
+
+def test_condensed_workspace_is_larger_and_covers_the_layer():
+    d = dims()
+    assert moe.moe_condensed_workspace_bytes(d) > moe.moe_workspace_bytes(d)
+    assert moe.lib().moe_condensed_workspace_bytes(None) == 0
+
+
+def test_condensed_layer_validation():
+    d = dims()
+    a = layer_args(d)
+    hyper, rep = (1 << 44), (1 << 44) + (1 << 32)  # apart from layer_args' buffers
+    need = moe.moe_condensed_workspace_bytes(d)
+    # hyperplanes are required; the threshold must not be NaN
+    assert _call_condensed(d, a, None, 0.9, None, need) == moe.MOE_ERR_INVALID_ARG
+    assert _call_condensed(d, a, hyper, float("nan"), None, need) == moe.MOE_ERR_INVALID_ARG
+    # the plain layer's workspace is not enough
+    assert _call_condensed(d, a, hyper, 0.9, rep, moe.moe_workspace_bytes(d)) == moe.MOE_ERR_WORKSPACE
+    # rep_out must not overlap another buffer, hyperplanes must be aligned
+    assert _call_condensed(d, a, hyper, 0.9, a["x"] + 256, need) == moe.MOE_ERR_INVALID_ARG
+    assert _call_condensed(d, a, hyper + 8, 0.9, None, need) == moe.MOE_ERR_INVALID_ARG
