@@ -12,7 +12,10 @@ three passes of the same number of steps:
 - on one stream through ``moe_layer_fwd_timed``, which records HIP events
   between the stages.
 ``value`` is the faster of the first two, which carry no instrumentation; all
-three are reported.  The default workload is the DeepSeek-V2-Lite-shaped layer
+three are reported.  For workloads with duplicated rows (or with
+``--condense COS``) a fourth pass times ``moe_layer_fwd_condensed``, token
+condensation, an approximation of the layer: it is reported under
+``condensed`` with the rows it keeps, never as ``value``.  The default workload is the DeepSeek-V2-Lite-shaped layer
 (T=4096, d=2048, 64 experts top-6 + 2 shared, I=1408), bf16 inputs with fp32
 accumulation, synthetic seeded data.
 
@@ -219,6 +222,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="deepseek_v2_lite", choices=list(moe_synth.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--condense", type=float, default=None, metavar="COS",
+                    help="also time moe_layer_fwd_condensed with this cosine threshold (the "
+                         "default for workloads with duplicated rows: 0.9)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="time only the one-stream layer (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -325,6 +331,29 @@ def main():
     # 3. one stream with HIP events between the stages (stage times, roofline)
     wall_timed = timed("moe_layer_fwd_timed (stage events)", lambda i: step_timed(events[i]))
 
+    # 4. token condensation (an approximation of the layer: reported apart, never as value)
+    condensed = None
+    cos_thr = args.condense if args.condense is not None else (0.9 if cfg.dup_frac > 0 else None)
+    if cos_thr is not None:
+        hyper = torch.from_numpy(moe_synth.condense_hyperplanes(cfg)).to(wdt).cuda()
+        cws_bytes = moe.moe_condensed_workspace_bytes(d)
+        cws = torch.empty(cws_bytes, dtype=torch.uint8, device="cuda")
+        c_off = torch.empty(cfg.E + 1, dtype=torch.int32, device="cuda")
+
+        def step_condensed():
+            moe.moe_layer_fwd_condensed(d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"],
+                                        dev["w_up"], dev["w_down"], dev["wsh_gate"], dev["wsh_up"],
+                                        dev["wsh_down"], hyper, cos_thr, out, None, None, None,
+                                        c_off, None, None, cws, cws_bytes, stream)
+
+        wall_cond = timed(f"moe_layer_fwd_condensed (cos >= {cos_thr})", lambda i: step_condensed())
+        rows = int(c_off[-1].item())
+        condensed = {"cos_threshold": cos_thr, "ms_per_step": round(wall_cond * 1e3 / args.steps, 4),
+                     "tokens_per_s": round(cfg.T / (wall_cond / args.steps), 1),
+                     "rows": rows, "rows_of": cfg.T * cfg.k,
+                     "rows_frac": round(rows / (cfg.T * cfg.k), 4),
+                     "speedup_vs_exact": round(min(wall, wall_overlap) / wall_cond, 4)}
+
     stage_ms = {s: 0.0 for s in STAGES}
     for ev in events:
         for j, s in enumerate(STAGES):
@@ -384,6 +413,7 @@ def main():
                            "value_from": "shared_on_second_stream" if best is overlap
                            else "single_stream"},
         "stages_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "condensed": condensed,
         "hbm": hbm,
     }
     if not args.no_cpu_baseline:
