@@ -102,11 +102,18 @@ __global__ __launch_bounds__(256) void condense_cand_kernel(const void* __restri
   const int i = blockIdx.x * 4 + wave;
   if (i >= T) return;
   const int p = tok[i], K = skey[i];
-  int lo = 0, hi = i;  // first position of key K: skey is ascending and skey[i] == K
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (skey[mid] < K) lo = mid + 1;
-    else hi = mid;
+  // first position of key K (skey is ascending and skey[i] == K): most buckets
+  // hold a few tokens, so step back up to 32 positions, then binary search
+  int lo = i;
+  for (int s = 0; s < 32 && lo > 0 && skey[lo - 1] == K; ++s) --lo;
+  if (lo > 0 && skey[lo - 1] == K) {
+    int a = 0, b = lo - 1;  // skey[b] == K
+    while (a < b) {
+      const int mid = (a + b) >> 1;
+      if (skey[mid] < K) a = mid + 1;
+      else b = mid;
+    }
+    lo = a;
   }
   const size_t es = BF16 ? 2 : 4;
   const uint8_t* xp = static_cast<const uint8_t*>(x) + (size_t)p * d * es;

@@ -150,6 +150,25 @@ def test_threshold_above_one_is_the_plain_layer(name):
         np.testing.assert_array_equal(got[key], plain[key], err_msg=key)
 
 
+def test_one_large_bucket_condenses_to_the_first_token():
+    """300 identical rows: one key bucket far larger than the 32 candidates
+    (its first position is found by the binary-search path).  Every token
+    condenses to token 0, only token 0's assignments keep rows, and the output
+    equals the plain layer's bit for bit (identical rows give identical
+    expert outputs)."""
+    cfg = MoEShape("same_rows", T=300, d=128, E=8, k=2, I=128, n_shared=1, I_shared=64, seed=25)
+    import gpu_helpers as gh
+    a = moe_synth.generate(cfg)
+    a["x"][:] = a["x"][0]
+    hyper = moe_synth.condense_hyperplanes(cfg)
+    lay = gh.Layer(cfg, a)
+    got = run_condensed(lay, hyper, THRESHOLD)
+    np.testing.assert_array_equal(got["rep"], np.zeros(cfg.T, np.int32))
+    assert got["offsets"][-1] == cfg.k
+    plain = lay.layer()
+    np.testing.assert_array_equal(got["out"], plain["out"])
+
+
 def test_condensed_layer_is_deterministic():
     cfg, a, hyper, lay = case("dup_bf16")
     g1 = run_condensed(lay, hyper, THRESHOLD)
