@@ -21,7 +21,11 @@ accumulation, synthetic seeded data.
 
 Prints one JSON line.  Per-stage times come from the third pass: HIP events
 that the library records on the layer's stream between its kernels, averaged
-over its timed steps.  The oracle (fp64 NumPy on the host cores) is timed on a bounded token
+over its timed steps.  ``cold`` times the layer again with a 1 GiB write
+between calls (no input left in the 256 MB MALL); ``grouped_roofline`` is each
+GEMM launch's ideal time, the sum over experts of max(FLOP / bf16 peak, bytes /
+HBM peak) for this input's expert loads, and its fraction of the measured
+time.  The oracle (fp64 NumPy on the host cores) is timed on a bounded token
 sample of the same workload as a CPU baseline.
 """
 import argparse
@@ -179,6 +183,25 @@ def gemm_flops(cfg):
     return gate_up, down
 
 
+def grouped_roofline_ms(cfg, counts):
+    """Ideal time of each grouped GEMM launch at the bf16 peak and the HBM
+    peak: the sum over experts (and the shared experts) of max(FLOP / peak,
+    bytes / bandwidth), with bytes = the expert's weights, its input rows and
+    its output rows.  Returns (gate_up_ms, down_ms)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    pk, bw = PEAK_BF16_TFLOPS * 1e12, PEAK_HBM_GBS * 1e9
+    groups = [(int(n), cfg.I) for n in counts if n > 0]
+    if cfg.n_shared:
+        groups.append((cfg.T, cfg.n_shared * cfg.I_shared))
+    gu = dn = 0.0
+    for n, width in groups:
+        gu += max(4.0 * n * cfg.d * width / pk,
+                  (2 * width * cfg.d * es + n * cfg.d * es + n * width * es) / bw)
+        dn += max(2.0 * n * cfg.d * width / pk,
+                  (width * cfg.d * es + n * width * es + n * cfg.d * 4) / bw)
+    return gu * 1e3, dn * 1e3
+
+
 def cpu_baseline(cfg, arrays, budget_s=10.0, max_runs=7):
     """Time the oracle on the first Ts tokens, doubling Ts until one run takes
     at least budget_s or covers the whole workload; when the whole workload
@@ -331,6 +354,30 @@ def main():
     # 3. one stream with HIP events between the stages (stage times, roofline)
     wall_timed = timed("moe_layer_fwd_timed (stage events)", lambda i: step_timed(events[i]))
 
+    # cold: each call after a 1 GiB scrub write, so that no input sits in the
+    # 256 MB MALL; the layer alone is timed by its own first and last events
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    for step_ev in cold_ev:
+        for e in step_ev:
+            e.record(stream)
+    print(f"[bench] timing {args.steps} cold steps (scrub between calls)", file=sys.stderr, flush=True)
+    for i in range(args.steps):
+        scrub.fill_(i & 255)
+        step_timed(cold_ev[i])
+    torch.cuda.synchronize()
+    cold_ms = sum(ev[0].elapsed_time(ev[n_ev - 1]) for ev in cold_ev) / args.steps
+    cold_stage_ms = {s_: round(sum(ev[j].elapsed_time(ev[j + 1]) for ev in cold_ev) / args.steps, 4)
+                     for j, s_ in enumerate(STAGES)}
+    del scrub
+
+    # expert loads of this input, for the grouped roofline (outside every timed region)
+    cnt = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    moe.moe_layer_fwd(d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
+                      dev["w_down"], dev["wsh_gate"], dev["wsh_up"], dev["wsh_down"], out, None,
+                      None, cnt, None, None, ws, ws_bytes, stream)
+    counts_np = cnt.cpu().numpy()
+
     # 4. token condensation (an approximation of the layer: reported apart, never as value)
     condensed = None
     cos_thr = args.condense if args.condense is not None else (0.9 if cfg.dup_frac > 0 else None)
@@ -375,6 +422,7 @@ def main():
         torch.cuda.synchronize()
 
     fl_gu, fl_dn = gemm_flops(cfg)
+    grl = grouped_roofline_ms(cfg, counts_np)
     gu_s, dn_s = stage_ms["gate_up"] * 1e-3, stage_ms["down"] * 1e-3
     gu_tflops = fl_gu / gu_s / 1e12
     gemm_tflops = (fl_gu + fl_dn) / (gu_s + dn_s) / 1e12
@@ -404,6 +452,12 @@ def main():
                      "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": load_traffic(cfg.name),
                      "flops_per_launch": fl_gu, "avg_launch_ms": round(stage_ms["gate_up"], 4)},
+        "grouped_roofline": {
+            "gate_up_ideal_ms": round(grl[0], 4), "down_ideal_ms": round(grl[1], 4),
+            "gate_up_frac": round(grl[0] / stage_ms["gate_up"], 4),
+            "down_frac": round(grl[1] / stage_ms["down"], 4)},
+        "cold": {"ms_per_layer": round(cold_ms, 4), "tokens_per_s": round(cfg.T / (cold_ms * 1e-3), 1),
+                 "stages_ms": cold_stage_ms},
         "grouped_gemm": {"tflops": round(gemm_tflops, 1),
                          "frac_bf16_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                          "down_tflops": round(fl_dn / dn_s / 1e12, 1)},
