@@ -34,7 +34,8 @@
 //
 // Work order: the routed tiles of expert 0, 1, ... (within an expert n-tile
 // outer, m-tile inner, so consecutive tiles share a weight slice), then the
-// shared experts' tiles; the expert of a routed tile is one lookup in the tile
+// shared experts' tiles (for the down product the shared tiles come first,
+// being the longest); the expert of a routed tile is one lookup in the tile
 // table the dispatch scan wrote.
 #include <algorithm>
 #include <cstdlib>
@@ -470,15 +471,21 @@ __device__ __forceinline__ int xcd_remap(int bid) {
 
 // One block per work slot; slots past the device-side tile count return.  A
 // launch of the shared experts' tiles alone reads nothing the dispatch writes
-// (it may run before the dispatch); a launch of the routed tiles alone stops
-// before the shared ones.
+// (it may run before the dispatch); a launch of the routed tiles alone has no
+// shared ones.
 template <bool GATE_UP, bool BUF>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, GemmGrid g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int n_routed = p.part == kSharedTiles ? 0 : p.tile_off[p.E] * g.nt_r;
-  const int L = xcd_remap(blockIdx.x);
-  const int end = p.part == kRoutedTiles ? n_routed : n_routed + g.n_shared;
-  if (L >= end) return;
+  const int ns_t = p.part == kRoutedTiles ? 0 : g.n_shared;
+  const int end = n_routed + ns_t;
+  const int L0 = xcd_remap(blockIdx.x);
+  if (L0 >= end) return;
+  // The down product takes the shared experts' tiles first: their K runs over
+  // all shared experts (n_s * I_s, twice a routed tile's I for two shared
+  // experts), so as the last tiles of the launch they would form its tail.
+  const int first = GATE_UP ? 0 : ns_t;
+  const int L = L0 < first ? n_routed + L0 : L0 - first;
   BTile t;
   if (GATE_UP) gate_up_tile(p, g, L, n_routed, t);
   else down_tile(p, g, L, n_routed, t);
