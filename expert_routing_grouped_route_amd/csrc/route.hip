@@ -125,7 +125,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
     float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ wts) {
   constexpr int TB = 16 * NTT;                  // tokens per block
   constexpr int EP = NET * 16 + 1;
-  constexpr int BATCH = NTT >= 4 ? 1 : 4 / NTT;  // K-steps in flight per wave
+  constexpr int BATCH = NTT >= 4 ? 2 : 4 / NTT;  // K-steps in flight per wave
   __shared__ float part[kRouteWaves][TB][EP];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * TB;
