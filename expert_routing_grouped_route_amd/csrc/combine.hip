@@ -8,7 +8,10 @@
 // weighted sum.  Accumulation order (ascending slot, shared term last) is a
 // reading, fixed so that results are reproducible bit for bit.
 //
-// One wave per token; 16-byte vectors along the hidden dimension.
+// One wave per token; 16-byte vectors along the hidden dimension.  For the
+// common k (1, 2, 4, 6, 8) the kernel is specialised on k so that every row's
+// loads are issued before the sums (the generic loop serialises them behind
+// its per-slot branches); the sum order is the same in both.
 #include "common.h"
 #include "kernels.h"
 
@@ -57,9 +60,101 @@ __global__ __launch_bounds__(256) void combine_kernel(const f32x4* __restrict__ 
   }
 }
 
+// k known at compile time: every row's loads are issued before the sums.
+template <int K, int U, bool SH>
+__global__ __launch_bounds__(256) void combine_k_kernel(const f32x4* __restrict__ y,
+                                                        const int32_t* __restrict__ inv_perm,
+                                                        const float* __restrict__ w,
+                                                        const f32x4* __restrict__ ysh, int T, int R,
+                                                        int d4, f32x4* __restrict__ out) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const f32x4* src[K];
+  float wt[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int r = inv_perm[(size_t)t * K + j];
+    const bool ok = (unsigned)r < (unsigned)R;
+    src[j] = y + (size_t)(ok ? r : 0) * d4;
+    wt[j] = ok ? w[(size_t)t * K + j] : 0.0f;
+  }
+  const f32x4* s_row = SH ? ysh + (size_t)t * d4 : nullptr;
+  f32x4* o_row = out + (size_t)t * d4;
+  int c = lane;
+  for (; c + 64 * (U - 1) < d4; c += 64 * U) {
+    f32x4 v[K][U], s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < K; ++j) v[j][u] = src[j][c + 64 * u];
+    if (SH) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) s[u] = s_row[c + 64 * u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        acc[0] = fmaf(wt[j], v[j][u][0], acc[0]);
+        acc[1] = fmaf(wt[j], v[j][u][1], acc[1]);
+        acc[2] = fmaf(wt[j], v[j][u][2], acc[2]);
+        acc[3] = fmaf(wt[j], v[j][u][3], acc[3]);
+      }
+      if (SH) {
+        acc[0] += s[u][0];
+        acc[1] += s[u][1];
+        acc[2] += s[u][2];
+        acc[3] += s[u][3];
+      }
+      o_row[c + 64 * u] = acc;
+    }
+  }
+  for (; c < d4; c += 64) {
+    f32x4 v[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = src[j][c];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      acc[0] = fmaf(wt[j], v[j][0], acc[0]);
+      acc[1] = fmaf(wt[j], v[j][1], acc[1]);
+      acc[2] = fmaf(wt[j], v[j][2], acc[2]);
+      acc[3] = fmaf(wt[j], v[j][3], acc[3]);
+    }
+    if (SH) {
+      const f32x4 sv = s_row[c];
+      acc[0] += sv[0];
+      acc[1] += sv[1];
+      acc[2] += sv[2];
+      acc[3] += sv[3];
+    }
+    o_row[c] = acc;
+  }
+}
+
+constexpr int kCombineChunks = 4;  // 16-byte chunks per lane and row in flight
+template <int K>
+static void launch_k(const CombineArgs& a, int64_t grid, hipStream_t stream) {
+  auto kern = a.ysh ? combine_k_kernel<K, kCombineChunks, true> : combine_k_kernel<K, kCombineChunks, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream,
+                     reinterpret_cast<const f32x4*>(a.y), a.inv, a.w,
+                     reinterpret_cast<const f32x4*>(a.ysh), (int)a.T, (int)(a.T * a.k), a.d / 4,
+                     reinterpret_cast<f32x4*>(a.out));
+}
+
 void launch_combine(const CombineArgs& a, hipStream_t stream) {
   const int64_t grid = (a.T + 3) / 4;
   if (grid == 0) return;
+  switch (a.k) {
+    case 1: launch_k<1>(a, grid, stream); return;
+    case 2: launch_k<2>(a, grid, stream); return;
+    case 4: launch_k<4>(a, grid, stream); return;
+    case 6: launch_k<6>(a, grid, stream); return;
+    case 8: launch_k<8>(a, grid, stream); return;
+    default: break;
+  }
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                      reinterpret_cast<const f32x4*>(a.y), a.inv, a.w,
                      reinterpret_cast<const f32x4*>(a.ysh), (int)a.T, a.k, (int)(a.T * a.k),
