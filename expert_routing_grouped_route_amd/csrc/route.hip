@@ -7,10 +7,11 @@
 // FarSkip-Collective review (axiom ledger, Eq. 9).  Softmax, renormalisation
 // over the kept k and the tie rule are readings: the pages name none of them.
 //
-// One block handles 16 tokens.  bf16 logits run on the matrix cores: eight
-// waves split the hidden dimension (K-steps of 32 taken round-robin), each
-// wave holding 16 tokens x E experts of fp32 partial sums; the partials meet
-// in LDS in a fixed order.  fp32 logits run on the vector ALUs in a fixed
+// One block handles 16, 32 or 64 tokens.  bf16 logits run on the matrix
+// cores: eight waves split the hidden dimension (pairs of K-steps of 32 taken
+// round-robin, in an order rotated per block), each wave holding the block's
+// tokens x E experts of fp32 partial sums; the partials meet in LDS in a
+// fixed order.  fp32 logits run on the vector ALUs in a fixed
 // lane order.  The top-k then takes one token per 16-lane row, each slot a
 // row-wide arg-max through the VALU's cross-lane data-parallel moves.
 #include "common.h"
@@ -112,9 +113,9 @@ __device__ __forceinline__ void topk_row16(const float* L, int E, int k, bool va
 }
 
 // Logits of 16 * NTT tokens x E experts, bf16 in, fp32 accumulate on the
-// matrix cores.  Eight waves split the hidden dimension (K-steps of 32 dealt
-// round-robin); each wave issues the loads of its next few K-steps before
-// their MFMAs.  A block reads all of W_r once, so larger token blocks (NTT)
+// matrix cores.  Eight waves split the hidden dimension (pairs of K-steps of
+// 32, one 128-byte line per row, dealt round-robin); each wave issues the
+// loads of its next few K-steps before their MFMAs.  A block reads all of W_r once, so larger token blocks (NTT)
 // cut the router-weight traffic on long inputs.
 constexpr int kRouteWaves = 8;
 
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
     float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ wts) {
   constexpr int TB = 16 * NTT;                  // tokens per block
   constexpr int EP = NET * 16 + 1;
-  constexpr int BATCH = NTT >= 4 ? 2 : 4 / NTT;  // K-steps in flight per wave
+  constexpr int BATCH = NTT >= 4 ? 2 : 4 / NTT;  // K-steps in flight per wave (in pairs)
   __shared__ float part[kRouteWaves][TB][EP];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * TB;
@@ -143,25 +144,42 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
   for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
     for (int et = 0; et < NET; ++et) acc[tt][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nks = d >> 5;
-  for (int s0 = wave; s0 < nks; s0 += kRouteWaves * BATCH) {
-    u32x4 av[BATCH][NTT], bv[BATCH][NET];
+  // K-steps of 32 taken in pairs: a wave loads both 64-byte halves of each
+  // row's 128-byte line back to back, so each line is fetched for one wave
+  // rather than for two.  The pairs are rotated per block (blocks b, b+8, ...
+  // share an XCD) so that the blocks of an XCD do not all read the same lines
+  // of W_r at once.  The order of the products within each sum is fixed per
+  // block, so results are reproducible.
+  const int npair = d >> 6;
+  const int rot = (int)((blockIdx.x >> 3) % (unsigned)npair);
+  constexpr int BP = BATCH >= 2 ? BATCH / 2 : 1;  // pairs in flight per wave
+  for (int p0 = wave; p0 < npair; p0 += kRouteWaves * BP) {
+    u32x4 av[BP][NTT][2], bv[BP][NET][2];
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      const int s = min(s0 + u * kRouteWaves, nks - 1);  // clamped steps are not used
+    for (int u = 0; u < BP; ++u) {
+      int pp = min(p0 + u * kRouteWaves, npair - 1) + rot;  // clamped pairs are not used
+      if (pp >= npair) pp -= npair;
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) av[u][tt] = ld_u32x4(xp[tt] + s * 32);
+      for (int tt = 0; tt < NTT; ++tt) {
+        av[u][tt][0] = ld_u32x4(xp[tt] + pp * 64);
+        av[u][tt][1] = ld_u32x4(xp[tt] + pp * 64 + 32);
+      }
 #pragma unroll
-      for (int et = 0; et < NET; ++et) bv[u][et] = ld_u32x4(wp[et] + s * 32);
+      for (int et = 0; et < NET; ++et) {
+        bv[u][et][0] = ld_u32x4(wp[et] + pp * 64);
+        bv[u][et][1] = ld_u32x4(wp[et] + pp * 64 + 32);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) {
-      if (s0 + u * kRouteWaves < nks) {
+    for (int u = 0; u < BP; ++u) {
+      if (p0 + u * kRouteWaves < npair) {
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int et = 0; et < NET; ++et)
-            acc[tt][et] = mfma_16x16x32_bf16(as_bf16x8(av[u][tt]), as_bf16x8(bv[u][et]), acc[tt][et]);
+          for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+            for (int et = 0; et < NET; ++et)
+              acc[tt][et] = mfma_16x16x32_bf16(as_bf16x8(av[u][tt][h]), as_bf16x8(bv[u][et][h]), acc[tt][et]);
       }
     }
   }
