@@ -177,6 +177,14 @@ def stage_bytes(cfg):
     }
 
 
+def gather_dispatch_bytes(cfg):
+    """Algorithmic bytes of the standalone dispatch: x and the ids read, every
+    assignment's row written to x_sorted, perm and inv_perm written."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    R = cfg.T * cfg.k
+    return cfg.T * cfg.d * es + R * 4 + R * cfg.d * es + 2 * R * 4
+
+
 def gemm_flops(cfg):
     R = cfg.T * cfg.k
     gate_up = 4 * R * cfg.d * cfg.I + 4 * cfg.T * cfg.d * cfg.n_shared * cfg.I_shared
@@ -393,6 +401,32 @@ def main():
                       None, cnt, None, None, ws, ws_bytes, stream)
     counts_np = cnt.cpu().numpy()
 
+    # the standalone dispatch with its row gather (x_sorted written), timed by HIP events
+    # on the stream it runs on; its bytes are the full dispatch of the method
+    ids_t = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device="cuda")
+    moe.moe_layer_fwd(d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
+                      dev["w_down"], dev["wsh_gate"], dev["wsh_up"], dev["wsh_down"], out, ids_t,
+                      None, None, None, None, ws, ws_bytes, stream)
+    R = cfg.T * cfg.k
+    d_cnt = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    d_off = torch.empty(cfg.E + 1, dtype=torch.int32, device="cuda")
+    d_perm = torch.empty(R, dtype=torch.int32, device="cuda")
+    d_inv = torch.empty(R, dtype=torch.int32, device="cuda")
+    x_sorted = torch.empty(R, cfg.d, dtype=wdt, device="cuda")
+    disp_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        moe.moe_dispatch(d, dev["x"], ids_t, d_cnt, d_off, d_perm, d_inv, x_sorted, ws, ws_bytes,
+                         stream)
+    for a_, b_ in disp_ev:
+        a_.record(stream)
+        moe.moe_dispatch(d, dev["x"], ids_t, d_cnt, d_off, d_perm, d_inv, x_sorted, ws, ws_bytes,
+                         stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    disp_ms = sum(a_.elapsed_time(b_) for a_, b_ in disp_ev) / args.steps
+    del x_sorted
+
     # 4. token condensation (an approximation of the layer: reported apart, never as value)
     condensed = None
     cos_thr = args.condense if args.condense is not None else (0.9 if cfg.dup_frac > 0 else None)
@@ -450,6 +484,11 @@ def main():
     hbm = {s: {"GB/s": round(sb[s] / (stage_ms[s] * 1e-3) / 1e9, 1),
                "frac_of_8TB/s": round(sb[s] / (stage_ms[s] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                "bytes": sb[s]} for s in sb}
+    gb = gather_dispatch_bytes(cfg)
+    hbm["dispatch_with_row_gather"] = {
+        "entry_point": "moe_dispatch", "ms": round(disp_ms, 4),
+        "GB/s": round(gb / (disp_ms * 1e-3) / 1e9, 1),
+        "frac_of_8TB/s": round(gb / (disp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": gb}
 
     rec = {
         "metric": METRIC,

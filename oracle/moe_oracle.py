@@ -309,7 +309,7 @@ def moe_layer(x, w_router, bias, w_gate, w_up, w_down, k: int,
 
 def moe_layer_dense(x, logits, w_gate, w_up, w_down, k: int,
                     wsh_gate=None, wsh_up=None, wsh_down=None,
-                    round_a: bool = True) -> np.ndarray:
+                    round_a: bool = True, gate_f32: bool = True) -> np.ndarray:
     """Brute force: run every expert on every token and mask.
 
     mask[t, e] = 1 when fewer than k experts rank above e, where e' ranks
@@ -328,7 +328,8 @@ def moe_layer_dense(x, logits, w_gate, w_up, w_down, k: int,
     p = p / p.sum(axis=1, keepdims=True)
     wt = np.where(mask, p, 0.0)
     wt = wt / wt.sum(axis=1, keepdims=True)
-    wt = wt.astype(np.float32).astype(np.float64)  # the gate weights are float32 values
+    if gate_f32:  # the gate weights are float32 values (False: kept in float64)
+        wt = wt.astype(np.float32).astype(np.float64)
     out = np.zeros((T, x.shape[1]), np.float64)
     for e in range(E):
         _, Y = swiglu_expert(x, w_gate[e], w_up[e], w_down[e], round_a)
