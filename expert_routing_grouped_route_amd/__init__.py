@@ -27,7 +27,7 @@ MOE_ERR_HIP = 4
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
                 "moe_grouped_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_fwd_timed",
                 "moe_layer_fwd_overlap", "moe_condensed_workspace_bytes",
-                "moe_layer_fwd_condensed")
+                "moe_layer_fwd_condensed", "moe_backward_workspace_bytes", "moe_layer_bwd")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -74,6 +74,8 @@ _SIGS = {
     "moe_layer_fwd_condensed": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P,
                                                ctypes.c_size_t, _P]),
+    "moe_backward_workspace_bytes": (ctypes.c_size_t, [_DIMS]),
+    "moe_layer_bwd": (ctypes.c_int, [_DIMS] + [_P] * 20 + [ctypes.c_size_t, _P]),
 }
 
 
@@ -210,3 +212,19 @@ def moe_layer_fwd_condensed(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_do
                                        _ptr(perm_out), _ptr(rep_out), _ptr(ws), int(ws_bytes),
                                        _stream(stream))
     _check("moe_layer_fwd_condensed", st)
+
+
+def moe_backward_workspace_bytes(d: moe_dims_t) -> int:
+    return int(lib().moe_backward_workspace_bytes(ctypes.byref(d)))
+
+
+def moe_layer_bwd(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up,
+                  wsh_down, dout, dx, dw_router, dbias, dw_gate, dw_up, dw_down, dwsh_gate,
+                  dwsh_up, dwsh_down, ws, ws_bytes, stream=None):
+    st = lib().moe_layer_bwd(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
+                             _ptr(w_up), _ptr(w_down), _ptr(wsh_gate), _ptr(wsh_up),
+                             _ptr(wsh_down), _ptr(dout), _ptr(dx), _ptr(dw_router), _ptr(dbias),
+                             _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(dwsh_gate),
+                             _ptr(dwsh_up), _ptr(dwsh_down), _ptr(ws), int(ws_bytes),
+                             _stream(stream))
+    _check("moe_layer_bwd", st)

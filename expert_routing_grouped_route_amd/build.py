@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 SOURCES = ("route.hip", "dispatch.hip", "gemm_bf16.hip", "gemm_f32.hip", "combine.hip",
-           "condense.hip", "moe_api.hip")
+           "condense.hip", "backward.hip", "moe_api.hip")
 ARCH = "gfx950"
 
 

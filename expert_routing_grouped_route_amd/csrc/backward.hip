@@ -1,0 +1,393 @@
+// Backward pass of the MoE layer: gradients of the layer output with respect
+// to the tokens, the router weights and bias, and every expert's weights.
+//
+// The pages time training runs (the DeepSeek-V3 MoE layers of the
+// FarSkip-Collective review, "What carries the argument"; the Luffy review's
+// training speed-ups, Fig. 8 caption), so the layer's backward pass is part of
+// the work they measure; they do not write its formulas out.  It follows from
+// the forward pass by the chain rule, with these readings: no gradient through
+// the choice of the top-k experts; the kept weights are the softmax over the
+// kept logits, so a token's logit gradient is w_i (dw_i - sum_j w_j dw_j) on
+// its kept experts; the bf16 rounding of the SwiGLU product passes the
+// gradient through unchanged; the bias gradient sums the logit gradient over
+// tokens.
+//
+// Every product is one launch of a grouped fp32 GEMM on the vector ALUs with
+// arbitrary element strides for both operands, so the same kernel serves the
+// products whose reduction runs along the weights' rows (input gradients) and
+// those that reduce over an expert's ragged rows (weight gradients).  bf16
+// operands are widened to fp32 on load; every output element is summed by
+// one thread in a fixed order, so results are reproducible bit for bit.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int GT = 64;   // output tile edge
+constexpr int GK = 16;   // K per LDS stage
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if (BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+  return static_cast<const float*>(p)[i];
+}
+
+// Group g's M-tiles of GT rows start at prefix[g]; prefix[G] is the total.
+__global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restrict__ off, int G,
+                                                         int32_t* __restrict__ prefix) {
+  if (threadIdx.x != 0) return;
+  int acc = 0;
+  for (int g = 0; g < G; ++g) {
+    prefix[g] = acc;
+    acc += (off[g + 1] - off[g] + GT - 1) / GT;
+  }
+  prefix[G] = acc;
+}
+
+// C(m, n) = [C(m, n) +] sum_k A(m, k) B(k, n), with A(m, k) at
+// A[g*a_g + m*a_sm + k*a_sk] and so on.  RAGGED_K false: group g owns the
+// rows off[g] .. off[g+1] of A and C (global row numbers) and tiles come from
+// `prefix`; off null: one group of `ext` rows.  RAGGED_K true: group g reduces
+// over k = off[g] .. off[g+1] (or 0 .. ext), blockIdx.y = g.
+template <bool A_BF16, bool B_BF16, bool RAGGED_K>
+__global__ __launch_bounds__(256) void gemm_f32_grouped_kernel(
+    const void* __restrict__ A, int64_t a_sm, int64_t a_sk, int64_t a_g,
+    const void* __restrict__ B, int64_t b_sk, int64_t b_sn, int64_t b_g,
+    float* __restrict__ C, int64_t c_sm, int64_t c_sn, int64_t c_g,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ prefix, int G, int ext,
+    int M, int N, int K, int accumulate) {
+  __shared__ float As[GK][GT + 4];
+  __shared__ float Bs[GK][GT + 4];
+  const int nt = (N + GT - 1) / GT;
+  const int tile = blockIdx.x;
+  const int n0 = (tile % nt) * GT;
+  int g = 0, m0, m1, k0, k1;
+  if (!RAGGED_K) {
+    const int mt = tile / nt;
+    if (off) {
+      if (mt >= prefix[G]) return;
+      int lo = 0, hi = G - 1;  // last g with prefix[g] <= mt
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= mt) lo = mid;
+        else hi = mid - 1;
+      }
+      g = lo;
+      m0 = off[g] + (mt - prefix[g]) * GT;
+      m1 = off[g + 1];
+    } else {
+      m0 = mt * GT;
+      m1 = ext;
+      if (m0 >= m1) return;
+    }
+    k0 = 0;
+    k1 = K;
+  } else {
+    g = blockIdx.y;
+    m0 = (tile / nt) * GT;
+    m1 = M;
+    k0 = off ? off[g] : 0;
+    k1 = off ? off[g + 1] : ext;
+  }
+  const void* Ab = A_BF16 ? (const void*)(static_cast<const uint16_t*>(A) + g * a_g)
+                          : (const void*)(static_cast<const float*>(A) + g * a_g);
+  const void* Bb = B_BF16 ? (const void*)(static_cast<const uint16_t*>(B) + g * b_g)
+                          : (const void*)(static_cast<const float*>(B) + g * b_g);
+  float* Cb = C + g * c_g;
+  const int t = threadIdx.x, tm = t >> 4, tn = t & 15;
+  const bool a_kc = a_sk == 1, b_nc = b_sn == 1;  // which index is contiguous in memory
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int kb = k0; kb < k1; kb += GK) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = t + 256 * u;
+      int m, k;
+      if (a_kc) { m = q / GK; k = q % GK; }
+      else { k = q / GT; m = q % GT; }
+      const int gm = m0 + m, gk = kb + k;
+      As[k][m] = (gm < m1 && gk < k1) ? load_elem<A_BF16>(Ab, gm * a_sm + gk * a_sk) : 0.f;
+      int n, k2;
+      if (b_nc) { k2 = q / GT; n = q % GT; }
+      else { n = q / GK; k2 = q % GK; }
+      const int gn = n0 + n, gk2 = kb + k2;
+      Bs[k2][n] = (gn < N && gk2 < k1) ? load_elem<B_BF16>(Bb, gk2 * b_sk + gn * b_sn) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < GK; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[k][tm + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[k][tn + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gm = m0 + tm + 16 * i;
+    if (gm >= m1) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gn = n0 + tn + 16 * j;
+      if (gn >= N) continue;
+      float* c = Cb + gm * c_sm + (int64_t)gn * c_sn;
+      *c = accumulate ? *c + acc[i][j] : acc[i][j];
+    }
+  }
+}
+
+struct GemmOp {
+  const void* A; bool a_bf16; int64_t a_sm, a_sk, a_g;
+  const void* B; bool b_bf16; int64_t b_sk, b_sn, b_g;
+  float* C; int64_t c_sm, c_sn, c_g;
+  const int32_t* off;     // ragged offsets [G+1] or null
+  const int32_t* prefix;  // ragged M: M-tile prefix [G+1] (from tile_prefix_kernel)
+  int G, ext;             // groups; extent when off is null
+  int64_t m_bound;        // ragged M: bound of the M-tiles over all groups
+  int M, N, K;
+  bool ragged_k;
+  bool accumulate;
+};
+
+template <bool AB, bool BB, bool RK>
+void launch_gemm_t(const GemmOp& o, hipStream_t s) {
+  const int nt = (o.N + GT - 1) / GT;
+  dim3 grid;
+  if (RK) grid = dim3((unsigned)(((int64_t)o.M + GT - 1) / GT * nt), (unsigned)o.G);
+  else grid = dim3((unsigned)(o.m_bound * nt));
+  if (grid.x == 0 || grid.y == 0) return;
+  hipLaunchKernelGGL((gemm_f32_grouped_kernel<AB, BB, RK>), grid, dim3(256), 0, s, o.A, o.a_sm,
+                     o.a_sk, o.a_g, o.B, o.b_sk, o.b_sn, o.b_g, o.C, o.c_sm, o.c_sn, o.c_g, o.off,
+                     o.prefix, o.G, o.ext, o.M, o.N, o.K, (int)o.accumulate);
+}
+
+void launch_gemm(const GemmOp& o, hipStream_t s) {
+#define MOE_G(AB, BB)                                   \
+  if (o.a_bf16 == AB && o.b_bf16 == BB) {               \
+    if (o.ragged_k) launch_gemm_t<AB, BB, true>(o, s);  \
+    else launch_gemm_t<AB, BB, false>(o, s);            \
+    return;                                             \
+  }
+  MOE_G(false, false)
+  MOE_G(false, true)
+  MOE_G(true, false)
+  MOE_G(true, true)
+#undef MOE_G
+}
+
+// dY[i] = w[a] * dout[t] and dw[a] = dout[t] . y[i] for sorted row i holding
+// assignment a = perm[i] of token t = a / k; one wave per row.
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const float* __restrict__ dout,
+                                                       const float* __restrict__ y,
+                                                       const int32_t* __restrict__ perm,
+                                                       const float* __restrict__ w, int R, int k,
+                                                       int d, float* __restrict__ dY,
+                                                       float* __restrict__ dw) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave;
+  if (i >= R) return;
+  const int a = perm[i], t = a / k;
+  const float wa = w[a];
+  const float* dr = dout + (size_t)t * d;
+  const float* yr = y + (size_t)i * d;
+  float* o = dY + (size_t)i * d;
+  float s = 0.f;
+  for (int c = lane; c < d; c += 64) {
+    const float g = dr[c];
+    o[c] = wa * g;
+    s = fmaf(g, yr[c], s);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if (lane == 0) dw[a] = s;
+}
+
+// Logit gradient of each token's kept weights: dL_j = w_j (dw_j - sum w dw).
+__global__ __launch_bounds__(256) void bwd_gate_kernel(const float* __restrict__ w,
+                                                       const float* __restrict__ dw, int T, int k,
+                                                       float* __restrict__ dl) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  const float* wt = w + (size_t)t * k;
+  const float* dt = dw + (size_t)t * k;
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) s = fmaf(wt[j], dt[j], s);
+  for (int j = 0; j < k; ++j) dl[(size_t)t * k + j] = wt[j] * (dt[j] - s);
+}
+
+// The forward's SwiGLU product from fp32 G and U, rounded to bf16 (round to
+// nearest even) for bf16 layers: A = silu(g) * u, stored as fp32 values.
+__global__ __launch_bounds__(256) void swiglu_fwd_kernel(const float* __restrict__ G,
+                                                         const float* __restrict__ U, int64_t n,
+                                                         int round_bf16, float* __restrict__ A) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float a = silu_times(G[i], U[i]);
+    if (round_bf16) {
+      const uint32_t b = pack_bf16x2_rne(a, 0.f);
+      a = __uint_as_float(b << 16);
+    }
+    A[i] = a;
+  }
+}
+
+// In place: G <- dA * U * silu'(G), U <- dA * silu(G).
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(float* __restrict__ G,
+                                                         float* __restrict__ U,
+                                                         const float* __restrict__ dA, int64_t n) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float g = G[i], u = U[i], da = dA[i];
+    const float s = 1.0f / (1.0f + __expf(-g));
+    G[i] = da * u * (s * (1.0f + g * (1.0f - s)));
+    U[i] = da * (g * s);
+  }
+}
+
+// dx[t] = sum_j dXs[inv[t*k+j]] + sum_j dl[t*k+j] W_r[ids[t*k+j]] (+ dxs[t]),
+// slot order, then the router term, then the shared experts' term.
+template <bool WR_BF16>
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dXs,
+                                                     const int32_t* __restrict__ inv,
+                                                     const int32_t* __restrict__ ids,
+                                                     const float* __restrict__ dl,
+                                                     const void* __restrict__ wr,
+                                                     const float* __restrict__ dxs, int T, int k,
+                                                     int d, float* __restrict__ dx) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  for (int c = lane; c < d; c += 64) {
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) s += dXs[(size_t)inv[(size_t)t * k + j] * d + c];
+    for (int j = 0; j < k; ++j)
+      s = fmaf(dl[(size_t)t * k + j], load_elem<WR_BF16>(wr, (int64_t)ids[(size_t)t * k + j] * d + c), s);
+    if (dxs) s += dxs[(size_t)t * d + c];
+    dx[(size_t)t * d + c] = s;
+  }
+}
+
+// dW_r[e, c] = sum over expert e's sorted rows i (ascending) of
+// dl[perm[i]] * xs[i, c]; dbias[e] = sum of dl[perm[i]].  Block (256 columns, e).
+template <bool X_BF16>
+__global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(const void* __restrict__ xs,
+                                                               const int32_t* __restrict__ perm,
+                                                               const int32_t* __restrict__ off,
+                                                               const float* __restrict__ dl, int d,
+                                                               float* __restrict__ dwr,
+                                                               float* __restrict__ db) {
+  const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
+  const int r0 = off[e], r1 = off[e + 1];
+  if (c < d) {
+    float s = 0.f;
+    for (int i = r0; i < r1; ++i) s = fmaf(dl[perm[i]], load_elem<X_BF16>(xs, (int64_t)i * d + c), s);
+    dwr[(size_t)e * d + c] = s;
+  }
+  if (db && blockIdx.x == 0 && threadIdx.x == 0) {
+    float s = 0.f;
+    for (int i = r0; i < r1; ++i) s += dl[perm[i]];
+    db[e] = s;
+  }
+}
+
+unsigned ew_grid(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); }
+
+}  // namespace
+
+void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
+  const int64_t T = a.T, R = a.T * a.k;
+  const int d = a.d, I = a.I, E = a.E;
+  const bool bf = a.bf16;
+  // M-tile prefix of the experts' row segments
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.offsets, E, a.prefix);
+  const int64_t mt_bound = (R + (int64_t)E * (GT - 1)) / GT;
+
+  auto ragged_m = [&](const void* A, bool ab, int64_t a_sm, const void* B, bool bb, int64_t b_sk,
+                      int64_t b_sn, int64_t b_g, float* C, int64_t c_sm, int N, int K, bool acc) {
+    GemmOp o = {A, ab, a_sm, 1, 0, B, bb, b_sk, b_sn, b_g, C, c_sm, 1, 0, a.offsets, a.prefix,
+                E, 0, mt_bound, 0, N, K, false, acc};
+    launch_gemm(o, s);
+  };
+  auto ragged_k = [&](const void* A, bool ab, int64_t a_sk, const void* B, bool bb, int64_t b_sk,
+                      float* C, int64_t c_sm, int64_t c_g, int M, int N) {
+    GemmOp o = {A, ab, 1, a_sk, 0, B, bb, b_sk, 1, 0, C, c_sm, 1, c_g, a.offsets, nullptr,
+                E, 0, 0, M, N, 0, true, false};
+    launch_gemm(o, s);
+  };
+
+  // forward recompute: G, U, the rounded SwiGLU product and the expert outputs
+  ragged_m(a.xs, bf, d, a.wg, bf, 1, d, (int64_t)I * d, a.G, I, I, d, false);
+  ragged_m(a.xs, bf, d, a.wu, bf, 1, d, (int64_t)I * d, a.U, I, I, d, false);
+  const int64_t nRI = R * I;
+  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, nRI,
+                     (int)bf, a.Ar);
+  ragged_m(a.Ar, false, I, a.wd, bf, 1, I, (int64_t)d * I, a.y, d, d, I, false);
+  // dY, dw, the gate's logit gradient
+  hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, a.dout, a.y,
+                     a.perm, a.w, (int)R, a.k, d, a.dY, a.dw);
+  hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, a.w,
+                     a.dw, (int)T, a.k, a.dl);
+  // dA = dY W_d[e]; dW_d[e] = dY_e^T A_e
+  ragged_m(a.dY, false, d, a.wd, bf, I, 1, (int64_t)d * I, a.dA, I, I, d, false);
+  ragged_k(a.dY, false, d, a.Ar, false, I, a.dw_down, I, (int64_t)d * I, d, I);
+  // dG, dU in place of G, U; dW_g, dW_u; dXs = dG W_g[e] + dU W_u[e]
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, a.dA, nRI);
+  ragged_k(a.G, false, I, a.xs, bf, d, a.dw_gate, d, (int64_t)I * d, I, d);
+  ragged_k(a.U, false, I, a.xs, bf, d, a.dw_up, d, (int64_t)I * d, I, d);
+  ragged_m(a.G, false, I, a.wg, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, false);
+  ragged_m(a.U, false, I, a.wu, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, true);
+
+  // shared experts, one after the other, on all T rows with weight 1
+  const int Is = a.Is;
+  for (int sh = 0; sh < a.ns; ++sh) {
+    const size_t wo = (size_t)sh * Is * d;
+    const void* wsg = bf ? (const void*)(static_cast<const uint16_t*>(a.wsg) + wo)
+                         : (const void*)(static_cast<const float*>(a.wsg) + wo);
+    const void* wsu = bf ? (const void*)(static_cast<const uint16_t*>(a.wsu) + wo)
+                         : (const void*)(static_cast<const float*>(a.wsu) + wo);
+    const void* wsd = bf ? (const void*)(static_cast<const uint16_t*>(a.wsd) + wo)
+                         : (const void*)(static_cast<const float*>(a.wsd) + wo);
+    auto uni_m = [&](const void* A, bool ab, int64_t a_sm, const void* B, bool bb, int64_t b_sk,
+                     int64_t b_sn, float* C, int64_t c_sm, int N, int K, bool acc) {
+      GemmOp o = {A, ab, a_sm, 1, 0, B, bb, b_sk, b_sn, 0, C, c_sm, 1, 0, nullptr, nullptr,
+                  1, (int)T, (T + GT - 1) / GT, 0, N, K, false, acc};
+      launch_gemm(o, s);
+    };
+    auto uni_k = [&](const void* A, bool ab, int64_t a_sk, const void* B, bool bb, int64_t b_sk,
+                     float* C, int64_t c_sm, int M, int N) {
+      GemmOp o = {A, ab, 1, a_sk, 0, B, bb, b_sk, 1, 0, C, c_sm, 1, 0, nullptr, nullptr,
+                  1, (int)T, 0, M, N, 0, true, false};
+      launch_gemm(o, s);
+    };
+    uni_m(a.x, bf, d, wsg, bf, 1, d, a.Gs, Is, Is, d, false);
+    uni_m(a.x, bf, d, wsu, bf, 1, d, a.Us, Is, Is, d, false);
+    const int64_t nT = T * Is;
+    hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, nT,
+                       (int)bf, a.As);
+    uni_m(a.dout, false, d, wsd, bf, Is, 1, a.dAs, Is, Is, d, false);
+    uni_k(a.dout, false, d, a.As, false, Is, a.dwsh_down + (size_t)sh * d * Is, Is, d, Is);
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, a.dAs, nT);
+    uni_k(a.Gs, false, Is, a.x, bf, d, a.dwsh_gate + wo, d, Is, d);
+    uni_k(a.Us, false, Is, a.x, bf, d, a.dwsh_up + wo, d, Is, d);
+    uni_m(a.Gs, false, Is, wsg, bf, d, 1, a.dxs, d, d, Is, sh > 0);
+    uni_m(a.Us, false, Is, wsu, bf, d, 1, a.dxs, d, d, Is, true);
+  }
+
+  // router weights and bias, then the token gradients
+  hipLaunchKernelGGL((bf ? bwd_router_wgrad_kernel<true> : bwd_router_wgrad_kernel<false>),
+                     dim3((unsigned)((d + 255) / 256), (unsigned)E), dim3(256), 0, s, a.xs, a.perm,
+                     a.offsets, a.dl, d, a.dw_router, a.dbias);
+  hipLaunchKernelGGL((bf ? bwd_dx_kernel<true> : bwd_dx_kernel<false>),
+                     dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, a.dXs, a.inv, a.ids, a.dl,
+                     a.wr, a.ns ? a.dxs : nullptr, (int)T, a.k, d, a.dx);
+}
+
+}  // namespace moe

@@ -290,9 +290,155 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
   return launched();
 }
 
+// Workspace of the backward pass: the routing and dispatch parts of the
+// forward layout, then the backward scratch.
+struct BLayout {
+  size_t xs, prefix, G, U, Ar, dA, y, dY, dXs, dw, dl, Gs, Us, As, dAs, dxs, total;
+};
+
+BLayout backward_layout_of(const moe_dims_t& D) {
+  const size_t T = (size_t)D.T, R = T * D.k, d = D.d, I = D.I, Is = D.I_shared;
+  BLayout B;
+  size_t o = layout_of(D).total;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  B.xs = take(R * d * elem_bytes(D));
+  B.prefix = take(((size_t)D.E + 1) * 4);
+  B.G = take(R * I * 4);
+  B.U = take(R * I * 4);
+  B.Ar = take(R * I * 4);
+  B.dA = take(R * I * 4);
+  B.y = take(R * d * 4);
+  B.dY = take(R * d * 4);
+  B.dXs = take(R * d * 4);
+  B.dw = take(R * 4);
+  B.dl = take(R * 4);
+  const size_t ts = D.n_shared ? T * Is * 4 : 0;
+  B.Gs = take(ts);
+  B.Us = take(ts);
+  B.As = take(ts);
+  B.dAs = take(ts);
+  B.dxs = take(D.n_shared ? T * d * 4 : 0);
+  B.total = o;
+  return B;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t moe_backward_workspace_bytes(const moe_dims_t* dims) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  return backward_layout_of(*dims).total;
+}
+
+moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_router,
+                           const float* bias, const void* w_gate, const void* w_up,
+                           const void* w_down, const void* wsh_gate, const void* wsh_up,
+                           const void* wsh_down, const float* dout, float* dx, float* dw_router,
+                           float* dbias, float* dw_gate, float* dw_up, float* dw_down,
+                           float* dwsh_gate, float* dwsh_up, float* dwsh_down, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims_t& D = *dims;
+  const Layout L = layout_of(D);
+  const BLayout B = backward_layout_of(D);
+  const size_t es = elem_bytes(D), T = (size_t)D.T, R = T * D.k, E = D.E, d = D.d;
+  const bool sh = D.n_shared > 0;
+  const size_t w_in = E * D.I * d * es, wsh_in = (size_t)D.n_shared * D.I_shared * d * es;
+  const size_t gw = E * D.I * d * 4, gsh = (size_t)D.n_shared * D.I_shared * d * 4;
+  st = check_bufs({{x, T * d * es, true, false},
+                   {w_router, E * d * es, true, false},
+                   {bias, E * 4, false, false},
+                   {w_gate, w_in, true, false},
+                   {w_up, w_in, true, false},
+                   {w_down, w_in, true, false},
+                   {wsh_gate, wsh_in, sh, false},
+                   {wsh_up, wsh_in, sh, false},
+                   {wsh_down, wsh_in, sh, false},
+                   {dout, T * d * 4, true, false},
+                   {dx, T * d * 4, true, true},
+                   {dw_router, E * d * 4, true, true},
+                   {dbias, E * 4, false, true},
+                   {dw_gate, gw, true, true},
+                   {dw_up, gw, true, true},
+                   {dw_down, gw, true, true},
+                   {dwsh_gate, gsh, sh, true},
+                   {dwsh_up, gsh, sh, true},
+                   {dwsh_down, gsh, sh, true},
+                   {ws, B.total, true, true}});
+  if (st != MOE_OK) return st;
+  if (ws_bytes < B.total) return MOE_ERR_WORKSPACE;
+  if (D.T == 0) return MOE_OK;
+  (void)hipGetLastError();
+  int32_t* ids = at<int32_t>(ws, L.ids);
+  float* wts = at<float>(ws, L.wts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* inv = at<int32_t>(ws, L.inv);
+  // the forward routing on the same inputs, and the dispatch with its row gather
+  RouteArgs ra = {x, w_router, bias, nullptr, nullptr, ids, wts, D.T, D.d, D.E, D.k,
+                  D.dtype == MOE_BF16};
+  launch_route(ra, stream);
+  DispatchArgs da = {x, ids, at<int32_t>(ws, L.counts), offsets, nullptr, nullptr, perm, inv,
+                     at<void>(ws, B.xs), at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k, (int)es,
+                     nullptr};
+  launch_dispatch(da, stream);
+  BwdArgs ba = {};
+  ba.x = x;
+  ba.wr = w_router;
+  ba.wg = w_gate;
+  ba.wu = w_up;
+  ba.wd = w_down;
+  ba.wsg = wsh_gate;
+  ba.wsu = wsh_up;
+  ba.wsd = wsh_down;
+  ba.dout = dout;
+  ba.ids = ids;
+  ba.w = wts;
+  ba.offsets = offsets;
+  ba.perm = perm;
+  ba.inv = inv;
+  ba.xs = at<void>(ws, B.xs);
+  ba.dx = dx;
+  ba.dw_router = dw_router;
+  ba.dbias = dbias;
+  ba.dw_gate = dw_gate;
+  ba.dw_up = dw_up;
+  ba.dw_down = dw_down;
+  ba.dwsh_gate = dwsh_gate;
+  ba.dwsh_up = dwsh_up;
+  ba.dwsh_down = dwsh_down;
+  ba.prefix = at<int32_t>(ws, B.prefix);
+  ba.G = at<float>(ws, B.G);
+  ba.U = at<float>(ws, B.U);
+  ba.Ar = at<float>(ws, B.Ar);
+  ba.dA = at<float>(ws, B.dA);
+  ba.y = at<float>(ws, B.y);
+  ba.dY = at<float>(ws, B.dY);
+  ba.dXs = at<float>(ws, B.dXs);
+  ba.dw = at<float>(ws, B.dw);
+  ba.dl = at<float>(ws, B.dl);
+  ba.Gs = sh ? at<float>(ws, B.Gs) : nullptr;
+  ba.Us = sh ? at<float>(ws, B.Us) : nullptr;
+  ba.As = sh ? at<float>(ws, B.As) : nullptr;
+  ba.dAs = sh ? at<float>(ws, B.dAs) : nullptr;
+  ba.dxs = sh ? at<float>(ws, B.dxs) : nullptr;
+  ba.T = D.T;
+  ba.d = D.d;
+  ba.E = D.E;
+  ba.k = D.k;
+  ba.I = D.I;
+  ba.ns = D.n_shared;
+  ba.Is = D.I_shared;
+  ba.bf16 = D.dtype == MOE_BF16;
+  launch_layer_bwd(ba, stream);
+  return launched();
+}
 
 size_t moe_workspace_bytes(const moe_dims_t* dims) {
   if (check_dims(dims) != MOE_OK) return 0;

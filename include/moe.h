@@ -236,6 +236,49 @@ MOE_API moe_status_t moe_layer_fwd_condensed(const moe_dims_t* dims, const void*
                                      int32_t* perm_out, int32_t* rep_out, void* ws,
                                      size_t ws_bytes, hipStream_t stream);
 
+/* Workspace of moe_layer_bwd: moe_workspace_bytes plus the backward scratch
+ * (the sorted token rows, four [T*k, I] and three [T*k, d] fp32 arrays, and
+ * per shared expert four [T, I_shared] arrays).  0 for invalid dims. */
+MOE_API size_t moe_backward_workspace_bytes(const moe_dims_t* dims);
+
+/* Backward pass of moe_layer_fwd: given the upstream gradient dout = dL/dout
+ * [T,d] fp32, the gradients of the layer output with respect to x, the
+ * router weights and bias, and every routed and shared expert's weights.
+ * The pages time training runs of MoE layers (the FarSkip-Collective review,
+ * "What carries the argument"; the Luffy review, Fig. 8 caption) but do not
+ * write the gradients out; they follow from the forward pass by the chain
+ * rule with these readings:
+ *   - the top-k choice of experts passes no gradient; the kept weights are
+ *     the softmax over the kept logits, so token t's logit gradient is
+ *     w_j (dw_j - sum_j' w_j' dw_j') on its kept experts, dw_j = dout[t] .
+ *     (expert output of slot j);
+ *   - dbias = the logit gradient summed over tokens (also when bias is NULL:
+ *     the gradient at a zero bias);
+ *   - the bf16 rounding of the SwiGLU product passes the gradient unchanged;
+ *     dw_down uses the rounded product the forward pass multiplied.
+ * The routing, the dispatch and the expert activations are recomputed from
+ * the inputs (nothing is carried over from a forward call).  All gradient
+ * arithmetic is fp32 (bf16 inputs widened), each output element summed in a
+ * fixed order: two calls give identical bits.
+ *   x, w_router, bias, w_gate, w_up, w_down, wsh_*: as in moe_layer_fwd.
+ *   dout: [T,d] fp32, required.
+ *   dx [T,d], dw_router [E,d], dw_gate, dw_up [E,I,d], dw_down [E,d,I]:
+ *     fp32 outputs, required; dbias [E] fp32 or NULL (not computed);
+ *     dwsh_gate, dwsh_up [n_shared,I_shared,d], dwsh_down
+ *     [n_shared,d,I_shared]: required iff n_shared > 0.  Experts that receive
+ *     no token get zero weight gradients.
+ *   ws: ws_bytes >= moe_backward_workspace_bytes(dims).
+ * Errors and asynchrony: as moe_layer_fwd (outputs must not overlap any
+ * other buffer). */
+MOE_API moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_router,
+                                   const float* bias, const void* w_gate, const void* w_up,
+                                   const void* w_down, const void* wsh_gate, const void* wsh_up,
+                                   const void* wsh_down, const float* dout, float* dx,
+                                   float* dw_router, float* dbias, float* dw_gate, float* dw_up,
+                                   float* dw_down, float* dwsh_gate, float* dwsh_up,
+                                   float* dwsh_down, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

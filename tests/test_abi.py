@@ -230,3 +230,44 @@ def test_condensed_layer_validation():
     # rep_out must not overlap another buffer, hyperplanes must be aligned
     assert _call_condensed(d, a, hyper, 0.9, a["x"] + 256, need) == moe.MOE_ERR_INVALID_ARG
     assert _call_condensed(d, a, hyper + 8, 0.9, None, need) == moe.MOE_ERR_INVALID_ARG
+
+
+def _bwd_call(d, ptrs, ws_bytes, **over):
+    names = ("x", "w_router", "bias", "w_gate", "w_up", "w_down", "wsh_gate", "wsh_up",
+             "wsh_down", "dout", "dx", "dw_router", "dbias", "dw_gate", "dw_up", "dw_down",
+             "dwsh_gate", "dwsh_up", "dwsh_down", "ws")
+    p = dict(ptrs)
+    p.update(over)
+    return moe.lib().moe_layer_bwd(ctypes.byref(d), *[p[n] for n in names], ws_bytes, 0)
+
+
+def _bwd_ptrs():
+    # distinct, 1 TiB apart, never dereferenced (every case fails validation)
+    names = ("x", "w_router", "bias", "w_gate", "w_up", "w_down", "wsh_gate", "wsh_up",
+             "wsh_down", "dout", "dx", "dw_router", "dbias", "dw_gate", "dw_up", "dw_down",
+             "dwsh_gate", "dwsh_up", "dwsh_down", "ws")
+    return {n: (i + 1) << 40 for i, n in enumerate(names)}
+
+
+def test_backward_workspace_covers_the_layer_workspace():
+    d = dims(n_shared=1, I_shared=128)
+    assert moe.moe_backward_workspace_bytes(d) > moe.moe_workspace_bytes(d)
+    assert moe.lib().moe_backward_workspace_bytes(None) == 0
+    assert moe.moe_backward_workspace_bytes(dims(E=300)) == 0
+
+
+def test_backward_validation():
+    d = dims(n_shared=1, I_shared=128)
+    need = moe.moe_backward_workspace_bytes(d)
+    p = _bwd_ptrs()
+    assert _bwd_call(dims(E=300), p, need) == moe.MOE_ERR_UNSUPPORTED
+    assert _bwd_call(d, p, need - 1) == moe.MOE_ERR_WORKSPACE
+    assert _bwd_call(d, p, moe.moe_workspace_bytes(d)) == moe.MOE_ERR_WORKSPACE
+    for req in ("x", "dout", "dx", "dw_router", "dw_gate", "dw_up", "dw_down", "dwsh_gate", "ws"):
+        assert _bwd_call(d, p, need, **{req: None}) == moe.MOE_ERR_INVALID_ARG, req
+    assert _bwd_call(d, p, need, dx=p["x"] + 16) == moe.MOE_ERR_INVALID_ARG  # output overlaps x
+    assert _bwd_call(d, p, need, dw_gate=p["dw_gate"] + 4) == moe.MOE_ERR_INVALID_ARG  # misaligned
+    # without shared experts their gradients may be NULL
+    d0 = dims()
+    assert _bwd_call(d0, p, need, wsh_gate=None, wsh_up=None, wsh_down=None, dwsh_gate=None,
+                     dwsh_up=None, dwsh_down=None, ws=None) == moe.MOE_ERR_INVALID_ARG
