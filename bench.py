@@ -119,8 +119,9 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib, workload, command):
     print(path)
 
 
-def kernel_label(name):
-    """Demangled kernel name without return type, anonymous namespace and arguments."""
+def kernel_label(name, limit=120):
+    """Demangled kernel name without return type, anonymous namespace and
+    arguments, cut to `limit` characters."""
     name = re.sub(r"^void ", "", name).replace("(anonymous namespace)::", "")
     depth = 0
     for i, ch in enumerate(name):  # cut at the argument list (first '(' outside template brackets)
@@ -129,18 +130,21 @@ def kernel_label(name):
         elif ch == ">":
             depth -= 1
         elif ch == "(" and depth == 0:
-            return name[:i]
-    return name
+            name = name[:i]
+            break
+    return name if len(name) <= limit else name[:limit] + "..."
 
 
-def summarize_stats(stats_csv, workload, command, bench_log=None):
+def summarize_stats(stats_csv, workload, command, bench_log=None, part="layer"):
     """Write the rocprofv3 --stats kernel summary (name, calls, average and total
     time), with the stage times that bench.py measured with HIP events in the
-    same profiled run when its log is given."""
+    same profiled run when its log is given.  part "backward" names the summary
+    of a run that also timed the backward pass."""
     rows = list(csv.DictReader(open(stats_csv)))
-    path = os.path.join(PROFILES, f"kernels_{workload}.md")
+    name = f"kernels_{workload}.md" if part == "layer" else f"kernels_{part}_{workload}.md"
+    path = os.path.join(PROFILES, name)
     with open(path, "w") as fh:
-        fh.write(f"# Kernel time, {workload} layer (rocprofv3 --kernel-trace --stats)\n\n")
+        fh.write(f"# Kernel time, {workload} {part} (rocprofv3 --kernel-trace --stats)\n\n")
         fh.write("Command (from the repository root):\n\n")
         for c in command:
             fh.write(f"    {c}\n")
@@ -155,6 +159,11 @@ def summarize_stats(stats_csv, workload, command, bench_log=None):
                     fh.write("\nThe same profiled run's HIP-event stage times (ms per layer call, "
                              "averaged over the timed steps): " +
                              ", ".join(f"{k} {v}" for k, v in rec["stages_ms"].items()) + ".\n")
+                    if part == "backward" and rec.get("backward"):
+                        b = rec["backward"]
+                        fh.write(f"\nBackward pass (moe_layer_bwd, HIP events over {b['calls_timed']} "
+                                 f"calls): {b['ms']} ms per call, {b['roofline']['achieved']} "
+                                 f"TFLOP/s of algorithmic work.\n")
     print(path)
 
 
@@ -183,6 +192,64 @@ def gather_dispatch_bytes(cfg):
     es = 2 if cfg.dtype == "bf16" else 4
     R = cfg.T * cfg.k
     return cfg.T * cfg.d * es + R * 4 + R * cfg.d * es + 2 * R * 4
+
+
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector peak
+
+
+def backward_flops(cfg):
+    """FLOPs of the backward pass.  Algorithmic: the gradient products of the
+    experts (dA, dW_down, dW_gate and dW_up, dx: 12 d I per routed row and
+    12 d n_s I_s per token); executed adds the recomputed forward products
+    (G, U and the expert outputs: 6 d I per row)."""
+    rows = cfg.T * cfg.k * cfg.d * cfg.I + cfg.T * cfg.d * cfg.n_shared * cfg.I_shared
+    return 12 * rows, 18 * rows
+
+
+def time_backward(cfg, dev, d, wdt, stream, warm=2, timed=5):
+    import torch
+
+    import expert_routing_grouped_route_amd as moe
+
+    f = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
+    g = dict(dx=f(cfg.T, cfg.d), dw_router=f(cfg.E, cfg.d), dbias=f(cfg.E),
+             dw_gate=f(cfg.E, cfg.I, cfg.d), dw_up=f(cfg.E, cfg.I, cfg.d),
+             dw_down=f(cfg.E, cfg.d, cfg.I))
+    sh = cfg.n_shared > 0
+    g["dwsh_gate"] = f(cfg.n_shared, cfg.I_shared, cfg.d) if sh else None
+    g["dwsh_up"] = f(cfg.n_shared, cfg.I_shared, cfg.d) if sh else None
+    g["dwsh_down"] = f(cfg.n_shared, cfg.d, cfg.I_shared) if sh else None
+    wsb = moe.moe_backward_workspace_bytes(d)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    dout = torch.randn(cfg.T, cfg.d, generator=torch.Generator(device="cuda").manual_seed(cfg.seed),
+                       device="cuda", dtype=torch.float32)
+
+    def call():
+        moe.moe_layer_bwd(d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
+                          dev["w_down"], dev["wsh_gate"], dev["wsh_up"], dev["wsh_down"], dout,
+                          g["dx"], g["dw_router"], g["dbias"], g["dw_gate"], g["dw_up"],
+                          g["dw_down"], g["dwsh_gate"], g["dwsh_up"], g["dwsh_down"], ws, wsb,
+                          stream)
+
+    print(f"[bench] timing {timed} calls of the backward pass", file=sys.stderr, flush=True)
+    for _ in range(warm):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(timed)]
+    for a_, b_ in ev:
+        a_.record(stream)
+        call()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a_.elapsed_time(b_) for a_, b_ in ev) / timed
+    fa, fe = backward_flops(cfg)
+    tf = fa / (ms * 1e-3) / 1e12
+    return {"entry_point": "moe_layer_bwd", "calls_timed": timed, "ms": round(ms, 3),
+            "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+            "flops_algorithmic": fa, "flops_executed": fe,
+            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_VALU_TFLOPS, 4),
+                         "note": "algorithmic FLOPs over the whole call; fp32 FMA on the VALU"}}
 
 
 def gemm_flops(cfg):
@@ -257,6 +324,8 @@ def main():
     ap.add_argument("--condense", type=float, default=None, metavar="COS",
                     help="also time moe_layer_fwd_condensed with this cosine threshold (the "
                          "default for workloads with duplicated rows: 0.9)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the timing of the backward pass (moe_layer_bwd)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="time only the one-stream layer (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -266,6 +335,8 @@ def main():
     ap.add_argument("--summarize-stats", metavar="STATS_CSV",
                     help="write the kernel-time summary from a rocprofv3 kernel_stats CSV")
     ap.add_argument("--bench-log", help="bench.py output of the profiled run (for --summarize-stats)")
+    ap.add_argument("--summary-part", default="layer", choices=("layer", "backward"),
+                    help="which summary --summarize-stats writes")
     ap.add_argument("--command", action="append", default=[],
                     help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
@@ -273,7 +344,8 @@ def main():
         summarize_pmc(*args.summarize_pmc, args.copy_calibration_mib, args.workload, args.command)
         return
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, args.workload, args.command, args.bench_log)
+        summarize_stats(args.summarize_stats, args.workload, args.command, args.bench_log,
+                        args.summary_part)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -427,6 +499,11 @@ def main():
     disp_ms = sum(a_.elapsed_time(b_) for a_, b_ in disp_ev) / args.steps
     del x_sorted
 
+    # the layer's backward pass (moe_layer_bwd), a few calls timed by HIP events
+    backward = None
+    if not args.no_backward:
+        backward = time_backward(cfg, dev, d, wdt, stream)
+
     # 4. token condensation (an approximation of the layer: reported apart, never as value)
     condensed = None
     cos_thr = args.condense if args.condense is not None else (0.9 if cfg.dup_frac > 0 else None)
@@ -527,6 +604,7 @@ def main():
                            "value_from": best_name},
         "stages_ms": {s: round(v, 4) for s, v in stage_ms.items()},
         "condensed": condensed,
+        "backward": backward,
         "hbm": hbm,
     }
     if not args.no_cpu_baseline:

@@ -1,0 +1,36 @@
+// Host-side launcher of the layer's backward pass (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Backward pass of the layer (backward.hip), after the route and the
+// dispatch (with its row gather) have run on the same inputs.
+struct BwdArgs {
+  const void *x, *wr, *wg, *wu, *wd;       // forward inputs (dtype of the layer)
+  const void *wsg, *wsu, *wsd;             // shared experts' weights or null
+  const float* dout;                       // [T,d]
+  const int32_t* ids;                      // [T,k] routing
+  const float* w;                          // [T,k] kept weights
+  const int32_t *offsets, *perm, *inv;     // dispatch
+  const void* xs;                          // [R,d] sorted token rows
+  float *dx, *dw_router, *dbias;           // [T,d], [E,d], [E] or null
+  float *dw_gate, *dw_up, *dw_down;        // [E,I,d], [E,I,d], [E,d,I]
+  float *dwsh_gate, *dwsh_up, *dwsh_down;  // [ns,Is,d], [ns,Is,d], [ns,d,Is]
+  // scratch
+  int32_t* prefix;                         // [E+1]
+  float *G, *U, *Ar, *dA;                  // [R,I] each
+  float *y, *dY, *dXs;                     // [R,d] each
+  float *dw, *dl;                          // [R] each
+  float *Gs, *Us, *As, *dAs;               // [T,Is] each
+  float* dxs;                              // [T,d]
+  int64_t T;
+  int d, E, k, I, ns, Is;
+  bool bf16;
+};
+void launch_layer_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace moe

@@ -20,6 +20,7 @@
 // one thread in a fixed order, so results are reproducible bit for bit.
 #include "common.h"
 #include "kernels.h"
+#include "backward.h"
 
 namespace moe {
 namespace {

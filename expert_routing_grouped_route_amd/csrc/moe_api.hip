@@ -6,6 +6,7 @@
 #include "moe.h"
 #include "common.h"
 #include "kernels.h"
+#include "backward.h"
 
 namespace {
 

@@ -44,7 +44,7 @@ def _np(t):
 class Case:
     def __init__(self, cfg):
         self.cfg = cfg
-        self.a = moe_synth.generate(cfg)
+        self.a = moe_synth.generate(cfg, workers=16)
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         self.t = {n: (None if v is None else torch.from_numpy(np.ascontiguousarray(v)).to(
             torch.float32 if n == "bias" else dt).cuda()) for n, v in self.a.items()}
@@ -147,3 +147,17 @@ def test_backward_is_deterministic(name):
     for n in GRADS:
         if g1[n] is not None:
             assert np.array_equal(g1[n], g2[n]), n
+
+
+def test_backward_full_size_deepseek_v2_lite():
+    """The DeepSeek-V2-Lite-shaped layer (4096 tokens, 64 experts top-6, two
+    shared experts) at full size, in the configuration bench.py times: every
+    gradient against the full fp64 oracle (about 10-20 s of host time)."""
+    cfg = moe_synth.CONFIGS["deepseek_v2_lite"]
+    c = Case(cfg)
+    L = c.logits()
+    got = c.backward()
+    print(f"[bwd {cfg.name}] GPU done; running the oracle", flush=True)
+    ref = c.reference(L)
+    for n in GRADS:
+        assert_grad_close(got[n], ref[n], f"{cfg.name}.{n}")
