@@ -194,7 +194,10 @@ def gather_dispatch_bytes(cfg):
     return cfg.T * cfg.d * es + R * 4 + R * cfg.d * es + 2 * R * 4
 
 
-PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector peak
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector peak (packed FMA: 2 per lane per clock)
+# without packed fp32 instructions (not generated here): 256 CUs x 64 lanes x
+# one FMA (2 FLOP) per lane per clock x 2.4 GHz
+PEAK_FP32_UNPACKED_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
 
 
 def backward_flops(cfg):
@@ -249,6 +252,9 @@ def time_backward(cfg, dev, d, wdt, stream, warm=2, timed=5):
             "flops_algorithmic": fa, "flops_executed": fe,
             "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_VALU_TFLOPS, 4),
+                         "peak_unpacked_fma": round(PEAK_FP32_UNPACKED_TFLOPS, 1),
+                         "frac_unpacked": round(tf / PEAK_FP32_UNPACKED_TFLOPS, 4),
+                         "executed_tflops": round(fe / (ms * 1e-3) / 1e12, 2),
                          "note": "algorithmic FLOPs over the whole call; fp32 FMA on the VALU"}}
 
 

@@ -24,7 +24,7 @@ struct BwdArgs {
   int32_t* prefix;                         // [E+1]
   float *G, *U, *Ar, *dA;                  // [R,I] each
   float *y, *dY, *dXs;                     // [R,d] each
-  float *dw, *dl;                          // [R] each
+  float *dw, *dl, *dls;                    // [R] each (dls: dl in sorted-row order)
   float *Gs, *Us, *As, *dAs;               // [T,Is] each
   float* dxs;                              // [T,d]
   int64_t T;

@@ -213,17 +213,25 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const float* __restrict__
   if (lane == 0) dw[a] = s;
 }
 
-// Logit gradient of each token's kept weights: dL_j = w_j (dw_j - sum w dw).
+// Logit gradient of each token's kept weights: dL_j = w_j (dw_j - sum w dw),
+// in assignment order (dl) and in sorted-row order (dls[inv[a]] = dl[a]).
 __global__ __launch_bounds__(256) void bwd_gate_kernel(const float* __restrict__ w,
-                                                       const float* __restrict__ dw, int T, int k,
-                                                       float* __restrict__ dl) {
+                                                       const float* __restrict__ dw,
+                                                       const int32_t* __restrict__ inv, int T,
+                                                       int k, float* __restrict__ dl,
+                                                       float* __restrict__ dls) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
   const float* wt = w + (size_t)t * k;
   const float* dt = dw + (size_t)t * k;
   float s = 0.f;
   for (int j = 0; j < k; ++j) s = fmaf(wt[j], dt[j], s);
-  for (int j = 0; j < k; ++j) dl[(size_t)t * k + j] = wt[j] * (dt[j] - s);
+  for (int j = 0; j < k; ++j) {
+    const size_t a = (size_t)t * k + j;
+    const float v = wt[j] * (dt[j] - s);
+    dl[a] = v;
+    dls[inv[a]] = v;
+  }
 }
 
 // The forward's SwiGLU product from fp32 G and U, rounded to bf16 (round to
@@ -276,27 +284,22 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   }
 }
 
-// dW_r[e, c] = sum over expert e's sorted rows i (ascending) of
-// dl[perm[i]] * xs[i, c]; dbias[e] = sum of dl[perm[i]].  Block (256 columns, e).
-template <bool X_BF16>
-__global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(const void* __restrict__ xs,
-                                                               const int32_t* __restrict__ perm,
-                                                               const int32_t* __restrict__ off,
-                                                               const float* __restrict__ dl, int d,
-                                                               float* __restrict__ dwr,
-                                                               float* __restrict__ db) {
-  const int e = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
-  const int r0 = off[e], r1 = off[e + 1];
-  if (c < d) {
-    float s = 0.f;
-    for (int i = r0; i < r1; ++i) s = fmaf(dl[perm[i]], load_elem<X_BF16>(xs, (int64_t)i * d + c), s);
-    dwr[(size_t)e * d + c] = s;
+// dbias[e] = sum of dls over expert e's sorted rows: 256 strided partial sums,
+// then a fixed-order tree in LDS.  One block per expert.
+__global__ __launch_bounds__(256) void bwd_bias_kernel(const float* __restrict__ dls,
+                                                       const int32_t* __restrict__ off,
+                                                       float* __restrict__ db) {
+  __shared__ float part[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  float s = 0.f;
+  for (int i = off[e] + tid; i < off[e + 1]; i += 256) s += dls[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int h = 128; h >= 1; h >>= 1) {
+    if (tid < h) part[tid] += part[tid + h];
+    __syncthreads();
   }
-  if (db && blockIdx.x == 0 && threadIdx.x == 0) {
-    float s = 0.f;
-    for (int i = r0; i < r1; ++i) s += dl[perm[i]];
-    db[e] = s;
-  }
+  if (tid == 0) db[e] = part[0];
 }
 
 unsigned ew_grid(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); }
@@ -335,7 +338,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, a.dout, a.y,
                      a.perm, a.w, (int)R, a.k, d, a.dY, a.dw);
   hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, a.w,
-                     a.dw, (int)T, a.k, a.dl);
+                     a.dw, a.inv, (int)T, a.k, a.dl, a.dls);
   // dA = dY W_d[e]; dW_d[e] = dY_e^T A_e
   ragged_m(a.dY, false, d, a.wd, bf, I, 1, (int64_t)d * I, a.dA, I, I, d, false);
   ragged_k(a.dY, false, d, a.Ar, false, I, a.dw_down, I, (int64_t)d * I, d, I);
@@ -382,10 +385,12 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     uni_m(a.Us, false, Is, wsu, bf, d, 1, a.dxs, d, d, Is, true);
   }
 
-  // router weights and bias, then the token gradients
-  hipLaunchKernelGGL((bf ? bwd_router_wgrad_kernel<true> : bwd_router_wgrad_kernel<false>),
-                     dim3((unsigned)((d + 255) / 256), (unsigned)E), dim3(256), 0, s, a.xs, a.perm,
-                     a.offsets, a.dl, d, a.dw_router, a.dbias);
+  // router weights (dW_r[e] = dls_e^T X_e, one output row per expert) and
+  // bias, then the token gradients
+  ragged_k(a.dls, false, 1, a.xs, bf, d, a.dw_router, 0, d, 1, d);
+  if (a.dbias)
+    hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)E), dim3(256), 0, s, a.dls, a.offsets,
+                       a.dbias);
   hipLaunchKernelGGL((bf ? bwd_dx_kernel<true> : bwd_dx_kernel<false>),
                      dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, a.dXs, a.inv, a.ids, a.dl,
                      a.wr, a.ns ? a.dxs : nullptr, (int)T, a.k, d, a.dx);

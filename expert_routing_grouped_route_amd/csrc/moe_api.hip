@@ -294,7 +294,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // Workspace of the backward pass: the routing and dispatch parts of the
 // forward layout, then the backward scratch.
 struct BLayout {
-  size_t xs, prefix, G, U, Ar, dA, y, dY, dXs, dw, dl, Gs, Us, As, dAs, dxs, total;
+  size_t xs, prefix, G, U, Ar, dA, y, dY, dXs, dw, dl, dls, Gs, Us, As, dAs, dxs, total;
 };
 
 BLayout backward_layout_of(const moe_dims_t& D) {
@@ -317,6 +317,7 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.dXs = take(R * d * 4);
   B.dw = take(R * 4);
   B.dl = take(R * 4);
+  B.dls = take(R * 4);
   const size_t ts = D.n_shared ? T * Is * 4 : 0;
   B.Gs = take(ts);
   B.Us = take(ts);
@@ -424,6 +425,7 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
   ba.dXs = at<float>(ws, B.dXs);
   ba.dw = at<float>(ws, B.dw);
   ba.dl = at<float>(ws, B.dl);
+  ba.dls = at<float>(ws, B.dls);
   ba.Gs = sh ? at<float>(ws, B.Gs) : nullptr;
   ba.Us = sh ? at<float>(ws, B.Us) : nullptr;
   ba.As = sh ? at<float>(ws, B.As) : nullptr;
