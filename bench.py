@@ -234,28 +234,41 @@ def time_backward(cfg, dev, d, wdt, stream, warm=2, timed=5):
                           g["dw_down"], g["dwsh_gate"], g["dwsh_up"], g["dwsh_down"], ws, wsb,
                           stream)
 
+    def timed_ms():
+        for _ in range(warm):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(timed)]
+        for a_, b_ in ev:
+            a_.record(stream)
+            call()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        return sum(a_.elapsed_time(b_) for a_, b_ in ev) / timed
+
     print(f"[bench] timing {timed} calls of the backward pass", file=sys.stderr, flush=True)
-    for _ in range(warm):
-        call()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(timed)]
-    for a_, b_ in ev:
-        a_.record(stream)
-        call()
-        b_.record(stream)
-    torch.cuda.synchronize()
-    ms = sum(a_.elapsed_time(b_) for a_, b_ in ev) / timed
+    ms = timed_ms()  # products on the matrix cores (the library's default)
+    os.environ["MOE_BWD_VALU"] = "1"  # read by the library at every call
+    try:
+        ms_valu = timed_ms()
+    finally:
+        del os.environ["MOE_BWD_VALU"]
     fa, fe = backward_flops(cfg)
     tf = fa / (ms * 1e-3) / 1e12
+    tf_v = fa / (ms_valu * 1e-3) / 1e12
     return {"entry_point": "moe_layer_bwd", "calls_timed": timed, "ms": round(ms, 3),
             "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
             "flops_algorithmic": fa, "flops_executed": fe,
-            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": PEAK_FP32_VALU_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_VALU_TFLOPS, 4),
-                         "peak_unpacked_fma": round(PEAK_FP32_UNPACKED_TFLOPS, 1),
-                         "frac_unpacked": round(tf / PEAK_FP32_UNPACKED_TFLOPS, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                          "executed_tflops": round(fe / (ms * 1e-3) / 1e12, 2),
-                         "note": "algorithmic FLOPs over the whole call; fp32 FMA on the VALU"}}
+                         "note": "algorithmic FLOPs over the whole call; products on bf16 MFMA, "
+                                 "each fp32 operand as bf16 hi + lo parts (2 or 3 MFMAs per "
+                                 "product)"},
+            "vector_alu_variant": {"ms": round(ms_valu, 3), "achieved_tflops": round(tf_v, 2),
+                                   "frac_of_unpacked_fp32_fma_peak": round(
+                                       tf_v / PEAK_FP32_UNPACKED_TFLOPS, 4),
+                                   "peak_unpacked_fma": round(PEAK_FP32_UNPACKED_TFLOPS, 1)}}
 
 
 def gemm_flops(cfg):

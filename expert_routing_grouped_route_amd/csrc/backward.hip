@@ -18,6 +18,9 @@
 // those that reduce over an expert's ragged rows (weight gradients).  bf16
 // operands are widened to fp32 on load; every output element is summed by
 // one thread in a fixed order, so results are reproducible bit for bit.
+#include <algorithm>
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 #include "backward.h"
@@ -34,14 +37,14 @@ __device__ __forceinline__ float load_elem(const void* p, int64_t i) {
   return static_cast<const float*>(p)[i];
 }
 
-// Group g's M-tiles of GT rows start at prefix[g]; prefix[G] is the total.
+// Group g's M-tiles of `tile` rows start at prefix[g]; prefix[G] is the total.
 __global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restrict__ off, int G,
-                                                         int32_t* __restrict__ prefix) {
+                                                         int tile, int32_t* __restrict__ prefix) {
   if (threadIdx.x != 0) return;
   int acc = 0;
   for (int g = 0; g < G; ++g) {
     prefix[g] = acc;
-    acc += (off[g + 1] - off[g] + GT - 1) / GT;
+    acc += (off[g + 1] - off[g] + tile - 1) / tile;
   }
   prefix[G] = acc;
 }
@@ -147,6 +150,207 @@ __global__ __launch_bounds__(256) void gemm_f32_grouped_kernel(
   }
 }
 
+// The same products on the bf16 matrix cores.  Operands are staged in LDS as
+// fp32 exactly as above (any strides); each fragment is rounded to bf16 when
+// read, and an fp32 operand is taken as hi + lo, hi = bf16(v), lo =
+// bf16(v - hi) (|v - hi - lo| <= 2^-16 |v|): D += hi_a hi_b + lo_a hi_b +
+// hi_a lo_b, the lo_a lo_b term dropped, accumulation in fp32.  128x128 tile,
+// K-stages of 32, four waves of 64x64 (2x2 MFMA 32x32x16 tiles).
+constexpr int MT = 128;
+constexpr int MK = 32;
+constexpr int MLD = MT + 1;  // LDS row stride (floats): a row's 8-wide column writes spread over banks
+
+// 8 consecutive elements as fp32 (16-byte aligned source).
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
+  if (BF16) {
+    const u32x4 w = *static_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4 a = static_cast<const f32x4*>(p)[0], b = static_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  }
+}
+
+// One operand's tile into LDS: dst[k][r] = X(rb + r, kb + k) for r < MT,
+// k < MK, zero outside rows [.., r1) and k-values [.., k1); X(r, k) at
+// base[r * s_r + k * s_k].  Along whichever index is contiguous in memory each
+// lane reads 8 elements at once (16-byte aligned, wholly inside the bounds),
+// else element by element.
+template <bool BF16>
+__device__ __forceinline__ void load_tile(const void* base, int64_t s_r, int64_t s_k, int rb,
+                                          int r1, int kb, int k1, float (*dst)[MLD]) {
+  const int t = threadIdx.x;
+  const size_t es = BF16 ? 2 : 4;
+  if (s_k == 1 || s_r == 1) {
+    const bool along_k = s_k == 1;
+#pragma unroll
+    for (int u = 0; u < (MT * MK) / (8 * 256); ++u) {
+      const int q = t + 256 * u;
+      int r, k;
+      if (along_k) { r = q / (MK / 8); k = (q % (MK / 8)) * 8; }
+      else { k = q / (MT / 8); r = (q % (MT / 8)) * 8; }
+      const int gr = rb + r, gk = kb + k;
+      const int64_t idx = (int64_t)gr * s_r + (int64_t)gk * s_k;
+      const uint8_t* ptr = static_cast<const uint8_t*>(base) + idx * (int64_t)es;
+      const bool whole = along_k ? (gr < r1 && gk + 8 <= k1) : (gk < k1 && gr + 8 <= r1);
+      float v[8];
+      if (whole && ((reinterpret_cast<uintptr_t>(ptr) & 15) == 0)) {
+        load8<BF16>(ptr, v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int er = along_k ? gr : gr + e, ek = along_k ? gk + e : gk;
+          v[e] = (er < r1 && ek < k1) ? load_elem<BF16>(base, (int64_t)er * s_r + (int64_t)ek * s_k)
+                                      : 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (along_k) dst[k + e][r] = v[e];
+        else dst[k][r + e] = v[e];
+      }
+    }
+  } else {
+#pragma unroll 4
+    for (int u = 0; u < (MT * MK) / 256; ++u) {
+      const int q = t + 256 * u;
+      const int k = q / MT, r = q % MT;
+      const int gr = rb + r, gk = kb + k;
+      dst[k][r] = (gr < r1 && gk < k1) ? load_elem<BF16>(base, (int64_t)gr * s_r + (int64_t)gk * s_k)
+                                       : 0.f;
+    }
+  }
+}
+
+// bf16 hi and lo parts of 8 fp32 values.
+__device__ __forceinline__ void split8(const float (&v)[8], bool want_lo, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    h[p] = pack_bf16x2_rne(v[2 * p], v[2 * p + 1]);
+    if (want_lo) {
+      const float r0 = v[2 * p] - __uint_as_float(h[p] << 16);
+      const float r1 = v[2 * p + 1] - __uint_as_float(h[p] & 0xFFFF0000u);
+      l[p] = pack_bf16x2_rne(r0, r1);
+    }
+  }
+  hi = as_bf16x8(h);
+  if (want_lo) lo = as_bf16x8(l);
+}
+
+template <bool A_BF16, bool B_BF16, bool RAGGED_K>
+__global__ __launch_bounds__(256) void gemm_mfma_grouped_kernel(
+    const void* __restrict__ A, int64_t a_sm, int64_t a_sk, int64_t a_g,
+    const void* __restrict__ B, int64_t b_sk, int64_t b_sn, int64_t b_g,
+    float* __restrict__ C, int64_t c_sm, int64_t c_sn, int64_t c_g,
+    const int32_t* __restrict__ off, const int32_t* __restrict__ prefix, int G, int ext,
+    int M, int N, int K, int accumulate) {
+  __shared__ float As[MK][MLD];
+  __shared__ float Bs[MK][MLD];
+  const int nt = (N + MT - 1) / MT;
+  const int tile = blockIdx.x;
+  const int n0 = (tile % nt) * MT;
+  int g = 0, m0, m1, k0, k1;
+  if (!RAGGED_K) {
+    const int mt = tile / nt;
+    if (off) {
+      if (mt >= prefix[G]) return;
+      int lo = 0, hi = G - 1;  // last g with prefix[g] <= mt
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= mt) lo = mid;
+        else hi = mid - 1;
+      }
+      g = lo;
+      m0 = off[g] + (mt - prefix[g]) * MT;
+      m1 = off[g + 1];
+    } else {
+      m0 = mt * MT;
+      m1 = ext;
+      if (m0 >= m1) return;
+    }
+    k0 = 0;
+    k1 = K;
+  } else {
+    g = blockIdx.y;
+    m0 = (tile / nt) * MT;
+    m1 = M;
+    k0 = off ? off[g] : 0;
+    k1 = off ? off[g + 1] : ext;
+  }
+  const void* Ab = A_BF16 ? (const void*)(static_cast<const uint16_t*>(A) + g * a_g)
+                          : (const void*)(static_cast<const float*>(A) + g * a_g);
+  const void* Bb = B_BF16 ? (const void*)(static_cast<const uint16_t*>(B) + g * b_g)
+                          : (const void*)(static_cast<const float*>(B) + g * b_g);
+  float* Cb = C + g * c_g;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r32 = lane & 31, kg = lane >> 5;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  for (int kb = k0; kb < k1; kb += MK) {
+    load_tile<A_BF16>(Ab, a_sm, a_sk, m0, m1, kb, k1, As);
+    load_tile<B_BF16>(Bb, b_sn, b_sk, n0, N, kb, k1, Bs);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < MK / 16; ++ks) {
+      bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = As[ks * 16 + kg * 8 + e][wm * 64 + i * 32 + r32];
+        split8(v, !A_BF16, ah[i], al[i]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = Bs[ks * 16 + kg * 8 + e][wn * 64 + j * 32 + r32];
+        split8(v, !B_BF16, bh[j], bl[j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = mfma_32x32x16_bf16(ah[i], bh[j], acc[i][j]);
+          if (!A_BF16) acc[i][j] = mfma_32x32x16_bf16(al[i], bh[j], acc[i][j]);
+          if (!B_BF16) acc[i][j] = mfma_32x32x16_bf16(ah[i], bl[j], acc[i][j]);
+        }
+    }
+    __syncthreads();
+  }
+  // lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4 of each 32x32 tile
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int gn = n0 + wn * 64 + j * 32 + r32;
+      if (gn >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int gm = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+        if (gm >= m1) continue;
+        float* c = Cb + gm * c_sm + (int64_t)gn * c_sn;
+        *c = accumulate ? *c + acc[i][j][v] : acc[i][j][v];
+      }
+    }
+}
+
 struct GemmOp {
   const void* A; bool a_bf16; int64_t a_sm, a_sk, a_g;
   const void* B; bool b_bf16; int64_t b_sk, b_sn, b_g;
@@ -158,18 +362,25 @@ struct GemmOp {
   int M, N, K;
   bool ragged_k;
   bool accumulate;
+  bool mfma;              // the matrix-core kernel (tiles of MT) or the VALU one (GT)
 };
 
 template <bool AB, bool BB, bool RK>
 void launch_gemm_t(const GemmOp& o, hipStream_t s) {
-  const int nt = (o.N + GT - 1) / GT;
+  const int tt = o.mfma ? MT : GT;
+  const int nt = (o.N + tt - 1) / tt;
   dim3 grid;
-  if (RK) grid = dim3((unsigned)(((int64_t)o.M + GT - 1) / GT * nt), (unsigned)o.G);
+  if (RK) grid = dim3((unsigned)(((int64_t)o.M + tt - 1) / tt * nt), (unsigned)o.G);
   else grid = dim3((unsigned)(o.m_bound * nt));
   if (grid.x == 0 || grid.y == 0) return;
-  hipLaunchKernelGGL((gemm_f32_grouped_kernel<AB, BB, RK>), grid, dim3(256), 0, s, o.A, o.a_sm,
-                     o.a_sk, o.a_g, o.B, o.b_sk, o.b_sn, o.b_g, o.C, o.c_sm, o.c_sn, o.c_g, o.off,
-                     o.prefix, o.G, o.ext, o.M, o.N, o.K, (int)o.accumulate);
+  if (o.mfma)
+    hipLaunchKernelGGL((gemm_mfma_grouped_kernel<AB, BB, RK>), grid, dim3(256), 0, s, o.A, o.a_sm,
+                       o.a_sk, o.a_g, o.B, o.b_sk, o.b_sn, o.b_g, o.C, o.c_sm, o.c_sn, o.c_g,
+                       o.off, o.prefix, o.G, o.ext, o.M, o.N, o.K, (int)o.accumulate);
+  else
+    hipLaunchKernelGGL((gemm_f32_grouped_kernel<AB, BB, RK>), grid, dim3(256), 0, s, o.A, o.a_sm,
+                       o.a_sk, o.a_g, o.B, o.b_sk, o.b_sn, o.b_g, o.C, o.c_sm, o.c_sn, o.c_g,
+                       o.off, o.prefix, o.G, o.ext, o.M, o.N, o.K, (int)o.accumulate);
 }
 
 void launch_gemm(const GemmOp& o, hipStream_t s) {
@@ -310,20 +521,26 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   const int64_t T = a.T, R = a.T * a.k;
   const int d = a.d, I = a.I, E = a.E;
   const bool bf = a.bf16;
+  // products on the matrix cores (bf16 hi/lo parts), or on the VALU in fp32
+  // when MOE_BWD_VALU=1 is in the environment (read at every call, so that a
+  // test can compare both)
+  const char* valu = std::getenv("MOE_BWD_VALU");
+  const bool mf = !(valu && valu[0] == '1');
+  const int tt = mf ? MT : GT;
   // M-tile prefix of the experts' row segments
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.offsets, E, a.prefix);
-  const int64_t mt_bound = (R + (int64_t)E * (GT - 1)) / GT;
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.offsets, E, tt, a.prefix);
+  const int64_t mt_bound = (R + (int64_t)E * (tt - 1)) / tt;
 
   auto ragged_m = [&](const void* A, bool ab, int64_t a_sm, const void* B, bool bb, int64_t b_sk,
                       int64_t b_sn, int64_t b_g, float* C, int64_t c_sm, int N, int K, bool acc) {
     GemmOp o = {A, ab, a_sm, 1, 0, B, bb, b_sk, b_sn, b_g, C, c_sm, 1, 0, a.offsets, a.prefix,
-                E, 0, mt_bound, 0, N, K, false, acc};
+                E, 0, mt_bound, 0, N, K, false, acc, mf};
     launch_gemm(o, s);
   };
   auto ragged_k = [&](const void* A, bool ab, int64_t a_sk, const void* B, bool bb, int64_t b_sk,
                       float* C, int64_t c_sm, int64_t c_g, int M, int N) {
     GemmOp o = {A, ab, 1, a_sk, 0, B, bb, b_sk, 1, 0, C, c_sm, 1, c_g, a.offsets, nullptr,
-                E, 0, 0, M, N, 0, true, false};
+                E, 0, 0, M, N, 0, true, false, mf};
     launch_gemm(o, s);
   };
 
@@ -362,13 +579,13 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     auto uni_m = [&](const void* A, bool ab, int64_t a_sm, const void* B, bool bb, int64_t b_sk,
                      int64_t b_sn, float* C, int64_t c_sm, int N, int K, bool acc) {
       GemmOp o = {A, ab, a_sm, 1, 0, B, bb, b_sk, b_sn, 0, C, c_sm, 1, 0, nullptr, nullptr,
-                  1, (int)T, (T + GT - 1) / GT, 0, N, K, false, acc};
+                  1, (int)T, (T + tt - 1) / tt, 0, N, K, false, acc, mf};
       launch_gemm(o, s);
     };
     auto uni_k = [&](const void* A, bool ab, int64_t a_sk, const void* B, bool bb, int64_t b_sk,
                      float* C, int64_t c_sm, int M, int N) {
       GemmOp o = {A, ab, 1, a_sk, 0, B, bb, b_sk, 1, 0, C, c_sm, 1, 0, nullptr, nullptr,
-                  1, (int)T, 0, M, N, 0, true, false};
+                  1, (int)T, 0, M, N, 0, true, false, mf};
       launch_gemm(o, s);
     };
     uni_m(a.x, bf, d, wsg, bf, 1, d, a.Gs, Is, Is, d, false);

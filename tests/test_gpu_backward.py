@@ -8,7 +8,9 @@ the kernel moe_layer_bwd runs too), so both sides keep the same experts.
 Gradients are compared with the layer's rules scaled to each tensor's size:
 mean |g - r| <= 1e-3 rms(r) and max_i |g_i - r_i| / max(|r_i|, rms(r)) <=
 2e-2.  Experts without tokens must get exactly zero weight gradients; two
-calls must agree bit for bit."""
+calls must agree bit for bit.  The products run on the matrix cores (each
+fp32 operand as bf16 hi + lo parts); the fp32 VALU variant is held to the
+same bar."""
 import numpy as np
 import pytest
 import torch
@@ -132,6 +134,20 @@ def test_backward_matches_oracle(name):
             assert np.all(got[n][e] == 0.0), (name, n, e)
     if c.cfg.k == 1:  # the kept weight is 1 whatever the logits
         assert np.all(got["dw_router"] == 0.0) and np.all(got["dbias"] == 0.0)
+
+
+@pytest.mark.parametrize("name", ["bwd_bf16_shared", "bwd_fp32_two_shared", "bwd_bf16_zipf"])
+def test_backward_vector_alu_variant_matches_oracle(name, monkeypatch):
+    """The products on the VALU in fp32 (MOE_BWD_VALU=1) instead of the matrix
+    cores' bf16 hi/lo parts: the same bar against the oracle."""
+    monkeypatch.setenv("MOE_BWD_VALU", "1")
+    c = get(name)
+    L = c.logits()
+    got = c.backward()
+    ref = c.reference(L)
+    for n in GRADS:
+        if ref[n] is not None:
+            assert_grad_close(got[n], ref[n], f"{name}.{n} (VALU)")
 
 
 def test_backward_has_empty_experts_in_skewed_case():
