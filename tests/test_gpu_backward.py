@@ -165,15 +165,24 @@ def test_backward_is_deterministic(name):
             assert np.array_equal(g1[n], g2[n]), n
 
 
-def test_backward_full_size_deepseek_v2_lite():
-    """The DeepSeek-V2-Lite-shaped layer (4096 tokens, 64 experts top-6, two
-    shared experts) at full size, in the configuration bench.py times: every
-    gradient against the full fp64 oracle (about 10-20 s of host time)."""
-    cfg = moe_synth.CONFIGS["deepseek_v2_lite"]
+@pytest.mark.parametrize("name", ["deepseek_v2_lite", "qwen3_30b_a3b"])
+def test_backward_full_size(name):
+    """Full-size layers in the configuration bench.py times: the
+    DeepSeek-V2-Lite shape (4096 tokens, 64 experts top-6, two shared
+    experts) and the Qwen3-30B-A3B shape (8192 tokens, 128 experts top-8,
+    Zipf-skewed routing with empty experts).  Every gradient against the full
+    fp64 oracle (10-30 s of host time each)."""
+    cfg = moe_synth.CONFIGS[name]
     c = Case(cfg)
     L = c.logits()
     got = c.backward()
     print(f"[bwd {cfg.name}] GPU done; running the oracle", flush=True)
     ref = c.reference(L)
     for n in GRADS:
+        if ref[n] is None:
+            assert got[n] is None
+            continue
         assert_grad_close(got[n], ref[n], f"{cfg.name}.{n}")
+    empty = np.nonzero(np.diff(np.asarray(ref["offsets"])) == 0)[0]
+    for e in empty:
+        assert np.all(got["dw_gate"][e] == 0.0) and np.all(got["dw_down"][e] == 0.0), e
