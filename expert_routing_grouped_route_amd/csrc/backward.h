@@ -21,6 +21,9 @@ struct BwdArgs {
   float *dw_gate, *dw_up, *dw_down;        // [E,I,d], [E,I,d], [E,d,I]
   float *dwsh_gate, *dwsh_up, *dwsh_down;  // [ns,Is,d], [ns,Is,d], [ns,d,Is]
   // scratch
+  int32_t* tile_off;                       // bf16: the dispatch's M-tile table
+  int32_t* ctr;                            // bf16: the GEMM counters (zeroed by the dispatch)
+  uint16_t* Abf;                           // bf16: [R,I] the SwiGLU product in bf16
   int32_t* prefix;                         // [E+1]
   float *G, *U, *Ar, *dA;                  // [R,I] each
   float *y, *dY, *dXs;                     // [R,d] each

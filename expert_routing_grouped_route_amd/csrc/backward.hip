@@ -445,16 +445,23 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float* __restrict__
   }
 }
 
-// The forward's SwiGLU product from fp32 G and U, rounded to bf16 (round to
-// nearest even) for bf16 layers: A = silu(g) * u, stored as fp32 values.
+// The forward's SwiGLU product from fp32 G and U: A = silu(g) * u, stored as
+// fp32 values.  For bf16 layers it is formed as the forward's gate/up
+// epilogue forms it (hardware reciprocal, round to nearest even to bf16), so
+// from the same G and U it is the same A bit for bit, and Abf (if given)
+// receives the bf16 bits.
 __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const float* __restrict__ G,
                                                          const float* __restrict__ U, int64_t n,
-                                                         int round_bf16, float* __restrict__ A) {
+                                                         int round_bf16, float* __restrict__ A,
+                                                         uint16_t* __restrict__ Abf) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    float a = silu_times(G[i], U[i]);
+    float a;
     if (round_bf16) {
-      const uint32_t b = pack_bf16x2_rne(a, 0.f);
+      const uint32_t b = pack_bf16x2_rne(silu_times_rcp(G[i], U[i]), 0.f);
       a = __uint_as_float(b << 16);
+      if (Abf) Abf[i] = (uint16_t)b;
+    } else {
+      a = silu_times(G[i], U[i]);
     }
     A[i] = a;
   }
@@ -544,13 +551,44 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     launch_gemm(o, s);
   };
 
-  // forward recompute: G, U, the rounded SwiGLU product and the expert outputs
-  ragged_m(a.xs, bf, d, a.wg, bf, 1, d, (int64_t)I * d, a.G, I, I, d, false);
-  ragged_m(a.xs, bf, d, a.wu, bf, 1, d, (int64_t)I * d, a.U, I, I, d, false);
+  // forward recompute: G, U, the rounded SwiGLU product and the expert outputs.
+  // bf16 layers run them on the forward pass's own grouped GEMMs (G and U
+  // stored raw, then the down product of the bf16 SwiGLU rows).
   const int64_t nRI = R * I;
-  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, nRI,
-                     (int)bf, a.Ar);
-  ragged_m(a.Ar, false, I, a.wd, bf, 1, I, (int64_t)d * I, a.y, d, d, I, false);
+  if (bf) {
+    FfnArgs f = {};
+    f.xs = a.xs;
+    f.perm = a.perm;
+    f.k = a.k;
+    f.x = a.x;
+    f.wg = a.wg;
+    f.wu = a.wu;
+    f.wd = a.wd;
+    f.offsets = a.offsets;
+    f.tile_off = a.tile_off;
+    f.ctr = a.ctr;
+    f.a = a.G;
+    f.u_raw = a.U;
+    f.T = T;
+    f.R = R;
+    f.d = d;
+    f.E = E;
+    f.I = I;
+    f.bf16 = true;
+    f.part = kRoutedTiles;
+    launch_gate_up_raw_bf16(f, s);
+    hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, nRI, 1,
+                       a.Ar, a.Abf);
+    f.a = a.Abf;
+    f.y = a.y;
+    launch_down_bf16(f, s);
+  } else {
+    ragged_m(a.xs, bf, d, a.wg, bf, 1, d, (int64_t)I * d, a.G, I, I, d, false);
+    ragged_m(a.xs, bf, d, a.wu, bf, 1, d, (int64_t)I * d, a.U, I, I, d, false);
+    hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, nRI, 0,
+                       a.Ar, nullptr);
+    ragged_m(a.Ar, false, I, a.wd, bf, 1, I, (int64_t)d * I, a.y, d, d, I, false);
+  }
   // dY, dw, the gate's logit gradient
   hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, a.dout, a.y,
                      a.perm, a.w, (int)R, a.k, d, a.dY, a.dw);
@@ -592,7 +630,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     uni_m(a.x, bf, d, wsu, bf, 1, d, a.Us, Is, Is, d, false);
     const int64_t nT = T * Is;
     hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, nT,
-                       (int)bf, a.As);
+                       (int)bf, a.As, nullptr);
     uni_m(a.dout, false, d, wsd, bf, Is, 1, a.dAs, Is, Is, d, false);
     uni_k(a.dout, false, d, a.As, false, Is, a.dwsh_down + (size_t)sh * d * Is, Is, d, Is);
     hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, a.dAs, nT);

@@ -118,6 +118,7 @@ struct BTile {
   uint8_t* Out;           // element (0, 0) of the tile
   size_t out_ld;          // elements between output rows
   int out_cols;           // valid output columns (a multiple of 64)
+  int64_t raw_off;        // gate/up RAW: element offset of the tile's (0, 0) in G and U
 };
 
 __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g, int L, int n_routed,
@@ -141,6 +142,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
     t.wrows = min(GU_COLS, p.I - n * GU_COLS);
     t.Out = static_cast<uint8_t*>(p.a) + ((size_t)r0 * p.I + (size_t)n * GU_COLS) * 2;
     t.out_ld = p.I;
+    t.raw_off = (int64_t)r0 * p.I + (int64_t)n * GU_COLS;
   } else {
     const int sb = L - n_routed;
     const int per_s = g.mt_s * g.nt_s;
@@ -157,6 +159,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
     const size_t ld = (size_t)p.ns * p.Is;
     t.Out = static_cast<uint8_t*>(p.ash) + ((size_t)r0 * ld + (size_t)s * p.Is + (size_t)n * GU_COLS) * 2;
     t.out_ld = ld;
+    t.raw_off = 0;
   }
   t.x_ld = (size_t)p.d * 2;
   t.w_ld = (size_t)p.d * 2;
@@ -211,8 +214,9 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
 // and 32-bit lane offsets), which cost the address path less than 64-bit
 // global addresses; the launcher uses them when every operand offset fits in
 // 32 bits.
-template <bool GATE_UP, bool BUF>
-__device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
+template <bool GATE_UP, bool BUF, bool RAW = false>
+__device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g_raw = nullptr,
+                                         float* u_raw = nullptr) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
 
@@ -401,7 +405,24 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem) {
   // position (piece ^ row), which spreads both the column writes and the row
   // reads over the banks.  Waves without valid rows write nothing but take
   // part in every barrier.
-  if (GATE_UP) {
+  if (GATE_UP && RAW) {
+    // G and U themselves, fp32: each lane stores its four columns of each
+    if (!mm || wn * 32 >= t.out_cols) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + r32;
+      if (row >= t.rows) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wn * 32 + 8 * q + 4 * kg;
+        const int64_t o = t.raw_off + (int64_t)row * t.out_ld + col;
+        *reinterpret_cast<f32x4*>(g_raw + o) =
+            f32x4{acc[i][0][4 * q], acc[i][0][4 * q + 1], acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(u_raw + o) =
+            f32x4{acc[i][1][4 * q], acc[i][1][4 * q + 1], acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]};
+      }
+    }
+  } else if (GATE_UP) {
     // bf16 output is small: each lane stores its four columns (8 bytes) directly
     if (!mm || wn * 32 >= t.out_cols) return;  // no valid rows, or columns past I
     uint16_t* out = reinterpret_cast<uint16_t*>(t.Out);
@@ -492,6 +513,18 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, 
   run_tile<GATE_UP, BUF>(t, smem);
 }
 
+// The routed gate/up tiles with G and U stored as fp32 (RAW epilogue).
+template <bool BUF>
+__global__ __launch_bounds__(NTHREADS) void gate_up_raw_bf16_kernel(FfnArgs p, GemmGrid g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+  const int n_routed = p.tile_off[p.E] * g.nt_r;
+  const int L = xcd_remap(blockIdx.x);
+  if (L >= n_routed) return;
+  BTile t;
+  gate_up_tile(p, g, L, n_routed, t);
+  run_tile<true, BUF, true>(t, smem, static_cast<float*>(p.a), p.u_raw);
+}
+
 GemmGrid bf16_gate_up_grid(const FfnArgs& a) {
   GemmGrid g;
   g.mtb = (int)routed_mtile_bound(a.R, a.E);
@@ -553,6 +586,14 @@ void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream) {
                                     : grouped_gemm_bf16_kernel<true, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a,
                      bf16_gate_up_grid(a));
+}
+
+void launch_gate_up_raw_bf16(const FfnArgs& a, hipStream_t stream) {
+  const GemmGrid g = bf16_gate_up_grid(a);
+  const int64_t slots = g.routed ? pad_slots(g.routed) : 0;
+  if (slots == 0) return;
+  auto kern = buffer_offsets_fit(a) ? gate_up_raw_bf16_kernel<true> : gate_up_raw_bf16_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a, g);
 }
 
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream) {

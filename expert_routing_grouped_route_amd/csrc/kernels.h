@@ -85,9 +85,13 @@ struct FfnArgs {
   int d, E, I, ns, Is;
   bool bf16;
   int part;               // tiles launched: 0 all, 1 routed experts only, 2 shared experts only
+  float* u_raw;           // launch_gate_up_raw_bf16: [R,I] fp32 U (G goes to `a`, fp32)
 };
 constexpr int kAllTiles = 0, kRoutedTiles = 1, kSharedTiles = 2;
 void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream);
+// The routed gate/up products G = X W_g^T and U = X W_u^T as fp32 [R,I] (G in
+// `a`, U in `u_raw`) instead of the SwiGLU product: the same tiles and K loop.
+void launch_gate_up_raw_bf16(const FfnArgs& a, hipStream_t stream);
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream);
 void launch_gate_up_f32(const FfnArgs& a, hipStream_t stream);
 void launch_down_f32(const FfnArgs& a, hipStream_t stream);

@@ -294,7 +294,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // Workspace of the backward pass: the routing and dispatch parts of the
 // forward layout, then the backward scratch.
 struct BLayout {
-  size_t xs, prefix, G, U, Ar, dA, y, dY, dXs, dw, dl, dls, Gs, Us, As, dAs, dxs, total;
+  size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, Gs, Us, As, dAs, dxs, total;
 };
 
 BLayout backward_layout_of(const moe_dims_t& D) {
@@ -311,6 +311,7 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.G = take(R * I * 4);
   B.U = take(R * I * 4);
   B.Ar = take(R * I * 4);
+  B.Abf = take(D.dtype == MOE_BF16 ? R * I * 2 : 0);
   B.dA = take(R * I * 4);
   B.y = take(R * d * 4);
   B.dY = take(R * d * 4);
@@ -386,9 +387,9 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
   RouteArgs ra = {x, w_router, bias, nullptr, nullptr, ids, wts, D.T, D.d, D.E, D.k,
                   D.dtype == MOE_BF16};
   launch_route(ra, stream);
-  DispatchArgs da = {x, ids, at<int32_t>(ws, L.counts), offsets, nullptr, nullptr, perm, inv,
-                     at<void>(ws, B.xs), at<int32_t>(ws, L.blk), D.T, D.d, D.E, D.k, (int)es,
-                     nullptr};
+  DispatchArgs da = {x, ids, at<int32_t>(ws, L.counts), offsets, at<int32_t>(ws, L.tile_off),
+                     at<int32_t>(ws, L.ctr), perm, inv, at<void>(ws, B.xs), at<int32_t>(ws, L.blk),
+                     D.T, D.d, D.E, D.k, (int)es, nullptr};
   launch_dispatch(da, stream);
   BwdArgs ba = {};
   ba.x = x;
@@ -415,6 +416,9 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
   ba.dwsh_gate = dwsh_gate;
   ba.dwsh_up = dwsh_up;
   ba.dwsh_down = dwsh_down;
+  ba.tile_off = at<int32_t>(ws, L.tile_off);
+  ba.ctr = at<int32_t>(ws, L.ctr);
+  ba.Abf = D.dtype == MOE_BF16 ? at<uint16_t>(ws, B.Abf) : nullptr;
   ba.prefix = at<int32_t>(ws, B.prefix);
   ba.G = at<float>(ws, B.G);
   ba.U = at<float>(ws, B.U);
