@@ -28,7 +28,8 @@ struct BwdArgs {
   float *G, *U, *Ar, *dA;                  // [R,I] each
   float *y, *dY, *dXs;                     // [R,d] each
   float *dw, *dl, *dls;                    // [R] each (dls: dl in sorted-row order)
-  float *Gs, *Us, *As, *dAs;               // [T,Is] each
+  float *Gs, *Us, *As, *dAs;               // [T, ns*Is] each (all shared experts)
+  uint16_t* Asbf;                          // bf16: [T, ns*Is] the shared SwiGLU products in bf16
   float* dxs;                              // [T,d]
   int64_t T;
   int d, E, k, I, ns, Is;

@@ -596,7 +596,8 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
                      a.dw, a.inv, (int)T, a.k, a.dl, a.dls);
   // dA = dY W_d[e]; dW_d[e] = dY_e^T A_e
   ragged_m(a.dY, false, d, a.wd, bf, I, 1, (int64_t)d * I, a.dA, I, I, d, false);
-  ragged_k(a.dY, false, d, a.Ar, false, I, a.dw_down, I, (int64_t)d * I, d, I);
+  if (bf) ragged_k(a.dY, false, d, a.Abf, true, I, a.dw_down, I, (int64_t)d * I, d, I);
+  else ragged_k(a.dY, false, d, a.Ar, false, I, a.dw_down, I, (int64_t)d * I, d, I);
   // dG, dU in place of G, U; dW_g, dW_u; dXs = dG W_g[e] + dU W_u[e]
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, a.dA, nRI);
   ragged_k(a.G, false, I, a.xs, bf, d, a.dw_gate, d, (int64_t)I * d, I, d);
@@ -604,40 +605,71 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   ragged_m(a.G, false, I, a.wg, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, false);
   ragged_m(a.U, false, I, a.wu, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, true);
 
-  // shared experts, one after the other, on all T rows with weight 1
-  const int Is = a.Is;
-  for (int sh = 0; sh < a.ns; ++sh) {
+  // shared experts on all T rows with weight 1; their G, U and products sit
+  // side by side in [T, ns*Is] arrays (expert s in columns s*Is ..)
+  const int Is = a.Is, ns = a.ns;
+  const int64_t ld = (int64_t)ns * Is;
+  auto uni_m = [&](const void* A, bool ab, int64_t a_sm, const void* B, bool bb, int64_t b_sk,
+                   int64_t b_sn, float* C, int64_t c_sm, int N, int K, bool acc) {
+    GemmOp o = {A, ab, a_sm, 1, 0, B, bb, b_sk, b_sn, 0, C, c_sm, 1, 0, nullptr, nullptr,
+                1, (int)T, (T + tt - 1) / tt, 0, N, K, false, acc, mf};
+    launch_gemm(o, s);
+  };
+  auto uni_k = [&](const void* A, bool ab, int64_t a_sk, const void* B, bool bb, int64_t b_sk,
+                   float* C, int64_t c_sm, int M, int N) {
+    GemmOp o = {A, ab, 1, a_sk, 0, B, bb, b_sk, 1, 0, C, c_sm, 1, 0, nullptr, nullptr,
+                1, (int)T, 0, M, N, 0, true, false, mf};
+    launch_gemm(o, s);
+  };
+  auto wslice = [&](const void* w, int sh) -> const void* {
     const size_t wo = (size_t)sh * Is * d;
-    const void* wsg = bf ? (const void*)(static_cast<const uint16_t*>(a.wsg) + wo)
-                         : (const void*)(static_cast<const float*>(a.wsg) + wo);
-    const void* wsu = bf ? (const void*)(static_cast<const uint16_t*>(a.wsu) + wo)
-                         : (const void*)(static_cast<const float*>(a.wsu) + wo);
-    const void* wsd = bf ? (const void*)(static_cast<const uint16_t*>(a.wsd) + wo)
-                         : (const void*)(static_cast<const float*>(a.wsd) + wo);
-    auto uni_m = [&](const void* A, bool ab, int64_t a_sm, const void* B, bool bb, int64_t b_sk,
-                     int64_t b_sn, float* C, int64_t c_sm, int N, int K, bool acc) {
-      GemmOp o = {A, ab, a_sm, 1, 0, B, bb, b_sk, b_sn, 0, C, c_sm, 1, 0, nullptr, nullptr,
-                  1, (int)T, (T + tt - 1) / tt, 0, N, K, false, acc, mf};
-      launch_gemm(o, s);
-    };
-    auto uni_k = [&](const void* A, bool ab, int64_t a_sk, const void* B, bool bb, int64_t b_sk,
-                     float* C, int64_t c_sm, int M, int N) {
-      GemmOp o = {A, ab, 1, a_sk, 0, B, bb, b_sk, 1, 0, C, c_sm, 1, 0, nullptr, nullptr,
-                  1, (int)T, 0, M, N, 0, true, false, mf};
-      launch_gemm(o, s);
-    };
-    uni_m(a.x, bf, d, wsg, bf, 1, d, a.Gs, Is, Is, d, false);
-    uni_m(a.x, bf, d, wsu, bf, 1, d, a.Us, Is, Is, d, false);
-    const int64_t nT = T * Is;
+    return bf ? (const void*)(static_cast<const uint16_t*>(w) + wo)
+              : (const void*)(static_cast<const float*>(w) + wo);
+  };
+  if (ns > 0) {
+    const int64_t nT = T * ld;
+    if (bf) {
+      FfnArgs f = {};
+      f.x = a.x;
+      f.wsg = a.wsg;
+      f.wsu = a.wsu;
+      f.tile_off = a.tile_off;
+      f.ctr = a.ctr;
+      f.a = a.Gs;
+      f.u_raw = a.Us;
+      f.T = T;
+      f.R = R;
+      f.d = d;
+      f.E = E;
+      f.I = I;
+      f.ns = ns;
+      f.Is = Is;
+      f.bf16 = true;
+      f.part = kSharedTiles;
+      launch_gate_up_raw_bf16(f, s);
+    } else {
+      for (int sh = 0; sh < ns; ++sh) {
+        uni_m(a.x, bf, d, wslice(a.wsg, sh), bf, 1, d, a.Gs + (size_t)sh * Is, ld, Is, d, false);
+        uni_m(a.x, bf, d, wslice(a.wsu, sh), bf, 1, d, a.Us + (size_t)sh * Is, ld, Is, d, false);
+      }
+    }
     hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, nT,
-                       (int)bf, a.As, nullptr);
-    uni_m(a.dout, false, d, wsd, bf, Is, 1, a.dAs, Is, Is, d, false);
-    uni_k(a.dout, false, d, a.As, false, Is, a.dwsh_down + (size_t)sh * d * Is, Is, d, Is);
+                       (int)bf, a.As, bf ? a.Asbf : nullptr);
+    for (int sh = 0; sh < ns; ++sh) {
+      const size_t cs = (size_t)sh * Is;
+      // dA_s = dout W_sd[s]; dW_sd[s] = dout^T A_s
+      uni_m(a.dout, false, d, wslice(a.wsd, sh), bf, Is, 1, a.dAs + cs, ld, Is, d, false);
+      if (bf) uni_k(a.dout, false, d, a.Asbf + cs, true, ld, a.dwsh_down + cs * d, Is, d, Is);
+      else uni_k(a.dout, false, d, a.As + cs, false, ld, a.dwsh_down + cs * d, Is, d, Is);
+    }
     hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, a.dAs, nT);
-    uni_k(a.Gs, false, Is, a.x, bf, d, a.dwsh_gate + wo, d, Is, d);
-    uni_k(a.Us, false, Is, a.x, bf, d, a.dwsh_up + wo, d, Is, d);
-    uni_m(a.Gs, false, Is, wsg, bf, d, 1, a.dxs, d, d, Is, sh > 0);
-    uni_m(a.Us, false, Is, wsu, bf, d, 1, a.dxs, d, d, Is, true);
+    for (int sh = 0; sh < ns; ++sh) {
+      const size_t cs = (size_t)sh * Is;
+      uni_k(a.Gs + cs, false, ld, a.x, bf, d, a.dwsh_gate + cs * d, d, Is, d);
+      uni_k(a.Us + cs, false, ld, a.x, bf, d, a.dwsh_up + cs * d, d, Is, d);
+      uni_m(a.Gs + cs, false, ld, wslice(a.wsg, sh), bf, d, 1, a.dxs, d, d, Is, sh > 0);
+      uni_m(a.Us + cs, false, ld, wslice(a.wsu, sh), bf, d, 1, a.dxs, d, d, Is, true);
+    }
   }
 
   // router weights (dW_r[e] = dls_e^T X_e, one output row per expert) and

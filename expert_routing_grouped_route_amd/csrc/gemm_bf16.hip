@@ -159,7 +159,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
     const size_t ld = (size_t)p.ns * p.Is;
     t.Out = static_cast<uint8_t*>(p.ash) + ((size_t)r0 * ld + (size_t)s * p.Is + (size_t)n * GU_COLS) * 2;
     t.out_ld = ld;
-    t.raw_off = 0;
+    t.raw_off = (int64_t)r0 * ld + (int64_t)s * p.Is + (int64_t)n * GU_COLS;
   }
   t.x_ld = (size_t)p.d * 2;
   t.w_ld = (size_t)p.d * 2;
@@ -513,13 +513,15 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, 
   run_tile<GATE_UP, BUF>(t, smem);
 }
 
-// The routed gate/up tiles with G and U stored as fp32 (RAW epilogue).
+// Gate/up tiles with G and U stored as fp32 (RAW epilogue): the routed
+// tiles into [R,I], or (part: shared) the shared experts' into [T, n_s*I_s].
 template <bool BUF>
 __global__ __launch_bounds__(NTHREADS) void gate_up_raw_bf16_kernel(FfnArgs p, GemmGrid g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
-  const int n_routed = p.tile_off[p.E] * g.nt_r;
+  const int n_routed = p.part == kSharedTiles ? 0 : p.tile_off[p.E] * g.nt_r;
+  const int ns_t = p.part == kRoutedTiles ? 0 : g.n_shared;
   const int L = xcd_remap(blockIdx.x);
-  if (L >= n_routed) return;
+  if (L >= n_routed + ns_t) return;
   BTile t;
   gate_up_tile(p, g, L, n_routed, t);
   run_tile<true, BUF, true>(t, smem, static_cast<float*>(p.a), p.u_raw);
@@ -590,7 +592,7 @@ void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream) {
 
 void launch_gate_up_raw_bf16(const FfnArgs& a, hipStream_t stream) {
   const GemmGrid g = bf16_gate_up_grid(a);
-  const int64_t slots = g.routed ? pad_slots(g.routed) : 0;
+  const int64_t slots = launch_slots(a, g);
   if (slots == 0) return;
   auto kern = buffer_offsets_fit(a) ? gate_up_raw_bf16_kernel<true> : gate_up_raw_bf16_kernel<false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a, g);

@@ -89,8 +89,10 @@ struct FfnArgs {
 };
 constexpr int kAllTiles = 0, kRoutedTiles = 1, kSharedTiles = 2;
 void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream);
-// The routed gate/up products G = X W_g^T and U = X W_u^T as fp32 [R,I] (G in
-// `a`, U in `u_raw`) instead of the SwiGLU product: the same tiles and K loop.
+// The gate/up products G = X W_g^T and U = X W_u^T as fp32 (G in `a`, U in
+// `u_raw`) instead of the SwiGLU product: the same tiles and K loop.  part
+// kRoutedTiles: the routed experts' [R,I]; kSharedTiles: the shared experts'
+// [T, n_s*I_s].
 void launch_gate_up_raw_bf16(const FfnArgs& a, hipStream_t stream);
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream);
 void launch_gate_up_f32(const FfnArgs& a, hipStream_t stream);

@@ -294,7 +294,8 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // Workspace of the backward pass: the routing and dispatch parts of the
 // forward layout, then the backward scratch.
 struct BLayout {
-  size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, Gs, Us, As, dAs, dxs, total;
+  size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, Gs, Us, As, Asbf, dAs, dxs,
+      total;
 };
 
 BLayout backward_layout_of(const moe_dims_t& D) {
@@ -319,11 +320,12 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.dw = take(R * 4);
   B.dl = take(R * 4);
   B.dls = take(R * 4);
-  const size_t ts = D.n_shared ? T * Is * 4 : 0;
-  B.Gs = take(ts);
-  B.Us = take(ts);
-  B.As = take(ts);
-  B.dAs = take(ts);
+  const size_t ts = T * (size_t)D.n_shared * Is;  // all shared experts side by side
+  B.Gs = take(ts * 4);
+  B.Us = take(ts * 4);
+  B.As = take(ts * 4);
+  B.Asbf = take(D.dtype == MOE_BF16 ? ts * 2 : 0);
+  B.dAs = take(ts * 4);
   B.dxs = take(D.n_shared ? T * d * 4 : 0);
   B.total = o;
   return B;
@@ -434,6 +436,7 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
   ba.Us = sh ? at<float>(ws, B.Us) : nullptr;
   ba.As = sh ? at<float>(ws, B.As) : nullptr;
   ba.dAs = sh ? at<float>(ws, B.dAs) : nullptr;
+  ba.Asbf = sh && D.dtype == MOE_BF16 ? at<uint16_t>(ws, B.Asbf) : nullptr;
   ba.dxs = sh ? at<float>(ws, B.dxs) : nullptr;
   ba.T = D.T;
   ba.d = D.d;

@@ -237,8 +237,9 @@ MOE_API moe_status_t moe_layer_fwd_condensed(const moe_dims_t* dims, const void*
                                      size_t ws_bytes, hipStream_t stream);
 
 /* Workspace of moe_layer_bwd: moe_workspace_bytes plus the backward scratch
- * (the sorted token rows, four [T*k, I] and three [T*k, d] fp32 arrays, and
- * per shared expert four [T, I_shared] arrays).  0 for invalid dims. */
+ * (the sorted token rows, four [T*k, I] and three [T*k, d] fp32 arrays, four
+ * [T, n_shared*I_shared] fp32 arrays, and for bf16 layers the SwiGLU
+ * products in bf16).  0 for invalid dims. */
 MOE_API size_t moe_backward_workspace_bytes(const moe_dims_t* dims);
 
 /* Backward pass of moe_layer_fwd: given the upstream gradient dout = dL/dout
