@@ -121,6 +121,7 @@ struct BTile {
   int64_t raw_off;        // gate/up RAW: element offset of the tile's (0, 0) in G and U
 };
 
+template <bool RAW = false>  // RAW: also the tile's offset in the raw G and U arrays
 __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g, int L, int n_routed,
                                              BTile& t) {
   if (L < n_routed) {
@@ -142,7 +143,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
     t.wrows = min(GU_COLS, p.I - n * GU_COLS);
     t.Out = static_cast<uint8_t*>(p.a) + ((size_t)r0 * p.I + (size_t)n * GU_COLS) * 2;
     t.out_ld = p.I;
-    t.raw_off = (int64_t)r0 * p.I + (int64_t)n * GU_COLS;
+    if (RAW) t.raw_off = (int64_t)r0 * p.I + (int64_t)n * GU_COLS;
   } else {
     const int sb = L - n_routed;
     const int per_s = g.mt_s * g.nt_s;
@@ -159,7 +160,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
     const size_t ld = (size_t)p.ns * p.Is;
     t.Out = static_cast<uint8_t*>(p.ash) + ((size_t)r0 * ld + (size_t)s * p.Is + (size_t)n * GU_COLS) * 2;
     t.out_ld = ld;
-    t.raw_off = (int64_t)r0 * ld + (int64_t)s * p.Is + (int64_t)n * GU_COLS;
+    if (RAW) t.raw_off = (int64_t)r0 * ld + (int64_t)s * p.Is + (int64_t)n * GU_COLS;
   }
   t.x_ld = (size_t)p.d * 2;
   t.w_ld = (size_t)p.d * 2;
@@ -523,7 +524,7 @@ __global__ __launch_bounds__(NTHREADS) void gate_up_raw_bf16_kernel(FfnArgs p, G
   const int L = xcd_remap(blockIdx.x);
   if (L >= n_routed + ns_t) return;
   BTile t;
-  gate_up_tile(p, g, L, n_routed, t);
+  gate_up_tile<true>(p, g, L, n_routed, t);
   run_tile<true, BUF, true>(t, smem, static_cast<float*>(p.a), p.u_raw);
 }
 
