@@ -165,10 +165,10 @@ def test_backward_is_deterministic(name):
             assert np.array_equal(g1[n], g2[n]), n
 
 
-@pytest.mark.parametrize("name", ["deepseek_v2_lite", "qwen3_30b_a3b"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "deepseek_v2_lite", "qwen3_30b_a3b"])
 def test_backward_full_size(name):
-    """Full-size layers in the configuration bench.py times: the
-    DeepSeek-V2-Lite shape (4096 tokens, 64 experts top-6, two shared
+    """Full-size layers in the configuration bench.py times: the tiny fp32
+    layer, the DeepSeek-V2-Lite shape (4096 tokens, 64 experts top-6, two shared
     experts) and the Qwen3-30B-A3B shape (8192 tokens, 128 experts top-8,
     Zipf-skewed routing with empty experts).  Every gradient against the full
     fp64 oracle (10-30 s of host time each)."""
@@ -186,3 +186,25 @@ def test_backward_full_size(name):
     empty = np.nonzero(np.diff(np.asarray(ref["offsets"])) == 0)[0]
     for e in empty:
         assert np.all(got["dw_gate"][e] == 0.0) and np.all(got["dw_down"][e] == 0.0), e
+
+
+def test_backward_zero_tokens_is_a_no_op():
+    """T = 0: the call returns MOE_OK and enqueues nothing (outputs untouched)."""
+    cfg = MoEShape("bwd_empty", T=0, d=64, E=4, k=2, I=64, seed=27)
+    d = moe.dims(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, 0, 0, "bf16")
+    f = lambda *s: torch.full(s, 7.0, dtype=torch.float32, device="cuda")
+    x = torch.empty(1, cfg.d, dtype=torch.bfloat16, device="cuda")
+    wr = torch.zeros(cfg.E, cfg.d, dtype=torch.bfloat16, device="cuda")
+    wg = torch.zeros(cfg.E, cfg.I, cfg.d, dtype=torch.bfloat16, device="cuda")
+    wu = torch.zeros_like(wg)
+    wd = torch.zeros(cfg.E, cfg.d, cfg.I, dtype=torch.bfloat16, device="cuda")
+    dout = torch.empty(1, cfg.d, dtype=torch.float32, device="cuda")
+    dx = f(1, cfg.d)
+    dwr, dwg, dwu, dwd = f(cfg.E, cfg.d), f(cfg.E, cfg.I, cfg.d), f(cfg.E, cfg.I, cfg.d), f(cfg.E, cfg.d, cfg.I)
+    wsb = moe.moe_backward_workspace_bytes(d)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda")
+    moe.moe_layer_bwd(d, x, wr, None, wg, wu, wd, None, None, None, dout, dx, dwr, None, dwg, dwu,
+                      dwd, None, None, None, ws, wsb)
+    torch.cuda.synchronize()
+    for t in (dx, dwr, dwg, dwu, dwd):
+        assert torch.all(t == 7.0)
