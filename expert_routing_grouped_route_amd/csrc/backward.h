@@ -24,6 +24,9 @@ struct BwdArgs {
   int32_t* tile_off;                       // bf16: the dispatch's M-tile table
   int32_t* ctr;                            // bf16: the GEMM counters (zeroed by the dispatch)
   uint16_t* Abf;                           // bf16: [R,I] the SwiGLU product in bf16
+  uint16_t *wdT, *wgT, *wuT;               // bf16: [E,I,d], [E,d,I], [E,d,I] transposed weights
+  uint16_t *dYh, *dYl;                     // bf16: [R,d] hi and lo parts of dY
+  uint16_t *dGh, *dGl, *dUh, *dUl;         // bf16: [R,I] hi and lo parts of dG and dU
   int32_t* prefix;                         // [E+1]
   float *G, *U, *Ar, *dA;                  // [R,I] each
   float *y, *dY, *dXs;                     // [R,d] each

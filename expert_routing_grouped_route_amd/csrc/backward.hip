@@ -522,6 +522,46 @@ __global__ __launch_bounds__(256) void bwd_bias_kernel(const float* __restrict__
 
 unsigned ew_grid(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); }
 
+// out[e][q][p] = in[e][p][q] for bf16 [E][P][Q]; 64x64 tiles through LDS,
+// reads and writes along the contiguous index.  Block (q-tile, p-tile, e).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
+                                                             int P, int Q,
+                                                             uint16_t* __restrict__ out) {
+  __shared__ uint16_t tile[64][65];
+  const int q0 = blockIdx.x * 64, p0 = blockIdx.y * 64, e = blockIdx.z;
+  const uint16_t* src = in + (size_t)e * P * Q;
+  uint16_t* dst = out + (size_t)e * P * Q;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int p = p0 + r, q = q0 + tx;
+    if (p < P && q < Q) tile[r][tx] = src[(size_t)p * Q + q];
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int q = q0 + r, p = p0 + tx;
+    if (q < Q && p < P) dst[(size_t)q * P + p] = tile[tx][r];
+  }
+}
+
+// hi = bf16(v), lo = bf16(v - hi), round to nearest even (|v - hi - lo| <=
+// 2^-16 |v|), for a product on the bf16 matrix cores in two parts.
+__global__ __launch_bounds__(256) void split_bf16_kernel(const float* __restrict__ v, int64_t n,
+                                                         uint16_t* __restrict__ hi,
+                                                         uint16_t* __restrict__ lo) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float x = v[i];
+    const uint32_t h = pack_bf16x2_rne(x, 0.f);
+    hi[i] = (uint16_t)h;
+    lo[i] = (uint16_t)pack_bf16x2_rne(x - __uint_as_float(h << 16), 0.f);
+  }
+}
+
+void launch_transpose_bf16(const void* in, int E, int P, int Q, void* out, hipStream_t s) {
+  const dim3 grid((unsigned)((Q + 63) / 64), (unsigned)((P + 63) / 64), (unsigned)E);
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s,
+                     static_cast<const uint16_t*>(in), P, Q, static_cast<uint16_t*>(out));
+}
+
 }  // namespace
 
 void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
@@ -594,16 +634,63 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
                      a.perm, a.w, (int)R, a.k, d, a.dY, a.dw);
   hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, a.w,
                      a.dw, a.inv, (int)T, a.k, a.dl, a.dls);
+  // bf16 layers run the input-gradient products dA = dY W_d[e] and
+  // dX = dG W_g[e] + dU W_u[e] on the forward down kernel: they have its
+  // shape once the weights are transposed (W_d^T [I,d], W_g^T and W_u^T
+  // [d,I]) and the fp32 operand is split into bf16 hi and lo rows, one
+  // launch per part, the later ones adding to the output.
+  FfnArgs fd = {};
+  if (bf) {
+    launch_transpose_bf16(a.wd, E, d, I, a.wdT, s);
+    launch_transpose_bf16(a.wg, E, I, d, a.wgT, s);
+    launch_transpose_bf16(a.wu, E, I, d, a.wuT, s);
+    fd.offsets = a.offsets;
+    fd.tile_off = a.tile_off;
+    fd.ctr = a.ctr;
+    fd.T = T;
+    fd.R = R;
+    fd.E = E;
+    fd.bf16 = true;
+    fd.part = kRoutedTiles;
+  }
+  auto down_parts = [&](const uint16_t* hi, const uint16_t* lo, const void* wT, int K, int N,
+                        float* out, bool acc) {
+    fd.wd = wT;
+    fd.I = K;  // the down kernel reduces over its I and writes d columns
+    fd.d = N;
+    fd.y = out;
+    fd.a = const_cast<uint16_t*>(hi);
+    launch_down_routed_bf16(fd, acc, s);
+    fd.a = const_cast<uint16_t*>(lo);
+    launch_down_routed_bf16(fd, true, s);
+  };
+
   // dA = dY W_d[e]; dW_d[e] = dY_e^T A_e
-  ragged_m(a.dY, false, d, a.wd, bf, I, 1, (int64_t)d * I, a.dA, I, I, d, false);
+  if (bf) {
+    const int64_t nRd = R * d;
+    hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nRd)), dim3(256), 0, s, a.dY, nRd, a.dYh,
+                       a.dYl);
+    down_parts(a.dYh, a.dYl, a.wdT, d, I, a.dA, false);
+  } else {
+    ragged_m(a.dY, false, d, a.wd, bf, I, 1, (int64_t)d * I, a.dA, I, I, d, false);
+  }
   if (bf) ragged_k(a.dY, false, d, a.Abf, true, I, a.dw_down, I, (int64_t)d * I, d, I);
   else ragged_k(a.dY, false, d, a.Ar, false, I, a.dw_down, I, (int64_t)d * I, d, I);
   // dG, dU in place of G, U; dW_g, dW_u; dXs = dG W_g[e] + dU W_u[e]
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, a.dA, nRI);
   ragged_k(a.G, false, I, a.xs, bf, d, a.dw_gate, d, (int64_t)I * d, I, d);
   ragged_k(a.U, false, I, a.xs, bf, d, a.dw_up, d, (int64_t)I * d, I, d);
-  ragged_m(a.G, false, I, a.wg, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, false);
-  ragged_m(a.U, false, I, a.wu, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, true);
+  if (bf) {
+    hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, nRI, a.dGh,
+                       a.dGl);
+    hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.U, nRI, a.dUh,
+                       a.dUl);
+    down_parts(a.dGh, a.dGl, a.wgT, I, d, a.dXs, false);
+    down_parts(a.dUh, a.dUl, a.wuT, I, d, a.dXs, true);
+  } else {
+    ragged_m(a.G, false, I, a.wg, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, false);
+    ragged_m(a.U, false, I, a.wu, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, true);
+  }
 
   // shared experts on all T rows with weight 1; their G, U and products sit
   // side by side in [T, ns*Is] arrays (expert s in columns s*Is ..)

@@ -215,7 +215,9 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
 // and 32-bit lane offsets), which cost the address path less than 64-bit
 // global addresses; the launcher uses them when every operand offset fits in
 // 32 bits.
-template <bool GATE_UP, bool BUF, bool RAW = false>
+// RAW (gate/up): store G and U as fp32 instead of the SwiGLU product.
+// ACC (down): add the product to the output instead of storing it.
+template <bool GATE_UP, bool BUF, bool RAW = false, bool ACC = false>
 __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g_raw = nullptr,
                                          float* u_raw = nullptr) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -471,8 +473,16 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
       for (int u = 0; u < 16; ++u) {  // one row per instruction, 16 rows per wave
         const int row = wave * 16 + u, grow = h * 128 + row;
         if (grow < t.rows && lane * 4 < t.out_cols)
-          *reinterpret_cast<f32x4*>(out + (size_t)grow * t.out_ld + lane * 4) =
-              *reinterpret_cast<const f32x4*>(sm + row * 256 + ((lane ^ (row & 63)) << 2));
+        {
+          f32x4* o = reinterpret_cast<f32x4*>(out + (size_t)grow * t.out_ld + lane * 4);
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sm + row * 256 + ((lane ^ (row & 63)) << 2));
+          if (ACC) {
+            const f32x4 w = *o;
+            *o = f32x4{w[0] + v[0], w[1] + v[1], w[2] + v[2], w[3] + v[3]};
+          } else {
+            *o = v;
+          }
+        }
       }
       if (h == 0) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // staged reads done before the second half
@@ -526,6 +536,18 @@ __global__ __launch_bounds__(NTHREADS) void gate_up_raw_bf16_kernel(FfnArgs p, G
   BTile t;
   gate_up_tile<true>(p, g, L, n_routed, t);
   run_tile<true, BUF, true>(t, smem, static_cast<float*>(p.a), p.u_raw);
+}
+
+// The routed down tiles, storing or (ACC) adding to the output.
+template <bool BUF, bool ACC>
+__global__ __launch_bounds__(NTHREADS) void down_routed_bf16_kernel(FfnArgs p, GemmGrid g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+  const int n_routed = p.tile_off[p.E] * g.nt_r;
+  const int L = xcd_remap(blockIdx.x);
+  if (L >= n_routed) return;
+  BTile t;
+  down_tile(p, g, L, n_routed, t);
+  run_tile<false, BUF, false, ACC>(t, smem);
 }
 
 GemmGrid bf16_gate_up_grid(const FfnArgs& a) {
@@ -596,6 +618,16 @@ void launch_gate_up_raw_bf16(const FfnArgs& a, hipStream_t stream) {
   const int64_t slots = launch_slots(a, g);
   if (slots == 0) return;
   auto kern = buffer_offsets_fit(a) ? gate_up_raw_bf16_kernel<true> : gate_up_raw_bf16_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a, g);
+}
+
+void launch_down_routed_bf16(const FfnArgs& a, bool accumulate, hipStream_t stream) {
+  const GemmGrid g = bf16_down_grid(a);
+  const int64_t slots = g.routed ? pad_slots(g.routed) : 0;
+  if (slots == 0) return;
+  const bool buf = buffer_offsets_fit(a);
+  auto kern = buf ? (accumulate ? down_routed_bf16_kernel<true, true> : down_routed_bf16_kernel<true, false>)
+                  : (accumulate ? down_routed_bf16_kernel<false, true> : down_routed_bf16_kernel<false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a, g);
 }
 

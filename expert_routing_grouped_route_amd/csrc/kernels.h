@@ -94,6 +94,9 @@ void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream);
 // kRoutedTiles: the routed experts' [R,I]; kSharedTiles: the shared experts'
 // [T, n_s*I_s].
 void launch_gate_up_raw_bf16(const FfnArgs& a, hipStream_t stream);
+// The routed experts' down product Y[rows] (+)= A[rows] W_d[e]^T alone (no
+// shared tiles), storing or, with accumulate, adding to `y`.
+void launch_down_routed_bf16(const FfnArgs& a, bool accumulate, hipStream_t stream);
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream);
 void launch_gate_up_f32(const FfnArgs& a, hipStream_t stream);
 void launch_down_f32(const FfnArgs& a, hipStream_t stream);

@@ -295,7 +295,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // forward layout, then the backward scratch.
 struct BLayout {
   size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, Gs, Us, As, Asbf, dAs, dxs,
-      total;
+      wdT, wgT, wuT, dYh, dYl, dGh, dGl, dUh, dUl, total;
 };
 
 BLayout backward_layout_of(const moe_dims_t& D) {
@@ -327,6 +327,17 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.Asbf = take(D.dtype == MOE_BF16 ? ts * 2 : 0);
   B.dAs = take(ts * 4);
   B.dxs = take(D.n_shared ? T * d * 4 : 0);
+  const bool bf = D.dtype == MOE_BF16;
+  const size_t wsz = bf ? (size_t)D.E * I * d * 2 : 0;
+  B.wdT = take(wsz);
+  B.wgT = take(wsz);
+  B.wuT = take(wsz);
+  B.dYh = take(bf ? R * d * 2 : 0);
+  B.dYl = take(bf ? R * d * 2 : 0);
+  B.dGh = take(bf ? R * I * 2 : 0);
+  B.dGl = take(bf ? R * I * 2 : 0);
+  B.dUh = take(bf ? R * I * 2 : 0);
+  B.dUl = take(bf ? R * I * 2 : 0);
   B.total = o;
   return B;
 }
@@ -421,6 +432,17 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
   ba.tile_off = at<int32_t>(ws, L.tile_off);
   ba.ctr = at<int32_t>(ws, L.ctr);
   ba.Abf = D.dtype == MOE_BF16 ? at<uint16_t>(ws, B.Abf) : nullptr;
+  if (D.dtype == MOE_BF16) {
+    ba.wdT = at<uint16_t>(ws, B.wdT);
+    ba.wgT = at<uint16_t>(ws, B.wgT);
+    ba.wuT = at<uint16_t>(ws, B.wuT);
+    ba.dYh = at<uint16_t>(ws, B.dYh);
+    ba.dYl = at<uint16_t>(ws, B.dYl);
+    ba.dGh = at<uint16_t>(ws, B.dGh);
+    ba.dGl = at<uint16_t>(ws, B.dGl);
+    ba.dUh = at<uint16_t>(ws, B.dUh);
+    ba.dUl = at<uint16_t>(ws, B.dUl);
+  }
   ba.prefix = at<int32_t>(ws, B.prefix);
   ba.G = at<float>(ws, B.G);
   ba.U = at<float>(ws, B.U);
