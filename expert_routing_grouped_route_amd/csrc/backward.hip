@@ -522,24 +522,49 @@ __global__ __launch_bounds__(256) void bwd_bias_kernel(const float* __restrict__
 
 unsigned ew_grid(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); }
 
-// out[e][q][p] = in[e][p][q] for bf16 [E][P][Q]; 64x64 tiles through LDS,
-// reads and writes along the contiguous index.  Block (q-tile, p-tile, e).
+// out[e][q][p] = in[e][p][q] for bf16 [E][P][Q]; 64x64 tiles through LDS.
+// Each lane reads 8 consecutive elements of a row (16 bytes) and writes 8
+// consecutive elements of a transposed row; edges and unaligned rows go
+// element by element.  Block (q-tile, p-tile, e).
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
                                                              int P, int Q,
                                                              uint16_t* __restrict__ out) {
-  __shared__ uint16_t tile[64][65];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // 144-byte rows
   const int q0 = blockIdx.x * 64, p0 = blockIdx.y * 64, e = blockIdx.z;
   const uint16_t* src = in + (size_t)e * P * Q;
   uint16_t* dst = out + (size_t)e * P * Q;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int p = p0 + r, q = q0 + tx;
-    if (p < P && q < Q) tile[r][tx] = src[(size_t)p * Q + q];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int v = threadIdx.x + 256 * u, r = v >> 3, c = (v & 7) * 8;
+    const int p = p0 + r, q = q0 + c;
+    const uint16_t* sp = src + (size_t)p * Q + q;
+    if (p < P && q + 8 <= Q && ((reinterpret_cast<uintptr_t>(sp) & 15) == 0)) {
+      *reinterpret_cast<u32x4*>(&tile[r][c]) = *reinterpret_cast<const u32x4*>(sp);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tile[r][c + i] = (p < P && q + i < Q) ? sp[i] : 0;
+    }
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) {
-    const int q = q0 + r, p = p0 + tx;
-    if (q < Q && p < P) dst[(size_t)q * P + p] = tile[tx][r];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int v = threadIdx.x + 256 * u, r = v >> 3, c = (v & 7) * 8;
+    const int q = q0 + r, p = p0 + c;
+    if (q >= Q) continue;
+    uint16_t* dp = dst + (size_t)q * P + p;
+    uint16_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = tile[c + i][r];
+    if (p + 8 <= P && ((reinterpret_cast<uintptr_t>(dp) & 15) == 0)) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (uint32_t)w[2 * i] | ((uint32_t)w[2 * i + 1] << 16);
+      *reinterpret_cast<u32x4*>(dp) = o;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (p + i < P) dp[i] = w[i];
+    }
   }
 }
 
