@@ -27,6 +27,9 @@ struct BwdArgs {
   uint16_t *wdT, *wgT, *wuT;               // bf16: [E,I,d], [E,d,I], [E,d,I] transposed weights
   uint16_t *dYh, *dYl;                     // bf16: [R,d] hi and lo parts of dY
   uint16_t *dGh, *dGl, *dUh, *dUl;         // bf16: [R,I] hi and lo parts of dG and dU
+  int32_t* poff;                           // bf16: [E+1] padded per-expert parts (seg_offsets_kernel)
+  int64_t seg_ld;                          // bf16: row length of tA and tB (>= poff[E])
+  uint16_t *tA, *tB;                       // bf16: [max(d,I), seg_ld] transposed operands
   int32_t* prefix;                         // [E+1]
   float *G, *U, *Ar, *dA;                  // [R,I] each
   float *y, *dY, *dXs;                     // [R,d] each

@@ -581,6 +581,97 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(const float* __restrict
   }
 }
 
+// Padded part of each expert along the reduction index of a weight-gradient
+// product: 2 * roundup(n_e, 64) columns (the hi half, then the lo half, or
+// twice the same bf16 rows), starting at poff[e].
+__global__ __launch_bounds__(64) void seg_offsets_kernel(const int32_t* __restrict__ off, int E,
+                                                         int32_t* __restrict__ poff) {
+  if (threadIdx.x != 0) return;
+  int acc = 0;
+  for (int e = 0; e < E; ++e) {
+    poff[e] = acc;
+    acc += 2 * ((off[e + 1] - off[e] + 63) / 64 * 64);
+  }
+  poff[E] = acc;
+}
+
+// dst[c][poff[e] + h*seg + j] = part h of src[off[e] + j][c] for the sorted
+// rows j < n_e of expert e (seg = roundup(n_e, 64)), zero for j >= n_e: the
+// rows transposed so that the reduction over an expert's rows is contiguous.
+// F32: part 0 = bf16(v), part 1 = bf16(v - part 0); bf16 source: both parts
+// are v.  64x64 tiles through LDS, 8 elements per lane on each side.  Block
+// (64 destination columns, 64 destination rows); tiles past poff[E] return.
+template <bool F32>
+__global__ __launch_bounds__(256) void seg_transpose_kernel(const void* __restrict__ src, int C,
+                                                            const int32_t* __restrict__ off,
+                                                            const int32_t* __restrict__ poff, int E,
+                                                            int64_t ld, uint16_t* __restrict__ dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // [j][c]
+  const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  if (j0 >= poff[E]) return;
+  int lo = 0, hi = E - 1;  // last e with poff[e] <= j0 (the expert whose part holds j0)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (poff[mid] <= j0) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int seg = (poff[e + 1] - poff[e]) / 2, local = j0 - poff[e];
+  const int half = local >= seg ? 1 : 0, col = local - half * seg;
+  const int n_e = off[e + 1] - off[e], r0 = off[e] + col;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int v = threadIdx.x + 256 * u, jj = v >> 3, cc = (v & 7) * 8;
+    const bool ok = col + jj < n_e && c0 + cc + 8 <= C;
+    uint16_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = 0;
+    if (ok) {
+      const size_t at = (size_t)(r0 + jj) * C + c0 + cc;
+      if (F32) {
+        const f32x4 x0 = reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + at)[0];
+        const f32x4 x1 = reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + at)[1];
+        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t h = pack_bf16x2_rne(x[i], 0.f);
+          w[i] = half ? (uint16_t)pack_bf16x2_rne(x[i] - __uint_as_float(h << 16), 0.f)
+                      : (uint16_t)h;
+        }
+      } else {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + at);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w[2 * i] = (uint16_t)q[i];
+          w[2 * i + 1] = (uint16_t)(q[i] >> 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[jj][cc + i] = w[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int v = threadIdx.x + 256 * u, r = v >> 3, jc = (v & 7) * 8;
+    if (c0 + r >= C) continue;
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)tile[jc + 2 * i][r] | ((uint32_t)tile[jc + 2 * i + 1][r] << 16);
+    *reinterpret_cast<u32x4*>(dst + (size_t)(c0 + r) * ld + j0 + jc) = o;
+  }
+}
+
+void launch_seg_transpose(const void* src, bool f32, int C, const int32_t* off,
+                          const int32_t* poff, int E, int64_t ld, uint16_t* dst, hipStream_t s) {
+  const dim3 grid((unsigned)(ld / 64), (unsigned)((C + 63) / 64));
+  if (f32)
+    hipLaunchKernelGGL(seg_transpose_kernel<true>, grid, dim3(256), 0, s, src, C, off, poff, E, ld, dst);
+  else
+    hipLaunchKernelGGL(seg_transpose_kernel<false>, grid, dim3(256), 0, s, src, C, off, poff, E, ld, dst);
+}
+
 void launch_transpose_bf16(const void* in, int E, int P, int Q, void* out, hipStream_t s) {
   const dim3 grid((unsigned)((Q + 63) / 64), (unsigned)((P + 63) / 64), (unsigned)E);
   hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s,
@@ -699,12 +790,32 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   } else {
     ragged_m(a.dY, false, d, a.wd, bf, I, 1, (int64_t)d * I, a.dA, I, I, d, false);
   }
-  if (bf) ragged_k(a.dY, false, d, a.Abf, true, I, a.dw_down, I, (int64_t)d * I, d, I);
-  else ragged_k(a.dY, false, d, a.Ar, false, I, a.dw_down, I, (int64_t)d * I, d, I);
+  // weight gradients.  bf16 layers: the operands transposed into per-expert
+  // zero-padded parts (an fp32 operand as its hi half then its lo half, the
+  // bf16 one twice), then one product per weight on the forward tile loop.
+  if (bf) {
+    hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(64), 0, s, a.offsets, E, a.poff);
+    launch_seg_transpose(a.dY, true, d, a.offsets, a.poff, E, a.seg_ld, a.tA, s);
+    launch_seg_transpose(a.Abf, false, I, a.offsets, a.poff, E, a.seg_ld, a.tB, s);
+    SegGemmArgs sg = {a.tA, a.tB, a.seg_ld, a.poff, a.dw_down, E, d, I};
+    launch_seg_gemm_bf16(sg, s);
+  } else {
+    ragged_k(a.dY, false, d, a.Ar, false, I, a.dw_down, I, (int64_t)d * I, d, I);
+  }
   // dG, dU in place of G, U; dW_g, dW_u; dXs = dG W_g[e] + dU W_u[e]
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, a.dA, nRI);
-  ragged_k(a.G, false, I, a.xs, bf, d, a.dw_gate, d, (int64_t)I * d, I, d);
-  ragged_k(a.U, false, I, a.xs, bf, d, a.dw_up, d, (int64_t)I * d, I, d);
+  if (bf) {
+    launch_seg_transpose(a.xs, false, d, a.offsets, a.poff, E, a.seg_ld, a.tB, s);
+    launch_seg_transpose(a.G, true, I, a.offsets, a.poff, E, a.seg_ld, a.tA, s);
+    SegGemmArgs sg = {a.tA, a.tB, a.seg_ld, a.poff, a.dw_gate, E, I, d};
+    launch_seg_gemm_bf16(sg, s);
+    launch_seg_transpose(a.U, true, I, a.offsets, a.poff, E, a.seg_ld, a.tA, s);
+    sg.out = a.dw_up;
+    launch_seg_gemm_bf16(sg, s);
+  } else {
+    ragged_k(a.G, false, I, a.xs, bf, d, a.dw_gate, d, (int64_t)I * d, I, d);
+    ragged_k(a.U, false, I, a.xs, bf, d, a.dw_up, d, (int64_t)I * d, I, d);
+  }
   if (bf) {
     hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, nRI, a.dGh,
                        a.dGl);

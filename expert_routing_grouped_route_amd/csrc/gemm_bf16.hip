@@ -550,6 +550,45 @@ __global__ __launch_bounds__(NTHREADS) void down_routed_bf16_kernel(FfnArgs p, G
   run_tile<false, BUF, false, ACC>(t, smem);
 }
 
+// Weight-gradient tiles: expert e, 256-row m-tile, 256-column n-tile; K runs
+// over the expert's zero-padded part of the shared reduction index.
+template <bool BUF>
+__global__ __launch_bounds__(NTHREADS) void seg_gemm_bf16_kernel(SegGemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+  const int mt = (p.M + kBM - 1) / kBM, ntl = (p.N + BN - 1) / BN;
+  const int per_e = mt * ntl;
+  const int L = xcd_remap(blockIdx.x);
+  if (L >= p.E * per_e) return;
+  const int e = L / per_e, rem = L - e * per_e;
+  const int m0 = (rem / ntl) * kBM, n0 = (rem % ntl) * BN;
+  const int k0 = p.poff[e], nk = (p.poff[e + 1] - k0) / BK;
+  BTile t;
+  t.rows = min(kBM, p.M - m0);
+  t.wrows = min(BN, p.N - n0);
+  float* out = p.out + (size_t)e * p.M * p.N + (size_t)m0 * p.N + n0;
+  if (nk == 0) {  // no rows: the gradient is zero
+    for (int i = threadIdx.x; i < t.rows * (t.wrows / 4); i += NTHREADS) {
+      const int r = i / (t.wrows / 4), c = (i % (t.wrows / 4)) * 4;
+      *reinterpret_cast<f32x4*>(out + (size_t)r * p.N + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  t.X = reinterpret_cast<const uint8_t*>(p.A + (size_t)m0 * p.ld + k0);
+  t.x_ld = (size_t)p.ld * 2;
+  t.rmap = nullptr;
+  t.rdiv = 1;
+  t.W[0] = t.W[1] = reinterpret_cast<const uint8_t*>(p.B + (size_t)n0 * p.ld + k0);
+  t.w_ld = (size_t)p.ld * 2;
+  t.nk = nk;
+  t.kps = 0;
+  t.w_seg = 0;
+  t.Out = reinterpret_cast<uint8_t*>(out);
+  t.out_ld = p.N;
+  t.out_cols = t.wrows;
+  t.raw_off = 0;
+  run_tile<false, BUF>(t, smem);
+}
+
 GemmGrid bf16_gate_up_grid(const FfnArgs& a) {
   GemmGrid g;
   g.mtb = (int)routed_mtile_bound(a.R, a.E);
@@ -629,6 +668,15 @@ void launch_down_routed_bf16(const FfnArgs& a, bool accumulate, hipStream_t stre
   auto kern = buf ? (accumulate ? down_routed_bf16_kernel<true, true> : down_routed_bf16_kernel<true, false>)
                   : (accumulate ? down_routed_bf16_kernel<false, true> : down_routed_bf16_kernel<false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a, g);
+}
+
+void launch_seg_gemm_bf16(const SegGemmArgs& a, hipStream_t stream) {
+  const int64_t tiles = (int64_t)a.E * ((a.M + kBM - 1) / kBM) * ((a.N + BN - 1) / BN);
+  if (tiles == 0) return;
+  // buffer loads when a tile's offsets (256 rows of ld elements) fit in 32 bits
+  const bool buf = (uint64_t)(kBM + 2) * (uint64_t)a.ld * 2 < (1ull << 32);
+  auto kern = buf ? seg_gemm_bf16_kernel<true> : seg_gemm_bf16_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)pad_slots(tiles)), dim3(NTHREADS), 0, stream, a);
 }
 
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream) {

@@ -97,6 +97,21 @@ void launch_gate_up_raw_bf16(const FfnArgs& a, hipStream_t stream);
 // The routed experts' down product Y[rows] (+)= A[rows] W_d[e]^T alone (no
 // shared tiles), storing or, with accumulate, adding to `y`.
 void launch_down_routed_bf16(const FfnArgs& a, bool accumulate, hipStream_t stream);
+
+// Per-expert products reduced over each expert's rows (weight gradients):
+// out[e] [M,N] = sum over k of A(m, k) B(n, k), where A [M, ld] and B [N, ld]
+// are bf16 with the reduction index contiguous, and expert e's part spans
+// columns poff[e] .. poff[e+1] (multiples of 64, zero-padded).  Experts with
+// an empty part get zeros.  On the gate/up and down kernels' tile loop.
+struct SegGemmArgs {
+  const uint16_t* A;      // [M, ld]
+  const uint16_t* B;      // [N, ld]
+  int64_t ld;             // elements between rows of A and of B
+  const int32_t* poff;    // [E+1]
+  float* out;             // [E, M, N] fp32
+  int E, M, N;
+};
+void launch_seg_gemm_bf16(const SegGemmArgs& a, hipStream_t stream);
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream);
 void launch_gate_up_f32(const FfnArgs& a, hipStream_t stream);
 void launch_down_f32(const FfnArgs& a, hipStream_t stream);

@@ -1,6 +1,7 @@
 // C ABI of the MoE-layer forward pass: argument validation, workspace
 // carving and launch sequencing on the caller's stream.  Declarations and
 // the contract of every entry point are in include/moe.h.
+#include <algorithm>
 #include <initializer_list>
 
 #include "moe.h"
@@ -295,7 +296,8 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // forward layout, then the backward scratch.
 struct BLayout {
   size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, Gs, Us, As, Asbf, dAs, dxs,
-      wdT, wgT, wuT, dYh, dYl, dGh, dGl, dUh, dUl, total;
+      wdT, wgT, wuT, dYh, dYl, dGh, dGl, dUh, dUl, poff, tA, tB, total;
+  int64_t seg_ld;
 };
 
 BLayout backward_layout_of(const moe_dims_t& D) {
@@ -338,6 +340,12 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.dGl = take(bf ? R * I * 2 : 0);
   B.dUh = take(bf ? R * I * 2 : 0);
   B.dUl = take(bf ? R * I * 2 : 0);
+  // weight-gradient operands: per expert 2 * roundup(n_e, 64) columns
+  B.seg_ld = ((int64_t)(2 * (R + 63 * (size_t)D.E)) + 63) / 64 * 64;
+  const size_t rows = std::max(d, I);
+  B.poff = take(bf ? ((size_t)D.E + 1) * 4 : 0);
+  B.tA = take(bf ? rows * (size_t)B.seg_ld * 2 : 0);
+  B.tB = take(bf ? rows * (size_t)B.seg_ld * 2 : 0);
   B.total = o;
   return B;
 }
@@ -442,6 +450,10 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
     ba.dGl = at<uint16_t>(ws, B.dGl);
     ba.dUh = at<uint16_t>(ws, B.dUh);
     ba.dUl = at<uint16_t>(ws, B.dUl);
+    ba.poff = at<int32_t>(ws, B.poff);
+    ba.seg_ld = B.seg_ld;
+    ba.tA = at<uint16_t>(ws, B.tA);
+    ba.tB = at<uint16_t>(ws, B.tB);
   }
   ba.prefix = at<int32_t>(ws, B.prefix);
   ba.G = at<float>(ws, B.G);
