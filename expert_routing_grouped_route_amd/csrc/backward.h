@@ -29,7 +29,8 @@ struct BwdArgs {
   uint16_t *dGh, *dGl, *dUh, *dUl;         // bf16: [R,I] hi and lo parts of dG and dU
   int32_t* poff;                           // bf16: [E+1] padded per-expert parts (seg_offsets_kernel)
   int64_t seg_ld;                          // bf16: row length of tA and tB (>= poff[E])
-  uint16_t *tA, *tB;                       // bf16: [max(d,I), seg_ld] transposed operands
+  uint16_t *tA, *tB;                       // bf16: [max(d, I, ns*Is), seg_ld] transposed operands
+  int32_t *off1, *poff1;                   // bf16: [2] each, the T rows as one segment
   int32_t* prefix;                         // [E+1]
   float *G, *U, *Ar, *dA;                  // [R,I] each
   float *y, *dY, *dXs;                     // [R,d] each

@@ -595,6 +595,16 @@ __global__ __launch_bounds__(64) void seg_offsets_kernel(const int32_t* __restri
   poff[E] = acc;
 }
 
+// One segment of T rows: off = {0, T}, poff = {0, 2 * roundup(T, 64)}.
+__global__ __launch_bounds__(64) void single_seg_offsets_kernel(int T, int32_t* __restrict__ off,
+                                                                int32_t* __restrict__ poff) {
+  if (threadIdx.x != 0) return;
+  off[0] = 0;
+  off[1] = T;
+  poff[0] = 0;
+  poff[1] = 2 * ((T + 63) / 64 * 64);
+}
+
 // dst[c][poff[e] + h*seg + j] = part h of src[off[e] + j][c] for the sorted
 // rows j < n_e of expert e (seg = roundup(n_e, 64)), zero for j >= n_e: the
 // rows transposed so that the reduction over an expert's rows is contiguous.
@@ -878,18 +888,47 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     }
     hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, nT,
                        (int)bf, a.As, bf ? a.Asbf : nullptr);
-    for (int sh = 0; sh < ns; ++sh) {
-      const size_t cs = (size_t)sh * Is;
-      // dA_s = dout W_sd[s]; dW_sd[s] = dout^T A_s
-      uni_m(a.dout, false, d, wslice(a.wsd, sh), bf, Is, 1, a.dAs + cs, ld, Is, d, false);
-      if (bf) uni_k(a.dout, false, d, a.Asbf + cs, true, ld, a.dwsh_down + cs * d, Is, d, Is);
-      else uni_k(a.dout, false, d, a.As + cs, false, ld, a.dwsh_down + cs * d, Is, d, Is);
+    // dA_s = dout W_sd[s]; dW_sd[s] = dout^T A_s.  bf16 layers take the
+    // weight gradients on the forward tile loop with the T rows as one
+    // segment (dout and the shared experts' tensors transposed once each).
+    for (int sh = 0; sh < ns; ++sh)
+      uni_m(a.dout, false, d, wslice(a.wsd, sh), bf, Is, 1, a.dAs + (size_t)sh * Is, ld, Is, d,
+            false);
+    auto seg1 = [&](const uint16_t* A_, const uint16_t* B_, float* out, int M, int N) {
+      SegGemmArgs g1 = {A_, B_, a.seg_ld, a.poff1, out, 1, M, N};
+      launch_seg_gemm_bf16(g1, s);
+    };
+    if (bf) {
+      hipLaunchKernelGGL(single_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.off1,
+                         a.poff1);
+      launch_seg_transpose(a.dout, true, d, a.off1, a.poff1, 1, a.seg_ld, a.tA, s);
+      launch_seg_transpose(a.Asbf, false, (int)ld, a.off1, a.poff1, 1, a.seg_ld, a.tB, s);
+      for (int sh = 0; sh < ns; ++sh)
+        seg1(a.tA, a.tB + (size_t)sh * Is * a.seg_ld, a.dwsh_down + (size_t)sh * d * Is, d, Is);
+    } else {
+      for (int sh = 0; sh < ns; ++sh) {
+        const size_t cs = (size_t)sh * Is;
+        uni_k(a.dout, false, d, a.As + cs, false, ld, a.dwsh_down + cs * d, Is, d, Is);
+      }
     }
     hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, a.dAs, nT);
+    if (bf) {
+      launch_seg_transpose(a.x, false, d, a.off1, a.poff1, 1, a.seg_ld, a.tB, s);
+      launch_seg_transpose(a.Gs, true, (int)ld, a.off1, a.poff1, 1, a.seg_ld, a.tA, s);
+      for (int sh = 0; sh < ns; ++sh)
+        seg1(a.tA + (size_t)sh * Is * a.seg_ld, a.tB, a.dwsh_gate + (size_t)sh * Is * d, Is, d);
+      launch_seg_transpose(a.Us, true, (int)ld, a.off1, a.poff1, 1, a.seg_ld, a.tA, s);
+      for (int sh = 0; sh < ns; ++sh)
+        seg1(a.tA + (size_t)sh * Is * a.seg_ld, a.tB, a.dwsh_up + (size_t)sh * Is * d, Is, d);
+    } else {
+      for (int sh = 0; sh < ns; ++sh) {
+        const size_t cs = (size_t)sh * Is;
+        uni_k(a.Gs + cs, false, ld, a.x, bf, d, a.dwsh_gate + cs * d, d, Is, d);
+        uni_k(a.Us + cs, false, ld, a.x, bf, d, a.dwsh_up + cs * d, d, Is, d);
+      }
+    }
     for (int sh = 0; sh < ns; ++sh) {
       const size_t cs = (size_t)sh * Is;
-      uni_k(a.Gs + cs, false, ld, a.x, bf, d, a.dwsh_gate + cs * d, d, Is, d);
-      uni_k(a.Us + cs, false, ld, a.x, bf, d, a.dwsh_up + cs * d, d, Is, d);
       uni_m(a.Gs + cs, false, ld, wslice(a.wsg, sh), bf, d, 1, a.dxs, d, d, Is, sh > 0);
       uni_m(a.Us + cs, false, ld, wslice(a.wsu, sh), bf, d, 1, a.dxs, d, d, Is, true);
     }

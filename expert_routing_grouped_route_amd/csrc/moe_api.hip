@@ -296,7 +296,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // forward layout, then the backward scratch.
 struct BLayout {
   size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, Gs, Us, As, Asbf, dAs, dxs,
-      wdT, wgT, wuT, dYh, dYl, dGh, dGl, dUh, dUl, poff, tA, tB, total;
+      wdT, wgT, wuT, dYh, dYl, dGh, dGl, dUh, dUl, poff, tA, tB, off1, poff1, total;
   int64_t seg_ld;
 };
 
@@ -342,8 +342,10 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.dUl = take(bf ? R * I * 2 : 0);
   // weight-gradient operands: per expert 2 * roundup(n_e, 64) columns
   B.seg_ld = ((int64_t)(2 * (R + 63 * (size_t)D.E)) + 63) / 64 * 64;
-  const size_t rows = std::max(d, I);
+  const size_t rows = std::max(std::max(d, I), (size_t)D.n_shared * Is);
   B.poff = take(bf ? ((size_t)D.E + 1) * 4 : 0);
+  B.off1 = take(bf ? 8 : 0);
+  B.poff1 = take(bf ? 8 : 0);
   B.tA = take(bf ? rows * (size_t)B.seg_ld * 2 : 0);
   B.tB = take(bf ? rows * (size_t)B.seg_ld * 2 : 0);
   B.total = o;
@@ -454,6 +456,8 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
     ba.seg_ld = B.seg_ld;
     ba.tA = at<uint16_t>(ws, B.tA);
     ba.tB = at<uint16_t>(ws, B.tB);
+    ba.off1 = at<int32_t>(ws, B.off1);
+    ba.poff1 = at<int32_t>(ws, B.poff1);
   }
   ba.prefix = at<int32_t>(ws, B.prefix);
   ba.G = at<float>(ws, B.G);
