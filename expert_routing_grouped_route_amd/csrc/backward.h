@@ -31,6 +31,10 @@ struct BwdArgs {
   int64_t seg_ld;                          // bf16: row length of tA and tB (>= poff[E])
   uint16_t *tA, *tB;                       // bf16: [max(d, I, ns*Is), seg_ld] transposed operands
   int32_t *off1, *poff1;                   // bf16: [2] each, the T rows as one segment
+  int32_t* tiles1;                         // bf16: M-tile table of that one segment
+  uint16_t *wsdT, *wsgT, *wsuT;            // bf16: [ns*Is, d], [d, ns*Is], [d, ns*Is]
+  uint16_t *dOh, *dOl;                     // bf16: [T,d] hi and lo parts of dout
+  uint16_t *sGh, *sGl, *sUh, *sUl;         // bf16: [T, ns*Is] hi and lo parts of dG_s and dU_s
   int32_t* prefix;                         // [E+1]
   float *G, *U, *Ar, *dA;                  // [R,I] each
   float *y, *dY, *dXs;                     // [R,d] each

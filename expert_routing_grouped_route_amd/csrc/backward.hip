@@ -890,17 +890,52 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
                        (int)bf, a.As, bf ? a.Asbf : nullptr);
     // dA_s = dout W_sd[s]; dW_sd[s] = dout^T A_s.  bf16 layers take the
     // weight gradients on the forward tile loop with the T rows as one
-    // segment (dout and the shared experts' tensors transposed once each).
-    for (int sh = 0; sh < ns; ++sh)
-      uni_m(a.dout, false, d, wslice(a.wsd, sh), bf, Is, 1, a.dAs + (size_t)sh * Is, ld, Is, d,
-            false);
+    // segment (dout and the shared experts' tensors transposed once each),
+    // and the input-gradient products of all shared experts at once on the
+    // forward down kernel: dA_all = dout [W_sd[0] | W_sd[1] | ..] and
+    // dx_shared = [dG_0 | dG_1 | ..] [W_sg[0]; W_sg[1]; ..] + the same for U,
+    // with the weights transposed and dout, dG, dU as bf16 hi and lo rows.
+    FfnArgs f1 = {};
+    auto down1 = [&](const uint16_t* hi_, const uint16_t* lo_, const uint16_t* wT, int K, int N,
+                     float* out, bool acc) {
+      f1.wd = wT;
+      f1.I = K;
+      f1.d = N;
+      f1.y = out;
+      f1.a = const_cast<uint16_t*>(hi_);
+      launch_down_routed_bf16(f1, acc, s);
+      f1.a = const_cast<uint16_t*>(lo_);
+      launch_down_routed_bf16(f1, true, s);
+    };
+    if (bf) {
+      hipLaunchKernelGGL(single_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.off1,
+                         a.poff1);
+      launch_tile_table(a.off1, 1, a.tiles1, a.ctr, s);
+      f1.offsets = a.off1;
+      f1.tile_off = a.tiles1;
+      f1.ctr = a.ctr;
+      f1.T = T;
+      f1.R = T;
+      f1.E = 1;
+      f1.bf16 = true;
+      f1.part = kRoutedTiles;
+      launch_transpose_bf16(a.wsd, ns, d, Is, a.wsdT, s);        // [ns*Is, d]
+      launch_transpose_bf16(a.wsg, 1, (int)ld, d, a.wsgT, s);    // [d, ns*Is]
+      launch_transpose_bf16(a.wsu, 1, (int)ld, d, a.wsuT, s);
+      const int64_t nTd = T * d;
+      hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nTd)), dim3(256), 0, s, a.dout, nTd,
+                         a.dOh, a.dOl);
+      down1(a.dOh, a.dOl, a.wsdT, d, (int)ld, a.dAs, false);
+    } else {
+      for (int sh = 0; sh < ns; ++sh)
+        uni_m(a.dout, false, d, wslice(a.wsd, sh), bf, Is, 1, a.dAs + (size_t)sh * Is, ld, Is, d,
+              false);
+    }
     auto seg1 = [&](const uint16_t* A_, const uint16_t* B_, float* out, int M, int N) {
       SegGemmArgs g1 = {A_, B_, a.seg_ld, a.poff1, out, 1, M, N};
       launch_seg_gemm_bf16(g1, s);
     };
     if (bf) {
-      hipLaunchKernelGGL(single_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.off1,
-                         a.poff1);
       launch_seg_transpose(a.dout, true, d, a.off1, a.poff1, 1, a.seg_ld, a.tA, s);
       launch_seg_transpose(a.Asbf, false, (int)ld, a.off1, a.poff1, 1, a.seg_ld, a.tB, s);
       for (int sh = 0; sh < ns; ++sh)
@@ -927,10 +962,19 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
         uni_k(a.Us + cs, false, ld, a.x, bf, d, a.dwsh_up + cs * d, d, Is, d);
       }
     }
-    for (int sh = 0; sh < ns; ++sh) {
-      const size_t cs = (size_t)sh * Is;
-      uni_m(a.Gs + cs, false, ld, wslice(a.wsg, sh), bf, d, 1, a.dxs, d, d, Is, sh > 0);
-      uni_m(a.Us + cs, false, ld, wslice(a.wsu, sh), bf, d, 1, a.dxs, d, d, Is, true);
+    if (bf) {
+      hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, nT, a.sGh,
+                         a.sGl);
+      hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Us, nT, a.sUh,
+                         a.sUl);
+      down1(a.sGh, a.sGl, a.wsgT, (int)ld, d, a.dxs, false);
+      down1(a.sUh, a.sUl, a.wsuT, (int)ld, d, a.dxs, true);
+    } else {
+      for (int sh = 0; sh < ns; ++sh) {
+        const size_t cs = (size_t)sh * Is;
+        uni_m(a.Gs + cs, false, ld, wslice(a.wsg, sh), bf, d, 1, a.dxs, d, d, Is, sh > 0);
+        uni_m(a.Us + cs, false, ld, wslice(a.wsu, sh), bf, d, 1, a.dxs, d, d, Is, true);
+      }
     }
   }
 

@@ -296,7 +296,8 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // forward layout, then the backward scratch.
 struct BLayout {
   size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, Gs, Us, As, Asbf, dAs, dxs,
-      wdT, wgT, wuT, dYh, dYl, dGh, dGl, dUh, dUl, poff, tA, tB, off1, poff1, total;
+      wdT, wgT, wuT, dYh, dYl, dGh, dGl, dUh, dUl, poff, tA, tB, off1, poff1, tiles1, wsdT,
+      wsgT, wsuT, dOh, dOl, sGh, sGl, sUh, sUl, total;
   int64_t seg_ld;
 };
 
@@ -346,6 +347,18 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.poff = take(bf ? ((size_t)D.E + 1) * 4 : 0);
   B.off1 = take(bf ? 8 : 0);
   B.poff1 = take(bf ? 8 : 0);
+  const bool bsh = bf && D.n_shared > 0;
+  const size_t nsI = (size_t)D.n_shared * Is;
+  B.tiles1 = take(bsh ? (size_t)tile_table_ints((int64_t)T, 1) * 4 : 0);
+  B.wsdT = take(bsh ? nsI * d * 2 : 0);
+  B.wsgT = take(bsh ? nsI * d * 2 : 0);
+  B.wsuT = take(bsh ? nsI * d * 2 : 0);
+  B.dOh = take(bsh ? T * d * 2 : 0);
+  B.dOl = take(bsh ? T * d * 2 : 0);
+  B.sGh = take(bsh ? T * nsI * 2 : 0);
+  B.sGl = take(bsh ? T * nsI * 2 : 0);
+  B.sUh = take(bsh ? T * nsI * 2 : 0);
+  B.sUl = take(bsh ? T * nsI * 2 : 0);
   B.tA = take(bf ? rows * (size_t)B.seg_ld * 2 : 0);
   B.tB = take(bf ? rows * (size_t)B.seg_ld * 2 : 0);
   B.total = o;
@@ -458,6 +471,18 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
     ba.tB = at<uint16_t>(ws, B.tB);
     ba.off1 = at<int32_t>(ws, B.off1);
     ba.poff1 = at<int32_t>(ws, B.poff1);
+    if (sh) {
+      ba.tiles1 = at<int32_t>(ws, B.tiles1);
+      ba.wsdT = at<uint16_t>(ws, B.wsdT);
+      ba.wsgT = at<uint16_t>(ws, B.wsgT);
+      ba.wsuT = at<uint16_t>(ws, B.wsuT);
+      ba.dOh = at<uint16_t>(ws, B.dOh);
+      ba.dOl = at<uint16_t>(ws, B.dOl);
+      ba.sGh = at<uint16_t>(ws, B.sGh);
+      ba.sGl = at<uint16_t>(ws, B.sGl);
+      ba.sUh = at<uint16_t>(ws, B.sUh);
+      ba.sUl = at<uint16_t>(ws, B.sUl);
+    }
   }
   ba.prefix = at<int32_t>(ws, B.prefix);
   ba.G = at<float>(ws, B.G);
