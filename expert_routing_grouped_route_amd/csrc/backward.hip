@@ -480,7 +480,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(float* __restrict__ G,
 }
 
 // dx[t] = sum_j dXs[inv[t*k+j]] + sum_j dl[t*k+j] W_r[ids[t*k+j]] (+ dxs[t]),
-// slot order, then the router term, then the shared experts' term.
+// slot order, then the router term, then the shared experts' term.  One wave
+// per token, four consecutive columns per lane and step.
 template <bool WR_BF16>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dXs,
                                                      const int32_t* __restrict__ inv,
@@ -492,13 +493,65 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  for (int c = lane; c < d; c += 64) {
-    float s = 0.f;
-    for (int j = 0; j < k; ++j) s += dXs[(size_t)inv[(size_t)t * k + j] * d + c];
-    for (int j = 0; j < k; ++j)
-      s = fmaf(dl[(size_t)t * k + j], load_elem<WR_BF16>(wr, (int64_t)ids[(size_t)t * k + j] * d + c), s);
-    if (dxs) s += dxs[(size_t)t * d + c];
-    dx[(size_t)t * d + c] = s;
+  int row[kMaxK], ex[kMaxK];
+  float g[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    row[j] = 0;
+    ex[j] = 0;
+    g[j] = 0.f;
+    if (j < k) {
+      row[j] = inv[(size_t)t * k + j];
+      ex[j] = ids[(size_t)t * k + j];
+      g[j] = dl[(size_t)t * k + j];
+    }
+  }
+  const int d4 = d >> 2;
+  for (int c = lane; c < d4; c += 64) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k) {
+        const f32x4 v = reinterpret_cast<const f32x4*>(dXs + (size_t)row[j] * d)[c];
+        acc[0] += v[0];
+        acc[1] += v[1];
+        acc[2] += v[2];
+        acc[3] += v[3];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k) {
+        float w[4];
+        if (WR_BF16) {
+          const uint2 q = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(wr) +
+                                                         (size_t)ex[j] * d)[c];
+          w[0] = __uint_as_float(q.x << 16);
+          w[1] = __uint_as_float(q.x & 0xFFFF0000u);
+          w[2] = __uint_as_float(q.y << 16);
+          w[3] = __uint_as_float(q.y & 0xFFFF0000u);
+        } else {
+          const f32x4 q = reinterpret_cast<const f32x4*>(static_cast<const float*>(wr) +
+                                                         (size_t)ex[j] * d)[c];
+          w[0] = q[0];
+          w[1] = q[1];
+          w[2] = q[2];
+          w[3] = q[3];
+        }
+        acc[0] = fmaf(g[j], w[0], acc[0]);
+        acc[1] = fmaf(g[j], w[1], acc[1]);
+        acc[2] = fmaf(g[j], w[2], acc[2]);
+        acc[3] = fmaf(g[j], w[3], acc[3]);
+      }
+    }
+    if (dxs) {
+      const f32x4 v = reinterpret_cast<const f32x4*>(dxs + (size_t)t * d)[c];
+      acc[0] += v[0];
+      acc[1] += v[1];
+      acc[2] += v[2];
+      acc[3] += v[3];
+    }
+    reinterpret_cast<f32x4*>(dx + (size_t)t * d)[c] = acc;
   }
 }
 
