@@ -248,14 +248,21 @@ def time_backward(cfg, dev, d, wdt, stream, warm=2, timed=5):
 
     print(f"[bench] timing {timed} calls of the backward pass", file=sys.stderr, flush=True)
     ms = timed_ms()  # products on the matrix cores (the library's default)
-    os.environ["MOE_BWD_VALU"] = "1"  # read by the library at every call
-    try:
-        ms_valu = timed_ms()
-    finally:
-        del os.environ["MOE_BWD_VALU"]
     fa, fe = backward_flops(cfg)
     tf = fa / (ms * 1e-3) / 1e12
-    tf_v = fa / (ms_valu * 1e-3) / 1e12
+    valu = None
+    if cfg.dtype == "f32":
+        # fp32 layers run every product on the grouped GEMM with free strides;
+        # MOE_BWD_VALU=1 (read by the library at every call) puts it on the VALU
+        os.environ["MOE_BWD_VALU"] = "1"
+        try:
+            ms_valu = timed_ms()
+        finally:
+            del os.environ["MOE_BWD_VALU"]
+        tf_v = fa / (ms_valu * 1e-3) / 1e12
+        valu = {"ms": round(ms_valu, 3), "achieved_tflops": round(tf_v, 2),
+                "frac_of_unpacked_fp32_fma_peak": round(tf_v / PEAK_FP32_UNPACKED_TFLOPS, 4),
+                "peak_unpacked_fma": round(PEAK_FP32_UNPACKED_TFLOPS, 1)}
     return {"entry_point": "moe_layer_bwd", "calls_timed": timed, "ms": round(ms, 3),
             "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
             "flops_algorithmic": fa, "flops_executed": fe,
@@ -263,12 +270,8 @@ def time_backward(cfg, dev, d, wdt, stream, warm=2, timed=5):
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                          "executed_tflops": round(fe / (ms * 1e-3) / 1e12, 2),
                          "note": "algorithmic FLOPs over the whole call; products on bf16 MFMA, "
-                                 "each fp32 operand as bf16 hi + lo parts (2 or 3 MFMAs per "
-                                 "product)"},
-            "vector_alu_variant": {"ms": round(ms_valu, 3), "achieved_tflops": round(tf_v, 2),
-                                   "frac_of_unpacked_fp32_fma_peak": round(
-                                       tf_v / PEAK_FP32_UNPACKED_TFLOPS, 4),
-                                   "peak_unpacked_fma": round(PEAK_FP32_UNPACKED_TFLOPS, 1)}}
+                                 "each fp32 operand as bf16 hi + lo parts"},
+            "vector_alu_variant": valu}
 
 
 def gemm_flops(cfg):
