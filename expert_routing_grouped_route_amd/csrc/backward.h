@@ -1,6 +1,7 @@
 // Host-side launcher of the layer's backward pass (internal to the library).
 #pragma once
 
+#include <algorithm>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -39,6 +40,7 @@ struct BwdArgs {
   float *G, *U, *Ar, *dA;                  // [R,I] each
   float *y, *dY, *dXs;                     // [R,d] each
   float *dw, *dl, *dls;                    // [R] each (dls: dl in sorted-row order)
+  float* rpart;                            // [router_part_rows(R, E), d] router-gradient partials
   float *Gs, *Us, *As, *dAs;               // [T, ns*Is] each (all shared experts)
   uint16_t* Asbf;                          // bf16: [T, ns*Is] the shared SwiGLU products in bf16
   float* dxs;                              // [T,d]
@@ -47,5 +49,11 @@ struct BwdArgs {
   bool bf16;
 };
 void launch_layer_bwd(const BwdArgs& a, hipStream_t stream);
+
+// Rows of BwdArgs::rpart: one per M-tile of the experts' row segments, for
+// tiles of 64 or of 128 rows (the VALU and matrix-core variants).
+inline int64_t router_part_rows(int64_t R, int E) {
+  return std::max((R + (int64_t)E * 63) / 64, (R + (int64_t)E * 127) / 128);
+}
 
 }  // namespace moe

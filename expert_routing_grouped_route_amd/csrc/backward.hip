@@ -12,12 +12,17 @@
 // gradient through unchanged; the bias gradient sums the logit gradient over
 // tokens.
 //
-// Every product is one launch of a grouped fp32 GEMM on the vector ALUs with
-// arbitrary element strides for both operands, so the same kernel serves the
-// products whose reduction runs along the weights' rows (input gradients) and
-// those that reduce over an expert's ragged rows (weight gradients).  bf16
-// operands are widened to fp32 on load; every output element is summed by
-// one thread in a fixed order, so results are reproducible bit for bit.
+// bf16 layers run every large product on the forward pass's bf16 GEMM
+// machinery: the recomputed G, U and expert outputs on the forward kernels,
+// the input gradients on the down kernel against transposed weight copies,
+// and the weight gradients, which reduce over an expert's ragged rows, on a
+// segment kernel over per-expert zero-padded transposed operands.  Each fp32
+// operand enters as a bf16 high part and a bf16 low part.  fp32 layers (and
+// MOE_BWD_VALU=1) use a grouped GEMM with free element strides, on the matrix
+// cores with split operands or on the VALU in fp32.  The router-weight
+// gradient is a two-pass fixed-order reduction on the VALU.  Every output
+// element is summed in a fixed order and no atomics are used, so results are
+// reproducible bit for bit.
 #include <algorithm>
 #include <cstdlib>
 
@@ -555,6 +560,109 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   }
 }
 
+// Router-weight gradient dW_r[e] = sum over expert e's sorted rows i of
+// dls[i] * xs[i], in two fixed-order passes.  Pass 1: block (m, c) takes M-tile
+// m of `tile` rows (tiles from `prefix`, as the grouped GEMMs number them) and
+// the 512 columns c*512 .. ; lane l of wave w owns 8 columns and sums the rows
+// w, w+4, ... of the tile in increasing order; the four waves' sums are added
+// in wave order into part[m][:].  Pass 2 adds each expert's tile partials in
+// tile order.  xs is bf16 or fp32; d is a multiple of 64.
+template <bool XBF>
+__device__ __forceinline__ void load8(const void* xs, int64_t at, float (&v)[8]) {
+  if (XBF) {
+    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xs) + at);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(xs) + at);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(xs) + at + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = a[j];
+      v[4 + j] = b[j];
+    }
+  }
+}
+
+template <bool XBF>
+__global__ __launch_bounds__(256) void router_grad_part_kernel(
+    const float* __restrict__ dls, const void* __restrict__ xs, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ prefix, int E, int d, int tile, float* __restrict__ part) {
+  __shared__ float red[3][512];
+  const int m = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (m >= prefix[E]) return;  // tiles past the last expert's
+  int lo = 0, hi = E - 1;      // the expert e with prefix[e] <= m < prefix[e + 1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= m) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int r0 = off[e] + (m - prefix[e]) * tile;
+  const int r1 = min(r0 + tile, off[e + 1]);
+  const int c = blockIdx.y * 512 + lane * 8;
+  const bool on = c < d;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (on) {
+    int i = r0 + w;
+    for (; i + 12 < r1; i += 16) {  // four rows in flight
+      float v[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) load8<XBF>(xs, (int64_t)(i + 4 * q) * d + c, v[q]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float g = dls[i + 4 * q];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, v[q][j], acc[j]);
+      }
+    }
+    for (; i < r1; i += 4) {
+      float v[8];
+      load8<XBF>(xs, (int64_t)i * d + c, v);
+      const float g = dls[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, v[j], acc[j]);
+    }
+  }
+  if (w > 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[w - 1][lane * 8 + j] = acc[j];
+  }
+  __syncthreads();
+  if (w == 0 && on) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += red[q][lane * 8 + j];
+    f32x4* o = reinterpret_cast<f32x4*>(part + (int64_t)m * d + c);
+    o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+}
+
+// Pass 2: block (e, c) sums part[prefix[e] .. prefix[e+1]) over 1024 columns
+// (4 per thread), in tile order; an expert without rows gets zeros.
+__global__ __launch_bounds__(256) void router_grad_reduce_kernel(const float* __restrict__ part,
+                                                                 const int32_t* __restrict__ prefix,
+                                                                 int d, float* __restrict__ dwr) {
+  const int e = blockIdx.x;
+  const int c = blockIdx.y * 1024 + threadIdx.x * 4;
+  if (c >= d) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int m = prefix[e]; m < prefix[e + 1]; ++m) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + (int64_t)m * d + c);
+    acc[0] += v[0];
+    acc[1] += v[1];
+    acc[2] += v[2];
+    acc[3] += v[3];
+  }
+  *reinterpret_cast<f32x4*>(dwr + (int64_t)e * d + c) = acc;
+}
+
 // dbias[e] = sum of dls over expert e's sorted rows: 256 strided partial sums,
 // then a fixed-order tree in LDS.  One block per expert.
 __global__ __launch_bounds__(256) void bwd_bias_kernel(const float* __restrict__ dls,
@@ -1033,7 +1141,13 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
 
   // router weights (dW_r[e] = dls_e^T X_e, one output row per expert) and
   // bias, then the token gradients
-  ragged_k(a.dls, false, 1, a.xs, bf, d, a.dw_router, 0, d, 1, d);
+  if (mt_bound > 0) {
+    const dim3 g1((unsigned)mt_bound, (unsigned)((d + 511) / 512));
+    hipLaunchKernelGGL((bf ? router_grad_part_kernel<true> : router_grad_part_kernel<false>), g1,
+                       dim3(256), 0, s, a.dls, a.xs, a.offsets, a.prefix, E, d, tt, a.rpart);
+  }
+  hipLaunchKernelGGL(router_grad_reduce_kernel, dim3((unsigned)E, (unsigned)((d + 1023) / 1024)),
+                     dim3(256), 0, s, a.rpart, a.prefix, d, a.dw_router);
   if (a.dbias)
     hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)E), dim3(256), 0, s, a.dls, a.offsets,
                        a.dbias);

@@ -295,7 +295,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // Workspace of the backward pass: the routing and dispatch parts of the
 // forward layout, then the backward scratch.
 struct BLayout {
-  size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, Gs, Us, As, Asbf, dAs, dxs,
+  size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, rpart, Gs, Us, As, Asbf, dAs, dxs,
       wdT, wgT, wuT, dYh, dYl, dGh, dGl, dUh, dUl, poff, tA, tB, off1, poff1, tiles1, wsdT,
       wsgT, wsuT, dOh, dOl, sGh, sGl, sUh, sUl, total;
   int64_t seg_ld;
@@ -323,6 +323,7 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.dw = take(R * 4);
   B.dl = take(R * 4);
   B.dls = take(R * 4);
+  B.rpart = take((size_t)router_part_rows((int64_t)R, D.E) * d * 4);
   const size_t ts = T * (size_t)D.n_shared * Is;  // all shared experts side by side
   B.Gs = take(ts * 4);
   B.Us = take(ts * 4);
@@ -495,6 +496,7 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
   ba.dw = at<float>(ws, B.dw);
   ba.dl = at<float>(ws, B.dl);
   ba.dls = at<float>(ws, B.dls);
+  ba.rpart = at<float>(ws, B.rpart);
   ba.Gs = sh ? at<float>(ws, B.Gs) : nullptr;
   ba.Us = sh ? at<float>(ws, B.Us) : nullptr;
   ba.As = sh ? at<float>(ws, B.As) : nullptr;
