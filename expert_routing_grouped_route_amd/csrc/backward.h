@@ -41,6 +41,9 @@ struct BwdArgs {
   float *y, *dY, *dXs;                     // [R,d] each
   float *dw, *dl, *dls;                    // [R] each (dls: dl in sorted-row order)
   float* rpart;                            // [router_part_rows(R, E), d] router-gradient partials
+  int32_t* poffS;                          // bf16, shared: [ksplit+1] slices of the shared K range
+  float* kpart;                            // bf16, shared: [ksplit, d*Is] split-K partial products
+  int ksplit;                              // bf16, shared: shared_k_split(T, d, Is)
   float *Gs, *Us, *As, *dAs;               // [T, ns*Is] each (all shared experts)
   uint16_t* Asbf;                          // bf16: [T, ns*Is] the shared SwiGLU products in bf16
   float* dxs;                              // [T,d]
@@ -49,6 +52,17 @@ struct BwdArgs {
   bool bf16;
 };
 void launch_layer_bwd(const BwdArgs& a, hipStream_t stream);
+
+// Slices of the reduction index (2 * roundup(T, 64) columns, as 64-column
+// steps) for a shared expert's weight gradient [M, N] on 256x256 tiles: as
+// many as keep all tiles within one round on 256 compute units, each at least
+// four steps long.
+inline int shared_k_split(int64_t T, int M, int N) {
+  const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t steps = 2 * ((T + 63) / 64);
+  const int64_t s = std::min<int64_t>(256 / std::max<int64_t>(tiles, 1), steps / 4);
+  return (int)std::max<int64_t>(s, 1);
+}
 
 // Rows of BwdArgs::rpart: one per M-tile of the experts' row segments, for
 // tiles of 64 or of 128 rows (the VALU and matrix-core variants).

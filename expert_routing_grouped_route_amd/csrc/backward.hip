@@ -766,6 +766,31 @@ __global__ __launch_bounds__(64) void single_seg_offsets_kernel(int T, int32_t* 
   poff[1] = 2 * ((T + 63) / 64 * 64);
 }
 
+// S slices of one segment's reduction index, 2 * roundup(T, 64) columns:
+// slice e covers the 64-column steps [e*n/S, (e+1)*n/S) of its n steps.
+__global__ __launch_bounds__(64) void split_seg_offsets_kernel(int T, int S,
+                                                               int32_t* __restrict__ poff) {
+  const int n = 2 * ((T + 63) / 64);
+  for (int e = threadIdx.x; e <= S; e += 64) poff[e] = (int)((int64_t)e * n / S) * 64;
+}
+
+// out[i] = sum over e < S of part[e*n + i], in slice order; n % 4 == 0.
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ part, int S,
+                                                         int64_t n, float* __restrict__ out) {
+  const int64_t n4 = n / 4;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 acc = reinterpret_cast<const f32x4*>(part)[i];
+    for (int e = 1; e < S; ++e) {
+      const f32x4 v = reinterpret_cast<const f32x4*>(part + (int64_t)e * n)[i];
+      acc[0] += v[0];
+      acc[1] += v[1];
+      acc[2] += v[2];
+      acc[3] += v[3];
+    }
+    reinterpret_cast<f32x4*>(out)[i] = acc;
+  }
+}
+
 // dst[c][poff[e] + h*seg + j] = part h of src[off[e] + j][c] for the sorted
 // rows j < n_e of expert e (seg = roundup(n_e, 64)), zero for j >= n_e: the
 // rows transposed so that the reduction over an expert's rows is contiguous.
@@ -1092,11 +1117,26 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
         uni_m(a.dout, false, d, wslice(a.wsd, sh), bf, Is, 1, a.dAs + (size_t)sh * Is, ld, Is, d,
               false);
     }
+    // A shared expert's weight gradient has few 256x256 tiles and a long
+    // reduction (all T rows): with ksplit > 1 the reduction is cut into
+    // ksplit slices, each slice's product goes to its own slab of kpart, and
+    // the slabs are added in slice order.
     auto seg1 = [&](const uint16_t* A_, const uint16_t* B_, float* out, int M, int N) {
-      SegGemmArgs g1 = {A_, B_, a.seg_ld, a.poff1, out, 1, M, N};
-      launch_seg_gemm_bf16(g1, s);
+      if (a.ksplit > 1) {
+        SegGemmArgs g1 = {A_, B_, a.seg_ld, a.poffS, a.kpart, a.ksplit, M, N};
+        launch_seg_gemm_bf16(g1, s);
+        const int64_t n = (int64_t)M * N;
+        hipLaunchKernelGGL(sum_slices_kernel, dim3(ew_grid(n / 4)), dim3(256), 0, s, a.kpart,
+                           a.ksplit, n, out);
+      } else {
+        SegGemmArgs g1 = {A_, B_, a.seg_ld, a.poff1, out, 1, M, N};
+        launch_seg_gemm_bf16(g1, s);
+      }
     };
     if (bf) {
+      if (a.ksplit > 1)
+        hipLaunchKernelGGL(split_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.ksplit,
+                           a.poffS);
       launch_seg_transpose(a.dout, true, d, a.off1, a.poff1, 1, a.seg_ld, a.tA, s);
       launch_seg_transpose(a.Asbf, false, (int)ld, a.off1, a.poff1, 1, a.seg_ld, a.tB, s);
       for (int sh = 0; sh < ns; ++sh)

@@ -297,8 +297,9 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 struct BLayout {
   size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, rpart, Gs, Us, As, Asbf, dAs, dxs,
       wdT, wgT, wuT, dYh, dYl, dGh, dGl, dUh, dUl, poff, tA, tB, off1, poff1, tiles1, wsdT,
-      wsgT, wsuT, dOh, dOl, sGh, sGl, sUh, sUl, total;
+      wsgT, wsuT, dOh, dOl, sGh, sGl, sUh, sUl, poffS, kpart, total;
   int64_t seg_ld;
+  int ksplit;
 };
 
 BLayout backward_layout_of(const moe_dims_t& D) {
@@ -360,6 +361,9 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.sGl = take(bsh ? T * nsI * 2 : 0);
   B.sUh = take(bsh ? T * nsI * 2 : 0);
   B.sUl = take(bsh ? T * nsI * 2 : 0);
+  B.ksplit = bsh ? shared_k_split((int64_t)T, (int)d, (int)Is) : 1;
+  B.poffS = take(bsh ? ((size_t)B.ksplit + 1) * 4 : 0);
+  B.kpart = take(bsh && B.ksplit > 1 ? (size_t)B.ksplit * d * Is * 4 : 0);
   B.tA = take(bf ? rows * (size_t)B.seg_ld * 2 : 0);
   B.tB = take(bf ? rows * (size_t)B.seg_ld * 2 : 0);
   B.total = o;
@@ -497,6 +501,9 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
   ba.dl = at<float>(ws, B.dl);
   ba.dls = at<float>(ws, B.dls);
   ba.rpart = at<float>(ws, B.rpart);
+  ba.ksplit = B.ksplit;
+  ba.poffS = B.ksplit > 0 && D.n_shared && D.dtype == MOE_BF16 ? at<int32_t>(ws, B.poffS) : nullptr;
+  ba.kpart = B.ksplit > 1 ? at<float>(ws, B.kpart) : nullptr;
   ba.Gs = sh ? at<float>(ws, B.Gs) : nullptr;
   ba.Us = sh ? at<float>(ws, B.Us) : nullptr;
   ba.As = sh ? at<float>(ws, B.As) : nullptr;
