@@ -26,16 +26,18 @@ struct BwdArgs {
   int32_t* ctr;                            // bf16: the GEMM counters (zeroed by the dispatch)
   uint16_t* Abf;                           // bf16: [R,I] the SwiGLU product in bf16
   uint16_t *wdT, *wgT, *wuT;               // bf16: [E,I,d], [E,d,I], [E,d,I] transposed weights
-  uint16_t *dYh, *dYl;                     // bf16: [R,d] hi and lo parts of dY
-  uint16_t *dGh, *dGl, *dUh, *dUl;         // bf16: [R,I] hi and lo parts of dG and dU
+                                           // (wuT after wgT in the same allocation)
+  uint16_t* dYp;                           // bf16: [R, 2d] rows of dY as [hi | lo] parts
+  uint16_t* dGU;                           // bf16: [R, 4I] rows [dG hi | dG lo | dU hi | dU lo]
   int32_t* poff;                           // bf16: [E+1] padded per-expert parts (seg_offsets_kernel)
   int64_t seg_ld;                          // bf16: row length of tA and tB (>= poff[E])
   uint16_t *tA, *tB;                       // bf16: [max(d, I, ns*Is), seg_ld] transposed operands
   int32_t *off1, *poff1;                   // bf16: [2] each, the T rows as one segment
   int32_t* tiles1;                         // bf16: M-tile table of that one segment
   uint16_t *wsdT, *wsgT, *wsuT;            // bf16: [ns*Is, d], [d, ns*Is], [d, ns*Is]
-  uint16_t *dOh, *dOl;                     // bf16: [T,d] hi and lo parts of dout
-  uint16_t *sGh, *sGl, *sUh, *sUl;         // bf16: [T, ns*Is] hi and lo parts of dG_s and dU_s
+                                           // (wsuT after wsgT in the same allocation)
+  uint16_t* dOp;                           // bf16: [T, 2d] rows of dout as [hi | lo] parts
+  uint16_t* sGU;                           // bf16: [T, 4*ns*Is] rows [dG_s hi | lo | dU_s hi | lo]
   int32_t* prefix;                         // [E+1]
   float *G, *U, *Ar, *dA;                  // [R,I] each
   float *y, *dY, *dXs;                     // [R,d] each

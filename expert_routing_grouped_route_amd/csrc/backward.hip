@@ -729,17 +729,40 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   }
 }
 
-// hi = bf16(v), lo = bf16(v - hi), round to nearest even (|v - hi - lo| <=
-// 2^-16 |v|), for a product on the bf16 matrix cores in two parts.
-__global__ __launch_bounds__(256) void split_bf16_kernel(const float* __restrict__ v, int64_t n,
-                                                         uint16_t* __restrict__ hi,
-                                                         uint16_t* __restrict__ lo) {
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const float x = v[i];
-    const uint32_t h = pack_bf16x2_rne(x, 0.f);
-    hi[i] = (uint16_t)h;
-    lo[i] = (uint16_t)pack_bf16x2_rne(x - __uint_as_float(h << 16), 0.f);
+// Row r of v [rows, cols] (fp32) as bf16 parts hi = bf16(v), lo = bf16(v - hi),
+// round to nearest even (|v - hi - lo| <= 2^-16 |v|), inside row r of out
+// (out_ld elements per row): hi at columns hi_col .., lo at lo_col ..; a
+// product on the bf16 matrix cores then takes both parts in one K loop.
+// cols % 4 == 0.  One row per block iteration, 4 elements per lane.
+__global__ __launch_bounds__(256) void split_rows_bf16_kernel(const float* __restrict__ v,
+                                                              int64_t rows, int cols,
+                                                              uint16_t* __restrict__ out,
+                                                              int64_t out_ld, int hi_col,
+                                                              int lo_col) {
+  const int c4 = cols / 4;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(v + r * cols);
+    uint16_t* o = out + r * out_ld;
+    for (int c = threadIdx.x; c < c4; c += 256) {
+      const f32x4 x = src[c];
+      uint32_t h[2], l[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        h[j] = pack_bf16x2_rne(x[2 * j], x[2 * j + 1]);
+        l[j] = pack_bf16x2_rne(x[2 * j] - __uint_as_float(h[j] << 16),
+                               x[2 * j + 1] - __uint_as_float(h[j] & 0xffff0000u));
+      }
+      *reinterpret_cast<uint2*>(o + hi_col + 4 * c) = make_uint2(h[0], h[1]);
+      *reinterpret_cast<uint2*>(o + lo_col + 4 * c) = make_uint2(l[0], l[1]);
+    }
   }
+}
+
+void launch_split_rows(const float* v, int64_t rows, int cols, uint16_t* out, int64_t out_ld,
+                       int hi_col, int lo_col, hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(split_rows_bf16_kernel, dim3((unsigned)std::min<int64_t>(rows, 16384)),
+                     dim3(256), 0, s, v, rows, cols, out, out_ld, hi_col, lo_col);
 }
 
 // Padded part of each expert along the reduction index of a weight-gradient
@@ -965,24 +988,25 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     fd.bf16 = true;
     fd.part = kRoutedTiles;
   }
-  auto down_parts = [&](const uint16_t* hi, const uint16_t* lo, const void* wT, int K, int N,
-                        float* out, bool acc) {
+  // out = sum over the `parts` K blocks of A's rows (K columns each) of block
+  // b times weight block b / 2 (w_part elements apart): one launch of the
+  // down kernel, which reduces over its I and writes d columns
+  auto down_parts = [&](const uint16_t* A, int parts, const void* wT, int64_t w_part, int K,
+                        int N, float* out) {
     fd.wd = wT;
-    fd.I = K;  // the down kernel reduces over its I and writes d columns
+    fd.I = K;
     fd.d = N;
     fd.y = out;
-    fd.a = const_cast<uint16_t*>(hi);
-    launch_down_routed_bf16(fd, acc, s);
-    fd.a = const_cast<uint16_t*>(lo);
-    launch_down_routed_bf16(fd, true, s);
+    fd.a = const_cast<uint16_t*>(A);
+    fd.a_parts = parts;
+    fd.w_part = w_part;
+    launch_down_routed_bf16(fd, false, s);
   };
 
   // dA = dY W_d[e]; dW_d[e] = dY_e^T A_e
   if (bf) {
-    const int64_t nRd = R * d;
-    hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nRd)), dim3(256), 0, s, a.dY, nRd, a.dYh,
-                       a.dYl);
-    down_parts(a.dYh, a.dYl, a.wdT, d, I, a.dA, false);
+    launch_split_rows(a.dY, R, d, a.dYp, 2 * (int64_t)d, 0, d, s);
+    down_parts(a.dYp, 2, a.wdT, 0, d, I, a.dA);
   } else {
     ragged_m(a.dY, false, d, a.wd, bf, I, 1, (int64_t)d * I, a.dA, I, I, d, false);
   }
@@ -1013,12 +1037,9 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     ragged_k(a.U, false, I, a.xs, bf, d, a.dw_up, d, (int64_t)I * d, I, d);
   }
   if (bf) {
-    hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, nRI, a.dGh,
-                       a.dGl);
-    hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.U, nRI, a.dUh,
-                       a.dUl);
-    down_parts(a.dGh, a.dGl, a.wgT, I, d, a.dXs, false);
-    down_parts(a.dUh, a.dUl, a.wuT, I, d, a.dXs, true);
+    launch_split_rows(a.G, R, I, a.dGU, 4 * (int64_t)I, 0, I, s);
+    launch_split_rows(a.U, R, I, a.dGU, 4 * (int64_t)I, 2 * I, 3 * I, s);
+    down_parts(a.dGU, 4, a.wgT, (int64_t)(a.wuT - a.wgT), I, d, a.dXs);
   } else {
     ragged_m(a.G, false, I, a.wg, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, false);
     ragged_m(a.U, false, I, a.wu, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, true);
@@ -1082,16 +1103,16 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     // dx_shared = [dG_0 | dG_1 | ..] [W_sg[0]; W_sg[1]; ..] + the same for U,
     // with the weights transposed and dout, dG, dU as bf16 hi and lo rows.
     FfnArgs f1 = {};
-    auto down1 = [&](const uint16_t* hi_, const uint16_t* lo_, const uint16_t* wT, int K, int N,
-                     float* out, bool acc) {
+    auto down1 = [&](const uint16_t* A, int parts, const uint16_t* wT, int64_t w_part, int K,
+                     int N, float* out) {
       f1.wd = wT;
       f1.I = K;
       f1.d = N;
       f1.y = out;
-      f1.a = const_cast<uint16_t*>(hi_);
-      launch_down_routed_bf16(f1, acc, s);
-      f1.a = const_cast<uint16_t*>(lo_);
-      launch_down_routed_bf16(f1, true, s);
+      f1.a = const_cast<uint16_t*>(A);
+      f1.a_parts = parts;
+      f1.w_part = w_part;
+      launch_down_routed_bf16(f1, false, s);
     };
     if (bf) {
       hipLaunchKernelGGL(single_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.off1,
@@ -1108,10 +1129,8 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       launch_transpose_bf16(a.wsd, ns, d, Is, a.wsdT, s);        // [ns*Is, d]
       launch_transpose_bf16(a.wsg, 1, (int)ld, d, a.wsgT, s);    // [d, ns*Is]
       launch_transpose_bf16(a.wsu, 1, (int)ld, d, a.wsuT, s);
-      const int64_t nTd = T * d;
-      hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nTd)), dim3(256), 0, s, a.dout, nTd,
-                         a.dOh, a.dOl);
-      down1(a.dOh, a.dOl, a.wsdT, d, (int)ld, a.dAs, false);
+      launch_split_rows(a.dout, T, d, a.dOp, 2 * (int64_t)d, 0, d, s);
+      down1(a.dOp, 2, a.wsdT, 0, d, (int)ld, a.dAs);
     } else {
       for (int sh = 0; sh < ns; ++sh)
         uni_m(a.dout, false, d, wslice(a.wsd, sh), bf, Is, 1, a.dAs + (size_t)sh * Is, ld, Is, d,
@@ -1164,12 +1183,9 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       }
     }
     if (bf) {
-      hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, nT, a.sGh,
-                         a.sGl);
-      hipLaunchKernelGGL(split_bf16_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Us, nT, a.sUh,
-                         a.sUl);
-      down1(a.sGh, a.sGl, a.wsgT, (int)ld, d, a.dxs, false);
-      down1(a.sUh, a.sUl, a.wsuT, (int)ld, d, a.dxs, true);
+      launch_split_rows(a.Gs, T, (int)ld, a.sGU, 4 * ld, 0, (int)ld, s);
+      launch_split_rows(a.Us, T, (int)ld, a.sGU, 4 * ld, 2 * (int)ld, 3 * (int)ld, s);
+      down1(a.sGU, 4, a.wsgT, (int64_t)(a.wsuT - a.wsgT), (int)ld, d, a.dxs);
     } else {
       for (int sh = 0; sh < ns; ++sh) {
         const size_t cs = (size_t)sh * Is;

@@ -113,8 +113,9 @@ struct BTile {
   int wrows;              // valid weight rows of each half (gate/up) or of the tile (down)
   size_t w_ld;            // bytes between weight rows
   int nk;                 // K-steps
-  int kps;                // shared down tiles: K-steps per shared expert (0: one segment)
-  size_t w_seg;           // bytes between shared experts' weight blocks
+  int kps;                // K-steps per weight block (0: one block; shared down tiles: per expert)
+  int kpw;                // with kps: K-steps between moves to the next weight block
+  size_t w_seg;           // bytes between weight blocks
   uint8_t* Out;           // element (0, 0) of the tile
   size_t out_ld;          // elements between output rows
   int out_cols;           // valid output columns (a multiple of 64)
@@ -166,6 +167,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
   t.w_ld = (size_t)p.d * 2;
   t.nk = p.d / BK;
   t.kps = 0;
+  t.kpw = 1;
   t.w_seg = 0;
   t.out_cols = t.wrows;
 }
@@ -179,13 +181,15 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     routed_decode(p, g, L, e, m, n);
     r0 = p.offsets[e] + m * kBM;
     t.rows = min(kBM, p.offsets[e + 1] - r0);
-    t.X = static_cast<const uint8_t*>(p.a) + (size_t)r0 * p.I * 2;
-    t.x_ld = (size_t)p.I * 2;
+    const int parts = p.a_parts > 1 ? p.a_parts : 1;  // blocks of I columns per A row
+    t.X = static_cast<const uint8_t*>(p.a) + (size_t)r0 * parts * p.I * 2;
+    t.x_ld = (size_t)parts * p.I * 2;
     w0 = static_cast<const uint8_t*>(p.wd) + ((size_t)e * p.d + (size_t)n * BN) * p.I * 2;
     t.w_ld = (size_t)p.I * 2;
-    t.nk = p.I / BK;
-    t.kps = 0;
-    t.w_seg = 0;
+    t.nk = parts * (p.I / BK);
+    t.kps = parts > 1 ? p.I / BK : 0;
+    t.kpw = 2 * (p.I / BK);
+    t.w_seg = parts > 1 ? (size_t)p.w_part * 2 : 0;
     t.Out = reinterpret_cast<uint8_t*>(p.y + (size_t)r0 * p.d + (size_t)n * BN);
   } else {
     const int sb = L - n_routed;
@@ -200,6 +204,7 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     t.w_ld = (size_t)p.Is * 2;
     t.nk = (int)(ld / BK);
     t.kps = p.Is / BK;
+    t.kpw = t.kps;
     t.w_seg = (size_t)p.d * p.Is * 2;
     t.Out = reinterpret_cast<uint8_t*>(p.ysh + (size_t)r0 * p.d + (size_t)n * BN);
   }
@@ -254,7 +259,7 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   // weight byte offset of K-step kt (the shared down tiles' K runs over the
   // shared experts' blocks one after the other)
   auto w_step = [&](int kt) -> size_t {
-    return t.kps ? (size_t)(kt / t.kps) * t.w_seg + (size_t)(kt % t.kps) * ROW_BYTES
+    return t.kps ? (size_t)(kt / t.kpw) * t.w_seg + (size_t)(kt % t.kps) * ROW_BYTES
                  : (size_t)kt * ROW_BYTES;
   };
   // direct loads of K-step kt: X load q (0..XLOADS-1), weight load q (0..WLOADS-1)
@@ -581,6 +586,7 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_bf16_kernel(SegGemmArgs p) 
   t.w_ld = (size_t)p.ld * 2;
   t.nk = nk;
   t.kps = 0;
+  t.kpw = 1;
   t.w_seg = 0;
   t.Out = reinterpret_cast<uint8_t*>(out);
   t.out_ld = p.N;
@@ -640,7 +646,12 @@ bool buffer_offsets_fit(const FfnArgs& a) {
   const uint64_t lim = 1ull << 32;
   const uint64_t w = (uint64_t)std::max(std::max(a.d, a.I), a.ns * a.Is);
   const uint64_t tile = 514 * w;  // a tile's rows plus the K offset, with margin
-  return (uint64_t)a.T * a.d * 2 + tile < lim && (uint64_t)a.ns * a.d * a.Is * 2 + tile < lim;
+  // A rows of a_parts blocks (their K offsets), and the weight blocks they step through
+  const uint64_t parts = a.a_parts > 1 ? (uint64_t)a.a_parts : 1;
+  const uint64_t xrows = 258 * parts * (uint64_t)a.I * 2;
+  const uint64_t wpart = parts > 1 ? (uint64_t)a.w_part * 2 * (parts / 2) : 0;
+  return (uint64_t)a.T * a.d * 2 + tile < lim && (uint64_t)a.ns * a.d * a.Is * 2 + tile < lim &&
+         xrows < lim && wpart + tile < lim;
 }
 
 void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream) {

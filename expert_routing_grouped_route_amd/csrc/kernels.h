@@ -86,6 +86,12 @@ struct FfnArgs {
   bool bf16;
   int part;               // tiles launched: 0 all, 1 routed experts only, 2 shared experts only
   float* u_raw;           // launch_gate_up_raw_bf16: [R,I] fp32 U (G goes to `a`, fp32)
+  // launch_down_routed_bf16 only: with a_parts > 1 each row of `a` holds
+  // a_parts blocks of I columns, and block b is multiplied by weight block
+  // b / 2, which starts w_part elements after block 0 per block index (the
+  // bf16 hi and lo parts of an fp32 operand against one weight, and so on).
+  int a_parts;
+  int64_t w_part;
 };
 constexpr int kAllTiles = 0, kRoutedTiles = 1, kSharedTiles = 2;
 void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream);

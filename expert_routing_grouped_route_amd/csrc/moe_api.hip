@@ -296,8 +296,8 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // forward layout, then the backward scratch.
 struct BLayout {
   size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, rpart, Gs, Us, As, Asbf, dAs, dxs,
-      wdT, wgT, wuT, dYh, dYl, dGh, dGl, dUh, dUl, poff, tA, tB, off1, poff1, tiles1, wsdT,
-      wsgT, wsuT, dOh, dOl, sGh, sGl, sUh, sUl, poffS, kpart, total;
+      wdT, wgT, wuT, dYp, dGU, poff, tA, tB, off1, poff1, tiles1, wsdT,
+      wsgT, wsuT, dOp, sGU, poffS, kpart, total;
   int64_t seg_ld;
   int ksplit;
 };
@@ -337,12 +337,8 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.wdT = take(wsz);
   B.wgT = take(wsz);
   B.wuT = take(wsz);
-  B.dYh = take(bf ? R * d * 2 : 0);
-  B.dYl = take(bf ? R * d * 2 : 0);
-  B.dGh = take(bf ? R * I * 2 : 0);
-  B.dGl = take(bf ? R * I * 2 : 0);
-  B.dUh = take(bf ? R * I * 2 : 0);
-  B.dUl = take(bf ? R * I * 2 : 0);
+  B.dYp = take(bf ? R * d * 4 : 0);
+  B.dGU = take(bf ? R * I * 8 : 0);
   // weight-gradient operands: per expert 2 * roundup(n_e, 64) columns
   B.seg_ld = ((int64_t)(2 * (R + 63 * (size_t)D.E)) + 63) / 64 * 64;
   const size_t rows = std::max(std::max(d, I), (size_t)D.n_shared * Is);
@@ -355,12 +351,8 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.wsdT = take(bsh ? nsI * d * 2 : 0);
   B.wsgT = take(bsh ? nsI * d * 2 : 0);
   B.wsuT = take(bsh ? nsI * d * 2 : 0);
-  B.dOh = take(bsh ? T * d * 2 : 0);
-  B.dOl = take(bsh ? T * d * 2 : 0);
-  B.sGh = take(bsh ? T * nsI * 2 : 0);
-  B.sGl = take(bsh ? T * nsI * 2 : 0);
-  B.sUh = take(bsh ? T * nsI * 2 : 0);
-  B.sUl = take(bsh ? T * nsI * 2 : 0);
+  B.dOp = take(bsh ? T * d * 4 : 0);
+  B.sGU = take(bsh ? T * nsI * 8 : 0);
   B.ksplit = bsh ? shared_k_split((int64_t)T, (int)d, (int)Is) : 1;
   B.poffS = take(bsh ? ((size_t)B.ksplit + 1) * 4 : 0);
   B.kpart = take(bsh && B.ksplit > 1 ? (size_t)B.ksplit * d * Is * 4 : 0);
@@ -464,12 +456,8 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
     ba.wdT = at<uint16_t>(ws, B.wdT);
     ba.wgT = at<uint16_t>(ws, B.wgT);
     ba.wuT = at<uint16_t>(ws, B.wuT);
-    ba.dYh = at<uint16_t>(ws, B.dYh);
-    ba.dYl = at<uint16_t>(ws, B.dYl);
-    ba.dGh = at<uint16_t>(ws, B.dGh);
-    ba.dGl = at<uint16_t>(ws, B.dGl);
-    ba.dUh = at<uint16_t>(ws, B.dUh);
-    ba.dUl = at<uint16_t>(ws, B.dUl);
+    ba.dYp = at<uint16_t>(ws, B.dYp);
+    ba.dGU = at<uint16_t>(ws, B.dGU);
     ba.poff = at<int32_t>(ws, B.poff);
     ba.seg_ld = B.seg_ld;
     ba.tA = at<uint16_t>(ws, B.tA);
@@ -481,12 +469,8 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
       ba.wsdT = at<uint16_t>(ws, B.wsdT);
       ba.wsgT = at<uint16_t>(ws, B.wsgT);
       ba.wsuT = at<uint16_t>(ws, B.wsuT);
-      ba.dOh = at<uint16_t>(ws, B.dOh);
-      ba.dOl = at<uint16_t>(ws, B.dOl);
-      ba.sGh = at<uint16_t>(ws, B.sGh);
-      ba.sGl = at<uint16_t>(ws, B.sGl);
-      ba.sUh = at<uint16_t>(ws, B.sUh);
-      ba.sUl = at<uint16_t>(ws, B.sUl);
+      ba.dOp = at<uint16_t>(ws, B.dOp);
+      ba.sGU = at<uint16_t>(ws, B.sGU);
     }
   }
   ba.prefix = at<int32_t>(ws, B.prefix);
