@@ -113,8 +113,8 @@ struct BTile {
   int wrows;              // valid weight rows of each half (gate/up) or of the tile (down)
   size_t w_ld;            // bytes between weight rows
   int nk;                 // K-steps
-  int kps;                // K-steps per weight block (0: one block; shared down tiles: per expert)
-  int kpw;                // with kps: K-steps between moves to the next weight block
+  int kps;                // K-steps per K block (0: one block; shared down tiles: per expert)
+  int wsh;                // PARTS tiles: 2^wsh K blocks share one weight block
   size_t w_seg;           // bytes between weight blocks
   uint8_t* Out;           // element (0, 0) of the tile
   size_t out_ld;          // elements between output rows
@@ -167,11 +167,12 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
   t.w_ld = (size_t)p.d * 2;
   t.nk = p.d / BK;
   t.kps = 0;
-  t.kpw = 1;
   t.w_seg = 0;
   t.out_cols = t.wrows;
 }
 
+// PARTS: the routed rows of `a` may hold a_parts K blocks (FfnArgs::a_parts).
+template <bool PARTS = false>
 __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, int L, int n_routed,
                                           BTile& t) {
   int n, r0;
@@ -181,14 +182,14 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     routed_decode(p, g, L, e, m, n);
     r0 = p.offsets[e] + m * kBM;
     t.rows = min(kBM, p.offsets[e + 1] - r0);
-    const int parts = p.a_parts > 1 ? p.a_parts : 1;  // blocks of I columns per A row
+    const int parts = PARTS && p.a_parts > 1 ? p.a_parts : 1;  // blocks of I columns per A row
     t.X = static_cast<const uint8_t*>(p.a) + (size_t)r0 * parts * p.I * 2;
     t.x_ld = (size_t)parts * p.I * 2;
     w0 = static_cast<const uint8_t*>(p.wd) + ((size_t)e * p.d + (size_t)n * BN) * p.I * 2;
     t.w_ld = (size_t)p.I * 2;
     t.nk = parts * (p.I / BK);
     t.kps = parts > 1 ? p.I / BK : 0;
-    t.kpw = 2 * (p.I / BK);
+    if (PARTS) t.wsh = 1;  // the hi and lo blocks of one operand share a weight
     t.w_seg = parts > 1 ? (size_t)p.w_part * 2 : 0;
     t.Out = reinterpret_cast<uint8_t*>(p.y + (size_t)r0 * p.d + (size_t)n * BN);
   } else {
@@ -204,7 +205,7 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     t.w_ld = (size_t)p.Is * 2;
     t.nk = (int)(ld / BK);
     t.kps = p.Is / BK;
-    t.kpw = t.kps;
+    if (PARTS) t.wsh = 0;
     t.w_seg = (size_t)p.d * p.Is * 2;
     t.Out = reinterpret_cast<uint8_t*>(p.ysh + (size_t)r0 * p.d + (size_t)n * BN);
   }
@@ -222,7 +223,7 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
 // 32 bits.
 // RAW (gate/up): store G and U as fp32 instead of the SwiGLU product.
 // ACC (down): add the product to the output instead of storing it.
-template <bool GATE_UP, bool BUF, bool RAW = false, bool ACC = false>
+template <bool GATE_UP, bool BUF, bool RAW = false, bool ACC = false, bool PARTS = false>
 __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g_raw = nullptr,
                                          float* u_raw = nullptr) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -259,7 +260,8 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   // weight byte offset of K-step kt (the shared down tiles' K runs over the
   // shared experts' blocks one after the other)
   auto w_step = [&](int kt) -> size_t {
-    return t.kps ? (size_t)(kt / t.kpw) * t.w_seg + (size_t)(kt % t.kps) * ROW_BYTES
+    return t.kps ? (size_t)(PARTS ? (kt / t.kps) >> t.wsh : kt / t.kps) * t.w_seg +
+                       (size_t)(kt % t.kps) * ROW_BYTES
                  : (size_t)kt * ROW_BYTES;
   };
   // direct loads of K-step kt: X load q (0..XLOADS-1), weight load q (0..WLOADS-1)
@@ -551,8 +553,8 @@ __global__ __launch_bounds__(NTHREADS) void down_routed_bf16_kernel(FfnArgs p, G
   const int L = xcd_remap(blockIdx.x);
   if (L >= n_routed) return;
   BTile t;
-  down_tile(p, g, L, n_routed, t);
-  run_tile<false, BUF, false, ACC>(t, smem);
+  down_tile<true>(p, g, L, n_routed, t);
+  run_tile<false, BUF, false, ACC, true>(t, smem);
 }
 
 // Weight-gradient tiles: expert e, 256-row m-tile, 256-column n-tile; K runs
@@ -586,7 +588,6 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_bf16_kernel(SegGemmArgs p) 
   t.w_ld = (size_t)p.ld * 2;
   t.nk = nk;
   t.kps = 0;
-  t.kpw = 1;
   t.w_seg = 0;
   t.Out = reinterpret_cast<uint8_t*>(out);
   t.out_ld = p.N;
