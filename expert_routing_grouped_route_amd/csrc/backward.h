@@ -34,8 +34,9 @@ struct BwdArgs {
   uint16_t *tA, *tB;                       // bf16: [max(d, I, ns*Is), seg_ld] transposed operands
   int32_t *off1, *poff1;                   // bf16: [2] each, the T rows as one segment
   int32_t* tiles1;                         // bf16: M-tile table of that one segment
+  int32_t *off2, *tiles2;                  // bf16, shared: {0, T, 2T} and its M-tile table
   uint16_t *wsdT, *wsgT, *wsuT;            // bf16: [ns*Is, d], [d, ns*Is], [d, ns*Is]
-                                           // (wsuT after wsgT in the same allocation)
+                                           // (wsuT = wsgT + d*ns*Is, read as one [2, d, ns*Is])
   uint16_t* dOp;                           // bf16: [T, 2d] rows of dout as [hi | lo] parts
   uint16_t* sGU;                           // bf16: [T, 4*ns*Is] rows [dG_s hi | lo | dU_s hi | lo]
   int32_t* prefix;                         // [E+1]
@@ -48,7 +49,7 @@ struct BwdArgs {
   int ksplit;                              // bf16, shared: shared_k_split(T, d, Is)
   float *Gs, *Us, *As, *dAs;               // [T, ns*Is] each (all shared experts)
   uint16_t* Asbf;                          // bf16: [T, ns*Is] the shared SwiGLU products in bf16
-  float* dxs;                              // [T,d]
+  float* dxs;                              // [T,d]; bf16: [2T,d], the dG and the dU terms
   int64_t T;
   int d, E, k, I, ns, Is;
   bool bf16;

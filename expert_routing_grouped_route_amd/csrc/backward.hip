@@ -484,8 +484,9 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(float* __restrict__ G,
   }
 }
 
-// dx[t] = sum_j dXs[inv[t*k+j]] + sum_j dl[t*k+j] W_r[ids[t*k+j]] (+ dxs[t]),
-// slot order, then the router term, then the shared experts' term.  One wave
+// dx[t] = sum_j dXs[inv[t*k+j]] + sum_j dl[t*k+j] W_r[ids[t*k+j]] (+ the
+// shared experts' term: dxs[t], then dxs[T + t] with two slabs), slot order,
+// then the router term, then the shared term.  One wave
 // per token, four consecutive columns per lane and step.
 template <bool WR_BF16>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dXs,
@@ -493,8 +494,9 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
                                                      const int32_t* __restrict__ ids,
                                                      const float* __restrict__ dl,
                                                      const void* __restrict__ wr,
-                                                     const float* __restrict__ dxs, int T, int k,
-                                                     int d, float* __restrict__ dx) {
+                                                     const float* __restrict__ dxs, int slabs,
+                                                     int T, int k, int d,
+                                                     float* __restrict__ dx) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
@@ -549,8 +551,8 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
         acc[3] = fmaf(g[j], w[3], acc[3]);
       }
     }
-    if (dxs) {
-      const f32x4 v = reinterpret_cast<const f32x4*>(dxs + (size_t)t * d)[c];
+    for (int sl = 0; dxs && sl < slabs; ++sl) {
+      const f32x4 v = reinterpret_cast<const f32x4*>(dxs + ((size_t)sl * T + t) * d)[c];
       acc[0] += v[0];
       acc[1] += v[1];
       acc[2] += v[2];
@@ -787,6 +789,14 @@ __global__ __launch_bounds__(64) void single_seg_offsets_kernel(int T, int32_t* 
   off[1] = T;
   poff[0] = 0;
   poff[1] = 2 * ((T + 63) / 64 * 64);
+}
+
+// Two row groups of T rows each: off = {0, T, 2T}.
+__global__ __launch_bounds__(64) void two_seg_offsets_kernel(int T, int32_t* __restrict__ off) {
+  if (threadIdx.x != 0) return;
+  off[0] = 0;
+  off[1] = T;
+  off[2] = 2 * T;
 }
 
 // S slices of one segment's reduction index, 2 * roundup(T, 64) columns:
@@ -1183,9 +1193,20 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       }
     }
     if (bf) {
-      launch_split_rows(a.Gs, T, (int)ld, a.sGU, 4 * ld, 0, (int)ld, s);
-      launch_split_rows(a.Us, T, (int)ld, a.sGU, 4 * ld, 2 * (int)ld, 3 * (int)ld, s);
-      down1(a.sGU, 4, a.wsgT, (int64_t)(a.wsuT - a.wsgT), (int)ld, d, a.dxs);
+      // dxs = dG_s W_sg + dU_s W_su as two row groups of one launch (256
+      // tiles rather than 128 for T = 4096): rows 0..T-1 of sGU hold
+      // [dG_s hi | lo] against W_sg^T, rows T..2T-1 [dU_s hi | lo] against
+      // W_su^T (the group-1 weight, d*ld elements after W_sg^T); their
+      // products go to the two slabs of dxs, added in bwd_dx_kernel
+      launch_split_rows(a.Gs, T, (int)ld, a.sGU, 2 * ld, 0, (int)ld, s);
+      launch_split_rows(a.Us, T, (int)ld, a.sGU + (size_t)T * 2 * ld, 2 * ld, 0, (int)ld, s);
+      hipLaunchKernelGGL(two_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.off2);
+      launch_tile_table(a.off2, 2, a.tiles2, a.ctr, s);
+      f1.offsets = a.off2;
+      f1.tile_off = a.tiles2;
+      f1.R = 2 * T;
+      f1.E = 2;
+      down1(a.sGU, 2, a.wsgT, 0, (int)ld, d, a.dxs);
     } else {
       for (int sh = 0; sh < ns; ++sh) {
         const size_t cs = (size_t)sh * Is;
@@ -1209,7 +1230,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
                        a.dbias);
   hipLaunchKernelGGL((bf ? bwd_dx_kernel<true> : bwd_dx_kernel<false>),
                      dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, a.dXs, a.inv, a.ids, a.dl,
-                     a.wr, a.ns ? a.dxs : nullptr, (int)T, a.k, d, a.dx);
+                     a.wr, a.ns ? a.dxs : nullptr, bf ? 2 : 1, (int)T, a.k, d, a.dx);
 }
 
 }  // namespace moe

@@ -296,7 +296,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // forward layout, then the backward scratch.
 struct BLayout {
   size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, rpart, Gs, Us, As, Asbf, dAs, dxs,
-      wdT, wgT, wuT, dYp, dGU, poff, tA, tB, off1, poff1, tiles1, wsdT,
+      wdT, wgT, wuT, dYp, dGU, poff, tA, tB, off1, poff1, tiles1, off2, tiles2, wsdT,
       wsgT, wsuT, dOp, sGU, poffS, kpart, total;
   int64_t seg_ld;
   int ksplit;
@@ -331,7 +331,7 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.As = take(ts * 4);
   B.Asbf = take(D.dtype == MOE_BF16 ? ts * 2 : 0);
   B.dAs = take(ts * 4);
-  B.dxs = take(D.n_shared ? T * d * 4 : 0);
+  B.dxs = take(D.n_shared ? (D.dtype == MOE_BF16 ? 2 : 1) * T * d * 4 : 0);
   const bool bf = D.dtype == MOE_BF16;
   const size_t wsz = bf ? (size_t)D.E * I * d * 2 : 0;
   B.wdT = take(wsz);
@@ -348,9 +348,11 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   const bool bsh = bf && D.n_shared > 0;
   const size_t nsI = (size_t)D.n_shared * Is;
   B.tiles1 = take(bsh ? (size_t)tile_table_ints((int64_t)T, 1) * 4 : 0);
+  B.off2 = take(bsh ? 12 : 0);
+  B.tiles2 = take(bsh ? (size_t)tile_table_ints(2 * (int64_t)T, 2) * 4 : 0);
   B.wsdT = take(bsh ? nsI * d * 2 : 0);
-  B.wsgT = take(bsh ? nsI * d * 2 : 0);
-  B.wsuT = take(bsh ? nsI * d * 2 : 0);
+  B.wsgT = take(bsh ? 2 * nsI * d * 2 : 0);  // W_sg^T then W_su^T, one after the other
+  B.wsuT = B.wsgT + nsI * d * 2;
   B.dOp = take(bsh ? T * d * 4 : 0);
   B.sGU = take(bsh ? T * nsI * 8 : 0);
   B.ksplit = bsh ? shared_k_split((int64_t)T, (int)d, (int)Is) : 1;
@@ -466,6 +468,8 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
     ba.poff1 = at<int32_t>(ws, B.poff1);
     if (sh) {
       ba.tiles1 = at<int32_t>(ws, B.tiles1);
+    ba.off2 = at<int32_t>(ws, B.off2);
+    ba.tiles2 = at<int32_t>(ws, B.tiles2);
       ba.wsdT = at<uint16_t>(ws, B.wsdT);
       ba.wsgT = at<uint16_t>(ws, B.wsgT);
       ba.wsuT = at<uint16_t>(ws, B.wsuT);

@@ -150,6 +150,27 @@ def test_backward_vector_alu_variant_matches_oracle(name, monkeypatch):
             assert_grad_close(got[n], ref[n], f"{name}.{n} (VALU)")
 
 
+@pytest.mark.parametrize("name", ["bwd_bf16_shared", "bwd_bf16_zipf"])
+def test_backward_global_load_variant(name, monkeypatch):
+    """The GEMM operands through 64-bit global loads instead of buffer loads
+    (the variant taken when a product's offsets exceed 32 bits; forced here
+    through MOE_GEMM_GLOBAL_LOADS=1): the same bar against the oracle, and the
+    same gradients bit for bit as the buffer-load call (same data in LDS, same
+    MFMA order)."""
+    c = get(name)
+    L = c.logits()
+    base = c.backward()
+    monkeypatch.setenv("MOE_GEMM_GLOBAL_LOADS", "1")
+    got = c.backward()
+    monkeypatch.delenv("MOE_GEMM_GLOBAL_LOADS")
+    ref = c.reference(L)
+    for n in GRADS:
+        if ref[n] is None:
+            continue
+        assert_grad_close(got[n], ref[n], f"{name}.{n} (global loads)")
+        assert np.array_equal(got[n], base[n]), n
+
+
 def test_backward_has_empty_experts_in_skewed_case():
     c = get("bwd_bf16_zipf")
     ref = c.reference(c.logits())
