@@ -204,9 +204,10 @@ def backward_flops(cfg):
     """FLOPs of the backward pass.  Algorithmic: the gradient products of the
     experts (dA, dW_down, dW_gate and dW_up, dx: 12 d I per routed row and
     12 d n_s I_s per token); executed adds the recomputed forward products
-    (G, U and the expert outputs: 6 d I per row)."""
+    G and U (4 d I per row).  The hi/lo parts of fp32 operands are not
+    counted."""
     rows = cfg.T * cfg.k * cfg.d * cfg.I + cfg.T * cfg.d * cfg.n_shared * cfg.I_shared
-    return 12 * rows, 18 * rows
+    return 12 * rows, 16 * rows
 
 
 def time_backward(cfg, dev, d, wdt, stream, warm=2, timed=5):

@@ -40,8 +40,8 @@ struct BwdArgs {
   uint16_t* dOp;                           // bf16: [T, 2d] rows of dout as [hi | lo] parts
   uint16_t* sGU;                           // bf16: [T, 4*ns*Is] rows [dG_s hi | lo | dU_s hi | lo]
   int32_t* prefix;                         // [E+1]
-  float *G, *U, *Ar, *dA;                  // [R,I] each
-  float *y, *dY, *dXs;                     // [R,d] each
+  float *G, *U, *Ar, *dA;                  // [R,I] each (Ar: fp32 layers only; bf16: dA = dout W_d)
+  float *y, *dY, *dXs;                     // [R,d] each (y: fp32 layers only)
   float *dw, *dl, *dls;                    // [R] each (dls: dl in sorted-row order)
   float* rpart;                            // [router_part_rows(R, E), d] router-gradient partials
   int32_t* poffS;                          // bf16, shared: [ksplit+1] slices of the shared K range

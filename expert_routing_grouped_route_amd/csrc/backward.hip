@@ -429,6 +429,85 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const float* __restrict__
   if (lane == 0) dw[a] = s;
 }
 
+// bf16 layers, per sorted row i (assignment a = perm[i], token t = a / k):
+// dY[i] = w[a] * dout[t] (fp32) and dYp[i] = [hi | lo] bf16 parts of the
+// unweighted dout[t] (hi = bf16(v), lo = bf16(v - hi), round to nearest
+// even).  One wave per row, four consecutive columns per lane and step.
+__global__ __launch_bounds__(256) void bwd_rows_split_kernel(const float* __restrict__ dout,
+                                                             const int32_t* __restrict__ perm,
+                                                             const float* __restrict__ w, int R,
+                                                             int k, int d,
+                                                             float* __restrict__ dY,
+                                                             uint16_t* __restrict__ dYp) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave;
+  if (i >= R) return;
+  const int a = perm[i], t = a / k;
+  const float wa = w[a];
+  const f32x4* dr = reinterpret_cast<const f32x4*>(dout + (size_t)t * d);
+  f32x4* o = reinterpret_cast<f32x4*>(dY + (size_t)i * d);
+  uint16_t* p = dYp + (size_t)i * 2 * d;
+  for (int c = lane; c < d / 4; c += 64) {
+    const f32x4 x = dr[c];
+    o[c] = f32x4{wa * x[0], wa * x[1], wa * x[2], wa * x[3]};
+    uint32_t h[2], l[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      h[j] = pack_bf16x2_rne(x[2 * j], x[2 * j + 1]);
+      l[j] = pack_bf16x2_rne(x[2 * j] - __uint_as_float(h[j] << 16),
+                             x[2 * j + 1] - __uint_as_float(h[j] & 0xffff0000u));
+    }
+    *reinterpret_cast<uint2*>(p + 4 * c) = make_uint2(h[0], h[1]);
+    *reinterpret_cast<uint2*>(p + d + 4 * c) = make_uint2(l[0], l[1]);
+  }
+}
+
+// bf16 layers, per sorted row i (a = perm[i]), with dA'[i] = dout[t] W_d[e]
+// (unweighted) in dA and the forward's bf16 SwiGLU row A[i] in Abf:
+//   dw[a] = sum_c A[i][c] dA'[i][c]   (= dout[t] . y[i], y = A W_d^T),
+//   G <- w[a] dA' * U * silu'(G),  U <- w[a] dA' * silu(G)  (in place).
+// One block per row; each lane sums its four-column chunks in order, then a
+// fixed xor tree in the wave and the four waves in order.
+__global__ __launch_bounds__(256) void swiglu_bwd_rows_kernel(float* __restrict__ G,
+                                                              float* __restrict__ U,
+                                                              const float* __restrict__ dA,
+                                                              const uint16_t* __restrict__ Abf,
+                                                              const int32_t* __restrict__ perm,
+                                                              const float* __restrict__ w, int I,
+                                                              float* __restrict__ dw) {
+  __shared__ float part[4];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int a = perm[i];
+  const float wa = w[a];
+  f32x4* g4 = reinterpret_cast<f32x4*>(G + (size_t)i * I);
+  f32x4* u4 = reinterpret_cast<f32x4*>(U + (size_t)i * I);
+  const f32x4* d4 = reinterpret_cast<const f32x4*>(dA + (size_t)i * I);
+  const uint2* a4 = reinterpret_cast<const uint2*>(Abf + (size_t)i * I);
+  float sum = 0.f;
+  for (int c = tid; c < I / 4; c += 256) {
+    const f32x4 g = g4[c], u = u4[c], da = d4[c];
+    const uint2 q = a4[c];
+    const float av[4] = {__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xffff0000u),
+                         __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xffff0000u)};
+    f32x4 og, ou;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sum = fmaf(av[j], da[j], sum);
+      const float sg = 1.0f / (1.0f + __expf(-g[j]));
+      const float dd = wa * da[j];
+      og[j] = dd * u[j] * (sg * (1.0f + g[j] * (1.0f - sg)));
+      ou[j] = dd * (g[j] * sg);
+    }
+    g4[c] = og;
+    u4[c] = ou;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+  if ((tid & 63) == 0) part[tid >> 6] = sum;
+  __syncthreads();
+  if (tid == 0) dw[a] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
 // Logit gradient of each token's kept weights: dL_j = w_j (dw_j - sum w dw),
 // in assignment order (dl) and in sorted-row order (dls[inv[a]] = dl[a]).
 __global__ __launch_bounds__(256) void bwd_gate_kernel(const float* __restrict__ w,
@@ -454,7 +533,7 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const float* __restrict__
 // fp32 values.  For bf16 layers it is formed as the forward's gate/up
 // epilogue forms it (hardware reciprocal, round to nearest even to bf16), so
 // from the same G and U it is the same A bit for bit, and Abf (if given)
-// receives the bf16 bits.
+// receives the bf16 bits.  A may be null (only the bf16 bits are kept).
 __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const float* __restrict__ G,
                                                          const float* __restrict__ U, int64_t n,
                                                          int round_bf16, float* __restrict__ A,
@@ -468,7 +547,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const float* __restrict
     } else {
       a = silu_times(G[i], U[i]);
     }
-    A[i] = a;
+    if (A) A[i] = a;
   }
 }
 
@@ -963,10 +1042,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     f.part = kRoutedTiles;
     launch_gate_up_raw_bf16(f, s);
     hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, nRI, 1,
-                       a.Ar, a.Abf);
-    f.a = a.Abf;
-    f.y = a.y;
-    launch_down_bf16(f, s);
+                       nullptr, a.Abf);
   } else {
     ragged_m(a.xs, bf, d, a.wg, bf, 1, d, (int64_t)I * d, a.G, I, I, d, false);
     ragged_m(a.xs, bf, d, a.wu, bf, 1, d, (int64_t)I * d, a.U, I, I, d, false);
@@ -974,11 +1050,18 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
                        a.Ar, nullptr);
     ragged_m(a.Ar, false, I, a.wd, bf, 1, I, (int64_t)d * I, a.y, d, d, I, false);
   }
-  // dY, dw, the gate's logit gradient
-  hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, a.dout, a.y,
-                     a.perm, a.w, (int)R, a.k, d, a.dY, a.dw);
-  hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, a.w,
-                     a.dw, a.inv, (int)T, a.k, a.dl, a.dls);
+  // dY, dw, the gate's logit gradient.  bf16 layers take dw later, as the
+  // row dot product of A with the unweighted dA' = dout W_d (no expert
+  // outputs y needed), and form here dY and the hi/lo parts of dout's rows.
+  if (bf) {
+    hipLaunchKernelGGL(bwd_rows_split_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s,
+                       a.dout, a.perm, a.w, (int)R, a.k, d, a.dY, a.dYp);
+  } else {
+    hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, a.dout,
+                       a.y, a.perm, a.w, (int)R, a.k, d, a.dY, a.dw);
+    hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, a.w,
+                       a.dw, a.inv, (int)T, a.k, a.dl, a.dls);
+  }
   // bf16 layers run the input-gradient products dA = dY W_d[e] and
   // dX = dG W_g[e] + dU W_u[e] on the forward down kernel: they have its
   // shape once the weights are transposed (W_d^T [I,d], W_g^T and W_u^T
@@ -1013,9 +1096,9 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     launch_down_routed_bf16(fd, false, s);
   };
 
-  // dA = dY W_d[e]; dW_d[e] = dY_e^T A_e
+  // dA = dY W_d[e] (bf16 layers: dA' = dout W_d[e], the gate weight applied
+  // in the SwiGLU backward); dW_d[e] = dY_e^T A_e
   if (bf) {
-    launch_split_rows(a.dY, R, d, a.dYp, 2 * (int64_t)d, 0, d, s);
     down_parts(a.dYp, 2, a.wdT, 0, d, I, a.dA);
   } else {
     ragged_m(a.dY, false, d, a.wd, bf, I, 1, (int64_t)d * I, a.dA, I, I, d, false);
@@ -1033,7 +1116,16 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     ragged_k(a.dY, false, d, a.Ar, false, I, a.dw_down, I, (int64_t)d * I, d, I);
   }
   // dG, dU in place of G, U; dW_g, dW_u; dXs = dG W_g[e] + dU W_u[e]
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, a.dA, nRI);
+  if (bf) {
+    if (R > 0)
+      hipLaunchKernelGGL(swiglu_bwd_rows_kernel, dim3((unsigned)R), dim3(256), 0, s, a.G, a.U,
+                         a.dA, a.Abf, a.perm, a.w, I, a.dw);
+    hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, a.w,
+                       a.dw, a.inv, (int)T, a.k, a.dl, a.dls);
+  } else {
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, a.dA,
+                       nRI);
+  }
   if (bf) {
     launch_seg_transpose(a.xs, false, d, a.offsets, a.poff, E, a.seg_ld, a.tB, s);
     launch_seg_transpose(a.G, true, I, a.offsets, a.poff, E, a.seg_ld, a.tA, s);

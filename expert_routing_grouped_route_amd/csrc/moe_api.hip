@@ -315,10 +315,10 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.prefix = take(((size_t)D.E + 1) * 4);
   B.G = take(R * I * 4);
   B.U = take(R * I * 4);
-  B.Ar = take(R * I * 4);
+  B.Ar = take(D.dtype == MOE_BF16 ? 0 : R * I * 4);  // fp32 layers only
   B.Abf = take(D.dtype == MOE_BF16 ? R * I * 2 : 0);
   B.dA = take(R * I * 4);
-  B.y = take(R * d * 4);
+  B.y = take(D.dtype == MOE_BF16 ? 0 : R * d * 4);   // fp32 layers only
   B.dY = take(R * d * 4);
   B.dXs = take(R * d * 4);
   B.dw = take(R * 4);
