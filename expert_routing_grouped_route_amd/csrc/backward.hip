@@ -465,22 +465,26 @@ __global__ __launch_bounds__(256) void bwd_rows_split_kernel(const float* __rest
 // bf16 layers, per sorted row i (a = perm[i]), with dA'[i] = dout[t] W_d[e]
 // (unweighted) in dA and the forward's bf16 SwiGLU row A[i] in Abf:
 //   dw[a] = sum_c A[i][c] dA'[i][c]   (= dout[t] . y[i], y = A W_d^T),
-//   G <- w[a] dA' * U * silu'(G),  U <- w[a] dA' * silu(G)  (in place).
+//   dG = w[a] dA' * U * silu'(G),  dU = w[a] dA' * silu(G),
+// written as row i of dGU [R, 4I]: [dG hi | dG lo | dU hi | dU lo] (bf16
+// parts, hi = bf16(v), lo = bf16(v - hi), round to nearest even).
 // One block per row; each lane sums its four-column chunks in order, then a
 // fixed xor tree in the wave and the four waves in order.
-__global__ __launch_bounds__(256) void swiglu_bwd_rows_kernel(float* __restrict__ G,
-                                                              float* __restrict__ U,
+__global__ __launch_bounds__(256) void swiglu_bwd_rows_kernel(const float* __restrict__ G,
+                                                              const float* __restrict__ U,
                                                               const float* __restrict__ dA,
                                                               const uint16_t* __restrict__ Abf,
                                                               const int32_t* __restrict__ perm,
                                                               const float* __restrict__ w, int I,
-                                                              float* __restrict__ dw) {
+                                                              float* __restrict__ dw,
+                                                              uint16_t* __restrict__ dGU) {
   __shared__ float part[4];
   const int i = blockIdx.x, tid = threadIdx.x;
   const int a = perm[i];
   const float wa = w[a];
-  f32x4* g4 = reinterpret_cast<f32x4*>(G + (size_t)i * I);
-  f32x4* u4 = reinterpret_cast<f32x4*>(U + (size_t)i * I);
+  const f32x4* g4 = reinterpret_cast<const f32x4*>(G + (size_t)i * I);
+  const f32x4* u4 = reinterpret_cast<const f32x4*>(U + (size_t)i * I);
+  uint16_t* o = dGU + (size_t)i * 4 * I;
   const f32x4* d4 = reinterpret_cast<const f32x4*>(dA + (size_t)i * I);
   const uint2* a4 = reinterpret_cast<const uint2*>(Abf + (size_t)i * I);
   float sum = 0.f;
@@ -498,8 +502,20 @@ __global__ __launch_bounds__(256) void swiglu_bwd_rows_kernel(float* __restrict_
       og[j] = dd * u[j] * (sg * (1.0f + g[j] * (1.0f - sg)));
       ou[j] = dd * (g[j] * sg);
     }
-    g4[c] = og;
-    u4[c] = ou;
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      h[j] = pack_bf16x2_rne(og[2 * j], og[2 * j + 1]);
+      l[j] = pack_bf16x2_rne(og[2 * j] - __uint_as_float(h[j] << 16),
+                             og[2 * j + 1] - __uint_as_float(h[j] & 0xffff0000u));
+      h[2 + j] = pack_bf16x2_rne(ou[2 * j], ou[2 * j + 1]);
+      l[2 + j] = pack_bf16x2_rne(ou[2 * j] - __uint_as_float(h[2 + j] << 16),
+                                 ou[2 * j + 1] - __uint_as_float(h[2 + j] & 0xffff0000u));
+    }
+    *reinterpret_cast<uint2*>(o + 4 * c) = make_uint2(h[0], h[1]);
+    *reinterpret_cast<uint2*>(o + I + 4 * c) = make_uint2(l[0], l[1]);
+    *reinterpret_cast<uint2*>(o + 2 * I + 4 * c) = make_uint2(h[2], h[3]);
+    *reinterpret_cast<uint2*>(o + 3 * I + 4 * c) = make_uint2(l[2], l[3]);
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
@@ -911,6 +927,7 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict
 // (64 destination columns, 64 destination rows); tiles past poff[E] return.
 template <bool F32>
 __global__ __launch_bounds__(256) void seg_transpose_kernel(const void* __restrict__ src, int C,
+                                                            int64_t sld, int part_col,
                                                             const int32_t* __restrict__ off,
                                                             const int32_t* __restrict__ poff, int E,
                                                             int64_t ld, uint16_t* __restrict__ dst) {
@@ -935,7 +952,7 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const void* __restri
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = 0;
     if (ok) {
-      const size_t at = (size_t)(r0 + jj) * C + c0 + cc;
+      const size_t at = (size_t)(r0 + jj) * sld + c0 + cc + (F32 ? 0 : half * part_col);
       if (F32) {
         const f32x4 x0 = reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + at)[0];
         const f32x4 x1 = reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + at)[1];
@@ -971,13 +988,19 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const void* __restri
   }
 }
 
+// sld: elements between source rows (0: C).  part_col (bf16 sources): part h
+// reads the columns h * part_col further on (0: both parts the same values).
 void launch_seg_transpose(const void* src, bool f32, int C, const int32_t* off,
-                          const int32_t* poff, int E, int64_t ld, uint16_t* dst, hipStream_t s) {
+                          const int32_t* poff, int E, int64_t ld, uint16_t* dst, hipStream_t s,
+                          int64_t sld = 0, int part_col = 0) {
   const dim3 grid((unsigned)(ld / 64), (unsigned)((C + 63) / 64));
+  if (sld == 0) sld = C;
   if (f32)
-    hipLaunchKernelGGL(seg_transpose_kernel<true>, grid, dim3(256), 0, s, src, C, off, poff, E, ld, dst);
+    hipLaunchKernelGGL(seg_transpose_kernel<true>, grid, dim3(256), 0, s, src, C, sld, 0, off, poff,
+                       E, ld, dst);
   else
-    hipLaunchKernelGGL(seg_transpose_kernel<false>, grid, dim3(256), 0, s, src, C, off, poff, E, ld, dst);
+    hipLaunchKernelGGL(seg_transpose_kernel<false>, grid, dim3(256), 0, s, src, C, sld, part_col,
+                       off, poff, E, ld, dst);
 }
 
 void launch_transpose_bf16(const void* in, int E, int P, int Q, void* out, hipStream_t s) {
@@ -1115,11 +1138,12 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   } else {
     ragged_k(a.dY, false, d, a.Ar, false, I, a.dw_down, I, (int64_t)d * I, d, I);
   }
-  // dG, dU in place of G, U; dW_g, dW_u; dXs = dG W_g[e] + dU W_u[e]
+  // dG, dU (bf16 layers: as the hi/lo rows of dGU; fp32: in place of G, U);
+  // dW_g, dW_u; dXs = dG W_g[e] + dU W_u[e]
   if (bf) {
     if (R > 0)
       hipLaunchKernelGGL(swiglu_bwd_rows_kernel, dim3((unsigned)R), dim3(256), 0, s, a.G, a.U,
-                         a.dA, a.Abf, a.perm, a.w, I, a.dw);
+                         a.dA, a.Abf, a.perm, a.w, I, a.dw, a.dGU);
     hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, a.w,
                        a.dw, a.inv, (int)T, a.k, a.dl, a.dls);
   } else {
@@ -1128,10 +1152,12 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   }
   if (bf) {
     launch_seg_transpose(a.xs, false, d, a.offsets, a.poff, E, a.seg_ld, a.tB, s);
-    launch_seg_transpose(a.G, true, I, a.offsets, a.poff, E, a.seg_ld, a.tA, s);
+    const int64_t ld4 = 4 * (int64_t)I;  // dGU rows: dG hi, dG lo, dU hi, dU lo
+    launch_seg_transpose(a.dGU, false, I, a.offsets, a.poff, E, a.seg_ld, a.tA, s, ld4, I);
     SegGemmArgs sg = {a.tA, a.tB, a.seg_ld, a.poff, a.dw_gate, E, I, d};
     launch_seg_gemm_bf16(sg, s);
-    launch_seg_transpose(a.U, true, I, a.offsets, a.poff, E, a.seg_ld, a.tA, s);
+    launch_seg_transpose(a.dGU + 2 * (size_t)I, false, I, a.offsets, a.poff, E, a.seg_ld, a.tA, s,
+                         ld4, I);
     sg.out = a.dw_up;
     launch_seg_gemm_bf16(sg, s);
   } else {
@@ -1139,8 +1165,6 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     ragged_k(a.U, false, I, a.xs, bf, d, a.dw_up, d, (int64_t)I * d, I, d);
   }
   if (bf) {
-    launch_split_rows(a.G, R, I, a.dGU, 4 * (int64_t)I, 0, I, s);
-    launch_split_rows(a.U, R, I, a.dGU, 4 * (int64_t)I, 2 * I, 3 * I, s);
     down_parts(a.dGU, 4, a.wgT, (int64_t)(a.wuT - a.wgT), I, d, a.dXs);
   } else {
     ragged_m(a.G, false, I, a.wg, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, false);
