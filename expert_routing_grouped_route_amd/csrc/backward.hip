@@ -1056,6 +1056,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     f.ctr = a.ctr;
     f.a = a.G;
     f.u_raw = a.U;
+    f.a_bf16 = a.Abf;
     f.T = T;
     f.R = R;
     f.d = d;
@@ -1063,9 +1064,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     f.I = I;
     f.bf16 = true;
     f.part = kRoutedTiles;
-    launch_gate_up_raw_bf16(f, s);
-    hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, nRI, 1,
-                       nullptr, a.Abf);
+    launch_gate_up_raw_bf16(f, s);  // G, U and the bf16 A
   } else {
     ragged_m(a.xs, bf, d, a.wg, bf, 1, d, (int64_t)I * d, a.G, I, I, d, false);
     ragged_m(a.xs, bf, d, a.wu, bf, 1, d, (int64_t)I * d, a.U, I, I, d, false);
@@ -1203,6 +1202,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       f.ctr = a.ctr;
       f.a = a.Gs;
       f.u_raw = a.Us;
+      f.a_bf16 = a.Asbf;
       f.T = T;
       f.R = R;
       f.d = d;
@@ -1219,8 +1219,9 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
         uni_m(a.x, bf, d, wslice(a.wsu, sh), bf, 1, d, a.Us + (size_t)sh * Is, ld, Is, d, false);
       }
     }
-    hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, nT,
-                       (int)bf, a.As, bf ? a.Asbf : nullptr);
+    if (!bf)  // bf16 layers have A_s from the gate/up epilogue
+      hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, nT, 0,
+                         a.As, nullptr);
     // dA_s = dout W_sd[s]; dW_sd[s] = dout^T A_s.  bf16 layers take the
     // weight gradients on the forward tile loop with the T rows as one
     // segment (dout and the shared experts' tensors transposed once each),

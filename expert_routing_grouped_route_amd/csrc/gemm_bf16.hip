@@ -221,11 +221,12 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
 // and 32-bit lane offsets), which cost the address path less than 64-bit
 // global addresses; the launcher uses them when every operand offset fits in
 // 32 bits.
-// RAW (gate/up): store G and U as fp32 instead of the SwiGLU product.
+// RAW (gate/up): store G and U as fp32 (and, with a_raw, the SwiGLU product
+// in bf16 at the same element offsets).
 // ACC (down): add the product to the output instead of storing it.
 template <bool GATE_UP, bool BUF, bool RAW = false, bool ACC = false, bool PARTS = false>
 __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g_raw = nullptr,
-                                         float* u_raw = nullptr) {
+                                         float* u_raw = nullptr, uint16_t* a_raw = nullptr) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
 
@@ -430,6 +431,13 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
             f32x4{acc[i][0][4 * q], acc[i][0][4 * q + 1], acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]};
         *reinterpret_cast<f32x4*>(u_raw + o) =
             f32x4{acc[i][1][4 * q], acc[i][1][4 * q + 1], acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]};
+        if (a_raw) {  // and the SwiGLU product as the forward epilogue forms it
+          float h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = silu_times_rcp(acc[i][0][4 * q + r], acc[i][1][4 * q + r]);
+          *reinterpret_cast<uint2*>(a_raw + o) =
+              make_uint2(pack_bf16x2_rne(h[0], h[1]), pack_bf16x2_rne(h[2], h[3]));
+        }
       }
     }
   } else if (GATE_UP) {
@@ -542,7 +550,7 @@ __global__ __launch_bounds__(NTHREADS) void gate_up_raw_bf16_kernel(FfnArgs p, G
   if (L >= n_routed + ns_t) return;
   BTile t;
   gate_up_tile<true>(p, g, L, n_routed, t);
-  run_tile<true, BUF, true>(t, smem, static_cast<float*>(p.a), p.u_raw);
+  run_tile<true, BUF, true>(t, smem, static_cast<float*>(p.a), p.u_raw, p.a_bf16);
 }
 
 // The routed down tiles, storing or (ACC) adding to the output.

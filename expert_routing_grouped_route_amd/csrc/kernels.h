@@ -92,6 +92,9 @@ struct FfnArgs {
   // bf16 hi and lo parts of an fp32 operand against one weight, and so on).
   int a_parts;
   int64_t w_part;
+  // launch_gate_up_raw_bf16 only: also the bf16 SwiGLU product, in the layout
+  // of G and U (or null)
+  uint16_t* a_bf16;
 };
 constexpr int kAllTiles = 0, kRoutedTiles = 1, kSharedTiles = 2;
 void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream);
