@@ -1115,7 +1115,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     fd.a = const_cast<uint16_t*>(A);
     fd.a_parts = parts;
     fd.w_part = w_part;
-    launch_down_routed_bf16(fd, false, s);
+    launch_down_routed_bf16(fd, s);
   };
 
   // dA = dY W_d[e] (bf16 layers: dA' = dout W_d[e], the gate weight applied
@@ -1239,7 +1239,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       f1.a = const_cast<uint16_t*>(A);
       f1.a_parts = parts;
       f1.w_part = w_part;
-      launch_down_routed_bf16(f1, false, s);
+      launch_down_routed_bf16(f1, s);
     };
     if (bf) {
       hipLaunchKernelGGL(single_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.off1,

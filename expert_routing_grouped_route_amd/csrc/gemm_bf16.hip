@@ -223,8 +223,7 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
 // 32 bits.
 // RAW (gate/up): store G and U as fp32 (and, with a_raw, the SwiGLU product
 // in bf16 at the same element offsets).
-// ACC (down): add the product to the output instead of storing it.
-template <bool GATE_UP, bool BUF, bool RAW = false, bool ACC = false, bool PARTS = false>
+template <bool GATE_UP, bool BUF, bool RAW = false, bool PARTS = false>
 __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g_raw = nullptr,
                                          float* u_raw = nullptr, uint16_t* a_raw = nullptr) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -491,12 +490,7 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
         {
           f32x4* o = reinterpret_cast<f32x4*>(out + (size_t)grow * t.out_ld + lane * 4);
           const f32x4 v = *reinterpret_cast<const f32x4*>(sm + row * 256 + ((lane ^ (row & 63)) << 2));
-          if (ACC) {
-            const f32x4 w = *o;
-            *o = f32x4{w[0] + v[0], w[1] + v[1], w[2] + v[2], w[3] + v[3]};
-          } else {
-            *o = v;
-          }
+          *o = v;
         }
       }
       if (h == 0) {
@@ -553,8 +547,8 @@ __global__ __launch_bounds__(NTHREADS) void gate_up_raw_bf16_kernel(FfnArgs p, G
   run_tile<true, BUF, true>(t, smem, static_cast<float*>(p.a), p.u_raw, p.a_bf16);
 }
 
-// The routed down tiles, storing or (ACC) adding to the output.
-template <bool BUF, bool ACC>
+// The routed down tiles alone (PARTS: A rows of several K blocks).
+template <bool BUF>
 __global__ __launch_bounds__(NTHREADS) void down_routed_bf16_kernel(FfnArgs p, GemmGrid g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int n_routed = p.tile_off[p.E] * g.nt_r;
@@ -562,7 +556,7 @@ __global__ __launch_bounds__(NTHREADS) void down_routed_bf16_kernel(FfnArgs p, G
   if (L >= n_routed) return;
   BTile t;
   down_tile<true>(p, g, L, n_routed, t);
-  run_tile<false, BUF, false, ACC, true>(t, smem);
+  run_tile<false, BUF, false, true>(t, smem);
 }
 
 // Weight-gradient tiles: expert e, 256-row m-tile, 256-column n-tile; K runs
@@ -680,13 +674,12 @@ void launch_gate_up_raw_bf16(const FfnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a, g);
 }
 
-void launch_down_routed_bf16(const FfnArgs& a, bool accumulate, hipStream_t stream) {
+void launch_down_routed_bf16(const FfnArgs& a, hipStream_t stream) {
   const GemmGrid g = bf16_down_grid(a);
   const int64_t slots = g.routed ? pad_slots(g.routed) : 0;
   if (slots == 0) return;
   const bool buf = buffer_offsets_fit(a);
-  auto kern = buf ? (accumulate ? down_routed_bf16_kernel<true, true> : down_routed_bf16_kernel<true, false>)
-                  : (accumulate ? down_routed_bf16_kernel<false, true> : down_routed_bf16_kernel<false, false>);
+  auto kern = buf ? down_routed_bf16_kernel<true> : down_routed_bf16_kernel<false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a, g);
 }
 

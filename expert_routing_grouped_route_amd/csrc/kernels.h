@@ -103,9 +103,9 @@ void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream);
 // kRoutedTiles: the routed experts' [R,I]; kSharedTiles: the shared experts'
 // [T, n_s*I_s].
 void launch_gate_up_raw_bf16(const FfnArgs& a, hipStream_t stream);
-// The routed experts' down product Y[rows] (+)= A[rows] W_d[e]^T alone (no
-// shared tiles), storing or, with accumulate, adding to `y`.
-void launch_down_routed_bf16(const FfnArgs& a, bool accumulate, hipStream_t stream);
+// The routed experts' down product Y[rows] = A[rows] W_d[e]^T alone (no
+// shared tiles), stored to `y` (a_parts and w_part apply).
+void launch_down_routed_bf16(const FfnArgs& a, hipStream_t stream);
 
 // Per-expert products reduced over each expert's rows (weight gradients):
 // out[e] [M,N] = sum over k of A(m, k) B(n, k), where A [M, ld] and B [N, ld]

@@ -236,10 +236,15 @@ MOE_API moe_status_t moe_layer_fwd_condensed(const moe_dims_t* dims, const void*
                                      int32_t* perm_out, int32_t* rep_out, void* ws,
                                      size_t ws_bytes, hipStream_t stream);
 
-/* Workspace of moe_layer_bwd: moe_workspace_bytes plus the backward scratch
- * (the sorted token rows, four [T*k, I] and three [T*k, d] fp32 arrays, four
- * [T, n_shared*I_shared] fp32 arrays, and for bf16 layers the SwiGLU
- * products in bf16).  0 for invalid dims. */
+/* Workspace of moe_layer_bwd: moe_workspace_bytes plus the backward scratch:
+ * the sorted token rows; fp32 [T*k, I] and [T*k, d] intermediates (G, U, the
+ * SwiGLU gradient, dY and the sorted rows' input gradients; fp32 layers also
+ * A and the expert outputs); fp32 [T, n_shared*I_shared] intermediates of
+ * the shared experts; and for bf16 layers the transposed weights, the bf16
+ * hi/lo parts of the fp32 operands, the per-expert zero-padded transposed
+ * operands of the weight-gradient products and split-K partial sums.  About
+ * 4.0 GB for 4096 tokens, d = 2048, 64 experts top-6 of I = 1408 and two
+ * shared experts.  0 for invalid dims. */
 MOE_API size_t moe_backward_workspace_bytes(const moe_dims_t* dims);
 
 /* Backward pass of moe_layer_fwd: given the upstream gradient dout = dL/dout
@@ -258,9 +263,13 @@ MOE_API size_t moe_backward_workspace_bytes(const moe_dims_t* dims);
  *   - the bf16 rounding of the SwiGLU product passes the gradient unchanged;
  *     dw_down uses the rounded product the forward pass multiplied.
  * The routing, the dispatch and the expert activations are recomputed from
- * the inputs (nothing is carried over from a forward call).  All gradient
- * arithmetic is fp32 (bf16 inputs widened), each output element summed in a
- * fixed order: two calls give identical bits.
+ * the inputs (nothing is carried over from a forward call).  The products
+ * run on the bf16 matrix cores with fp32 accumulation, each fp32 operand
+ * taken as bf16 parts hi = bf16(v), lo = bf16(v - hi) (|v - hi - lo| <=
+ * 2^-16 |v|); with MOE_BWD_VALU=1 in the environment, fp32 layers run them
+ * on the vector ALUs in fp32 instead.
+ * All other arithmetic is fp32 (bf16 inputs widened), and each output element
+ * is summed in a fixed order: two calls give identical bits.
  *   x, w_router, bias, w_gate, w_up, w_down, wsh_*: as in moe_layer_fwd.
  *   dout: [T,d] fp32, required.
  *   dx [T,d], dw_router [E,d], dw_gate, dw_up [E,I,d], dw_down [E,d,I]:
