@@ -27,7 +27,6 @@ struct BwdArgs {
   uint16_t* Abf;                           // bf16: [R,I] the SwiGLU product in bf16
   uint16_t *wdT, *wgT, *wuT;               // bf16: [E,I,d], [E,d,I], [E,d,I] transposed weights
                                            // (wuT after wgT in the same allocation)
-  uint16_t* dYp;                           // bf16: [R, 2d] rows of dY as [hi | lo] parts
   uint16_t* dGU;                           // bf16: [R, 4I] rows [dG hi | dG lo | dU hi | dU lo]
   int32_t* poff;                           // bf16: [E+1] padded per-expert parts (seg_offsets_kernel)
   int64_t seg_ld;                          // bf16: row length of tA and tB (>= poff[E])
@@ -41,7 +40,7 @@ struct BwdArgs {
   uint16_t* sGU;                           // bf16: [T, 4*ns*Is] rows [dG_s hi | lo | dU_s hi | lo]
   int32_t* prefix;                         // [E+1]
   float *G, *U, *Ar, *dA;                  // [R,I] each (Ar: fp32 layers only; bf16: dA = dout W_d)
-  float *y, *dY, *dXs;                     // [R,d] each (y: fp32 layers only)
+  float *y, *dY, *dXs;                     // [R,d] each (y, dY: fp32 layers only)
   float *dw, *dl, *dls;                    // [R] each (dls: dl in sorted-row order)
   float* rpart;                            // [router_part_rows(R, E), d] router-gradient partials
   int32_t* poffS;                          // bf16, shared: [ksplit+1] slices of the shared K range

@@ -429,39 +429,6 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const float* __restrict__
   if (lane == 0) dw[a] = s;
 }
 
-// bf16 layers, per sorted row i (assignment a = perm[i], token t = a / k):
-// dY[i] = w[a] * dout[t] (fp32) and dYp[i] = [hi | lo] bf16 parts of the
-// unweighted dout[t] (hi = bf16(v), lo = bf16(v - hi), round to nearest
-// even).  One wave per row, four consecutive columns per lane and step.
-__global__ __launch_bounds__(256) void bwd_rows_split_kernel(const float* __restrict__ dout,
-                                                             const int32_t* __restrict__ perm,
-                                                             const float* __restrict__ w, int R,
-                                                             int k, int d,
-                                                             float* __restrict__ dY,
-                                                             uint16_t* __restrict__ dYp) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i = blockIdx.x * 4 + wave;
-  if (i >= R) return;
-  const int a = perm[i], t = a / k;
-  const float wa = w[a];
-  const f32x4* dr = reinterpret_cast<const f32x4*>(dout + (size_t)t * d);
-  f32x4* o = reinterpret_cast<f32x4*>(dY + (size_t)i * d);
-  uint16_t* p = dYp + (size_t)i * 2 * d;
-  for (int c = lane; c < d / 4; c += 64) {
-    const f32x4 x = dr[c];
-    o[c] = f32x4{wa * x[0], wa * x[1], wa * x[2], wa * x[3]};
-    uint32_t h[2], l[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      h[j] = pack_bf16x2_rne(x[2 * j], x[2 * j + 1]);
-      l[j] = pack_bf16x2_rne(x[2 * j] - __uint_as_float(h[j] << 16),
-                             x[2 * j + 1] - __uint_as_float(h[j] & 0xffff0000u));
-    }
-    *reinterpret_cast<uint2*>(p + 4 * c) = make_uint2(h[0], h[1]);
-    *reinterpret_cast<uint2*>(p + d + 4 * c) = make_uint2(l[0], l[1]);
-  }
-}
-
 // bf16 layers, per sorted row i (a = perm[i]), with dA'[i] = dout[t] W_d[e]
 // (unweighted) in dA and the forward's bf16 SwiGLU row A[i] in Abf:
 //   dw[a] = sum_c A[i][c] dA'[i][c]   (= dout[t] . y[i], y = A W_d^T),
@@ -925,9 +892,13 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict
 // F32: part 0 = bf16(v), part 1 = bf16(v - part 0); bf16 source: both parts
 // are v.  64x64 tiles through LDS, 8 elements per lane on each side.  Block
 // (64 destination columns, 64 destination rows); tiles past poff[E] return.
-template <bool F32>
+// GATHER (fp32 sources): sorted row r is g_w[g_perm[r]] times source row
+// g_perm[r] / g_k (the gate-weighted dout rows, formed here instead of stored).
+template <bool F32, bool GATHER = false>
 __global__ __launch_bounds__(256) void seg_transpose_kernel(const void* __restrict__ src, int C,
                                                             int64_t sld, int part_col,
+                                                            const int32_t* __restrict__ g_perm,
+                                                            const float* __restrict__ g_w, int g_k,
                                                             const int32_t* __restrict__ off,
                                                             const int32_t* __restrict__ poff, int E,
                                                             int64_t ld, uint16_t* __restrict__ dst) {
@@ -952,11 +923,22 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const void* __restri
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = 0;
     if (ok) {
-      const size_t at = (size_t)(r0 + jj) * sld + c0 + cc + (F32 ? 0 : half * part_col);
+      int srow = r0 + jj;
+      float scale = 1.f;
+      if (GATHER) {
+        const int a = g_perm[srow];
+        srow = a / g_k;
+        scale = g_w[a];
+      }
+      const size_t at = (size_t)srow * sld + c0 + cc + (F32 ? 0 : half * part_col);
       if (F32) {
         const f32x4 x0 = reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + at)[0];
         const f32x4 x1 = reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + at)[1];
-        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        if (GATHER) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = scale * x[i];
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const uint32_t h = pack_bf16x2_rne(x[i], 0.f);
@@ -996,11 +978,21 @@ void launch_seg_transpose(const void* src, bool f32, int C, const int32_t* off,
   const dim3 grid((unsigned)(ld / 64), (unsigned)((C + 63) / 64));
   if (sld == 0) sld = C;
   if (f32)
-    hipLaunchKernelGGL(seg_transpose_kernel<true>, grid, dim3(256), 0, s, src, C, sld, 0, off, poff,
-                       E, ld, dst);
+    hipLaunchKernelGGL(seg_transpose_kernel<true>, grid, dim3(256), 0, s, src, C, sld, 0, nullptr,
+                       nullptr, 1, off, poff, E, ld, dst);
   else
     hipLaunchKernelGGL(seg_transpose_kernel<false>, grid, dim3(256), 0, s, src, C, sld, part_col,
-                       off, poff, E, ld, dst);
+                       nullptr, nullptr, 1, off, poff, E, ld, dst);
+}
+
+// The same for the gate-weighted rows w[perm[r]] * src[perm[r] / k] of an fp32
+// source [T, C] (split into hi and lo parts).
+void launch_seg_transpose_gather(const float* src, int C, const int32_t* perm, const float* w,
+                                 int k, const int32_t* off, const int32_t* poff, int E, int64_t ld,
+                                 uint16_t* dst, hipStream_t s) {
+  const dim3 grid((unsigned)(ld / 64), (unsigned)((C + 63) / 64));
+  hipLaunchKernelGGL((seg_transpose_kernel<true, true>), grid, dim3(256), 0, s, src, C,
+                     (int64_t)C, 0, perm, w, k, off, poff, E, ld, dst);
 }
 
 void launch_transpose_bf16(const void* in, int E, int P, int Q, void* out, hipStream_t s) {
@@ -1074,10 +1066,10 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   }
   // dY, dw, the gate's logit gradient.  bf16 layers take dw later, as the
   // row dot product of A with the unweighted dA' = dout W_d (no expert
-  // outputs y needed), and form here dY and the hi/lo parts of dout's rows.
+  // outputs y needed); they form no dY but the hi/lo parts of dout's token
+  // rows, which the products gather through perm.
   if (bf) {
-    hipLaunchKernelGGL(bwd_rows_split_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s,
-                       a.dout, a.perm, a.w, (int)R, a.k, d, a.dY, a.dYp);
+    launch_split_rows(a.dout, T, d, a.dOp, 2 * (int64_t)d, 0, d, s);
   } else {
     hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, a.dout,
                        a.y, a.perm, a.w, (int)R, a.k, d, a.dY, a.dw);
@@ -1106,8 +1098,11 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   // out = sum over the `parts` K blocks of A's rows (K columns each) of block
   // b times weight block b / 2 (w_part elements apart): one launch of the
   // down kernel, which reduces over its I and writes d columns
+  // (rows_perm: A holds token rows, sorted row r reading token rows_perm[r] / k)
   auto down_parts = [&](const uint16_t* A, int parts, const void* wT, int64_t w_part, int K,
-                        int N, float* out) {
+                        int N, float* out, const int32_t* rows_perm) {
+    fd.perm = rows_perm;
+    fd.k = a.k;
     fd.wd = wT;
     fd.I = K;
     fd.d = N;
@@ -1121,7 +1116,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   // dA = dY W_d[e] (bf16 layers: dA' = dout W_d[e], the gate weight applied
   // in the SwiGLU backward); dW_d[e] = dY_e^T A_e
   if (bf) {
-    down_parts(a.dYp, 2, a.wdT, 0, d, I, a.dA);
+    down_parts(a.dOp, 2, a.wdT, 0, d, I, a.dA, a.perm);
   } else {
     ragged_m(a.dY, false, d, a.wd, bf, I, 1, (int64_t)d * I, a.dA, I, I, d, false);
   }
@@ -1130,7 +1125,8 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   // bf16 one twice), then one product per weight on the forward tile loop.
   if (bf) {
     hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(64), 0, s, a.offsets, E, a.poff);
-    launch_seg_transpose(a.dY, true, d, a.offsets, a.poff, E, a.seg_ld, a.tA, s);
+    launch_seg_transpose_gather(a.dout, d, a.perm, a.w, a.k, a.offsets, a.poff, E, a.seg_ld,
+                                a.tA, s);
     launch_seg_transpose(a.Abf, false, I, a.offsets, a.poff, E, a.seg_ld, a.tB, s);
     SegGemmArgs sg = {a.tA, a.tB, a.seg_ld, a.poff, a.dw_down, E, d, I};
     launch_seg_gemm_bf16(sg, s);
@@ -1164,7 +1160,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     ragged_k(a.U, false, I, a.xs, bf, d, a.dw_up, d, (int64_t)I * d, I, d);
   }
   if (bf) {
-    down_parts(a.dGU, 4, a.wgT, (int64_t)(a.wuT - a.wgT), I, d, a.dXs);
+    down_parts(a.dGU, 4, a.wgT, (int64_t)(a.wuT - a.wgT), I, d, a.dXs, nullptr);
   } else {
     ragged_m(a.G, false, I, a.wg, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, false);
     ragged_m(a.U, false, I, a.wu, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, true);
@@ -1256,8 +1252,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       launch_transpose_bf16(a.wsd, ns, d, Is, a.wsdT, s);        // [ns*Is, d]
       launch_transpose_bf16(a.wsg, 1, (int)ld, d, a.wsgT, s);    // [d, ns*Is]
       launch_transpose_bf16(a.wsu, 1, (int)ld, d, a.wsuT, s);
-      launch_split_rows(a.dout, T, d, a.dOp, 2 * (int64_t)d, 0, d, s);
-      down1(a.dOp, 2, a.wsdT, 0, d, (int)ld, a.dAs);
+      down1(a.dOp, 2, a.wsdT, 0, d, (int)ld, a.dAs);  // dOp: formed for the routed part
     } else {
       for (int sh = 0; sh < ns; ++sh)
         uni_m(a.dout, false, d, wslice(a.wsd, sh), bf, Is, 1, a.dAs + (size_t)sh * Is, ld, Is, d,

@@ -210,6 +210,11 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     t.Out = reinterpret_cast<uint8_t*>(p.ysh + (size_t)r0 * p.d + (size_t)n * BN);
   }
   t.rmap = nullptr;
+  if (PARTS && L < n_routed && p.perm) {  // A row r is token row perm[r] / k of `a`
+    t.X = static_cast<const uint8_t*>(p.a);
+    t.rmap = p.perm + r0;
+    t.rdiv = p.k;
+  }
   t.W[0] = t.W[1] = w0;
   t.wrows = min(BN, p.d - n * BN);
   t.out_ld = p.d;
@@ -649,9 +654,10 @@ bool buffer_offsets_fit(const FfnArgs& a) {
   const uint64_t lim = 1ull << 32;
   const uint64_t w = (uint64_t)std::max(std::max(a.d, a.I), a.ns * a.Is);
   const uint64_t tile = 514 * w;  // a tile's rows plus the K offset, with margin
-  // A rows of a_parts blocks (their K offsets), and the weight blocks they step through
+  // A rows of a_parts blocks (their K offsets; all T token rows when gathered
+  // through perm), and the weight blocks they step through
   const uint64_t parts = a.a_parts > 1 ? (uint64_t)a.a_parts : 1;
-  const uint64_t xrows = 258 * parts * (uint64_t)a.I * 2;
+  const uint64_t xrows = (a.perm ? (uint64_t)a.T + 2 : 258) * parts * (uint64_t)a.I * 2;
   const uint64_t wpart = parts > 1 ? (uint64_t)a.w_part * 2 * (parts / 2) : 0;
   return (uint64_t)a.T * a.d * 2 + tile < lim && (uint64_t)a.ns * a.d * a.Is * 2 + tile < lim &&
          xrows < lim && wpart + tile < lim;

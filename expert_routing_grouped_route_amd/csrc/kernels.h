@@ -90,6 +90,8 @@ struct FfnArgs {
   // a_parts blocks of I columns, and block b is multiplied by weight block
   // b / 2, which starts w_part elements after block 0 per block index (the
   // bf16 hi and lo parts of an fp32 operand against one weight, and so on).
+  // With perm set as well, `a` holds token rows and routed row r reads token
+  // row perm[r] / k.
   int a_parts;
   int64_t w_part;
   // launch_gate_up_raw_bf16 only: also the bf16 SwiGLU product, in the layout

@@ -296,7 +296,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // forward layout, then the backward scratch.
 struct BLayout {
   size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, rpart, Gs, Us, As, Asbf, dAs, dxs,
-      wdT, wgT, wuT, dYp, dGU, poff, tA, tB, off1, poff1, tiles1, off2, tiles2, wsdT,
+      wdT, wgT, wuT, dGU, poff, tA, tB, off1, poff1, tiles1, off2, tiles2, wsdT,
       wsgT, wsuT, dOp, sGU, poffS, kpart, total;
   int64_t seg_ld;
   int ksplit;
@@ -319,7 +319,7 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.Abf = take(D.dtype == MOE_BF16 ? R * I * 2 : 0);
   B.dA = take(R * I * 4);
   B.y = take(D.dtype == MOE_BF16 ? 0 : R * d * 4);   // fp32 layers only
-  B.dY = take(R * d * 4);
+  B.dY = take(D.dtype == MOE_BF16 ? 0 : R * d * 4);   // fp32 layers only
   B.dXs = take(R * d * 4);
   B.dw = take(R * 4);
   B.dl = take(R * 4);
@@ -337,7 +337,7 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.wdT = take(wsz);
   B.wgT = take(wsz);
   B.wuT = take(wsz);
-  B.dYp = take(bf ? R * d * 4 : 0);
+  B.dOp = take(bf ? T * d * 4 : 0);
   B.dGU = take(bf ? R * I * 8 : 0);
   // weight-gradient operands: per expert 2 * roundup(n_e, 64) columns
   B.seg_ld = ((int64_t)(2 * (R + 63 * (size_t)D.E)) + 63) / 64 * 64;
@@ -353,7 +353,6 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.wsdT = take(bsh ? nsI * d * 2 : 0);
   B.wsgT = take(bsh ? 2 * nsI * d * 2 : 0);  // W_sg^T then W_su^T, one after the other
   B.wsuT = B.wsgT + nsI * d * 2;
-  B.dOp = take(bsh ? T * d * 4 : 0);
   B.sGU = take(bsh ? T * nsI * 8 : 0);
   B.ksplit = bsh ? shared_k_split((int64_t)T, (int)d, (int)Is) : 1;
   B.poffS = take(bsh ? ((size_t)B.ksplit + 1) * 4 : 0);
@@ -458,7 +457,7 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
     ba.wdT = at<uint16_t>(ws, B.wdT);
     ba.wgT = at<uint16_t>(ws, B.wgT);
     ba.wuT = at<uint16_t>(ws, B.wuT);
-    ba.dYp = at<uint16_t>(ws, B.dYp);
+    ba.dOp = at<uint16_t>(ws, B.dOp);
     ba.dGU = at<uint16_t>(ws, B.dGU);
     ba.poff = at<int32_t>(ws, B.poff);
     ba.seg_ld = B.seg_ld;
@@ -473,7 +472,6 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
       ba.wsdT = at<uint16_t>(ws, B.wsdT);
       ba.wsgT = at<uint16_t>(ws, B.wsgT);
       ba.wsuT = at<uint16_t>(ws, B.wsuT);
-      ba.dOp = at<uint16_t>(ws, B.dOp);
       ba.sGU = at<uint16_t>(ws, B.sGU);
     }
   }

@@ -238,12 +238,12 @@ MOE_API moe_status_t moe_layer_fwd_condensed(const moe_dims_t* dims, const void*
 
 /* Workspace of moe_layer_bwd: moe_workspace_bytes plus the backward scratch:
  * the sorted token rows; fp32 [T*k, I] and [T*k, d] intermediates (G, U, the
- * SwiGLU gradient, dY and the sorted rows' input gradients; fp32 layers also
- * A and the expert outputs); fp32 [T, n_shared*I_shared] intermediates of
+ * SwiGLU gradient and the sorted rows' input gradients; fp32 layers also A,
+ * dY and the expert outputs); fp32 [T, n_shared*I_shared] intermediates of
  * the shared experts; and for bf16 layers the transposed weights, the bf16
  * hi/lo parts of the fp32 operands, the per-expert zero-padded transposed
  * operands of the weight-gradient products and split-K partial sums.  About
- * 4.0 GB for 4096 tokens, d = 2048, 64 experts top-6 of I = 1408 and two
+ * 3.6 GB for 4096 tokens, d = 2048, 64 experts top-6 of I = 1408 and two
  * shared experts.  0 for invalid dims. */
 MOE_API size_t moe_backward_workspace_bytes(const moe_dims_t* dims);
 
