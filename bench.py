@@ -228,21 +228,24 @@ def time_backward(cfg, dev, d, wdt, stream, warm=2, timed=5):
     dout = torch.randn(cfg.T, cfg.d, generator=torch.Generator(device="cuda").manual_seed(cfg.seed),
                        device="cuda", dtype=torch.float32)
 
-    def call():
-        moe.moe_layer_bwd(d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
-                          dev["w_down"], dev["wsh_gate"], dev["wsh_up"], dev["wsh_down"], dout,
-                          g["dx"], g["dw_router"], g["dbias"], g["dw_gate"], g["dw_up"],
-                          g["dw_down"], g["dwsh_gate"], g["dwsh_up"], g["dwsh_down"], ws, wsb,
-                          stream)
+    def call(variant=0):
+        args = (d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
+                dev["w_down"], dev["wsh_gate"], dev["wsh_up"], dev["wsh_down"], dout, g["dx"],
+                g["dw_router"], g["dbias"], g["dw_gate"], g["dw_up"], g["dw_down"],
+                g["dwsh_gate"], g["dwsh_up"], g["dwsh_down"], ws, wsb)
+        if variant:
+            moe.moe_layer_bwd_variant(*args, variant, stream)
+        else:
+            moe.moe_layer_bwd(*args, stream)
 
-    def timed_ms():
+    def timed_ms(variant=0):
         for _ in range(warm):
-            call()
+            call(variant)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(timed)]
         for a_, b_ in ev:
             a_.record(stream)
-            call()
+            call(variant)
             b_.record(stream)
         torch.cuda.synchronize()
         return sum(a_.elapsed_time(b_) for a_, b_ in ev) / timed
@@ -254,12 +257,8 @@ def time_backward(cfg, dev, d, wdt, stream, warm=2, timed=5):
     valu = None
     if cfg.dtype == "f32":
         # fp32 layers run every product on the grouped GEMM with free strides;
-        # MOE_BWD_VALU=1 (read by the library at every call) puts it on the VALU
-        os.environ["MOE_BWD_VALU"] = "1"
-        try:
-            ms_valu = timed_ms()
-        finally:
-            del os.environ["MOE_BWD_VALU"]
+        # the vector-ALU variant puts it on the VALU in fp32
+        ms_valu = timed_ms(moe.MOE_VARIANT_BWD_VALU)
         tf_v = fa / (ms_valu * 1e-3) / 1e12
         valu = {"ms": round(ms_valu, 3), "achieved_tflops": round(tf_v, 2),
                 "frac_of_unpacked_fp32_fma_peak": round(tf_v / PEAK_FP32_UNPACKED_TFLOPS, 4),

@@ -24,10 +24,14 @@ MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
 
+MOE_VARIANT_GLOBAL_LOADS = 1
+MOE_VARIANT_BWD_VALU = 2
+
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
                 "moe_grouped_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_fwd_timed",
                 "moe_layer_fwd_overlap", "moe_condensed_workspace_bytes",
-                "moe_layer_fwd_condensed", "moe_backward_workspace_bytes", "moe_layer_bwd")
+                "moe_layer_fwd_condensed", "moe_backward_workspace_bytes", "moe_layer_bwd",
+                "moe_layer_fwd_variant", "moe_layer_bwd_variant")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -76,6 +80,10 @@ _SIGS = {
                                                ctypes.c_size_t, _P]),
     "moe_backward_workspace_bytes": (ctypes.c_size_t, [_DIMS]),
     "moe_layer_bwd": (ctypes.c_int, [_DIMS] + [_P] * 20 + [ctypes.c_size_t, _P]),
+    "moe_layer_fwd_variant": (ctypes.c_int, [_DIMS] + [_P] * 16 + [ctypes.c_size_t, ctypes.c_int,
+                                                                   _P]),
+    "moe_layer_bwd_variant": (ctypes.c_int, [_DIMS] + [_P] * 20 + [ctypes.c_size_t, ctypes.c_int,
+                                                                   _P]),
 }
 
 
@@ -228,3 +236,28 @@ def moe_layer_bwd(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_down, wsh_ga
                              _ptr(dwsh_up), _ptr(dwsh_down), _ptr(ws), int(ws_bytes),
                              _stream(stream))
     _check("moe_layer_bwd", st)
+
+
+def moe_layer_fwd_variant(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_down, wsh_gate,
+                          wsh_up, wsh_down, out, topk_ids_out, topk_w_out, counts_out,
+                          offsets_out, perm_out, ws, ws_bytes, variant, stream=None):
+    st = lib().moe_layer_fwd_variant(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(bias),
+                                     _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(wsh_gate),
+                                     _ptr(wsh_up), _ptr(wsh_down), _ptr(out), _ptr(topk_ids_out),
+                                     _ptr(topk_w_out), _ptr(counts_out), _ptr(offsets_out),
+                                     _ptr(perm_out), _ptr(ws), int(ws_bytes), int(variant),
+                                     _stream(stream))
+    _check("moe_layer_fwd_variant", st)
+
+
+def moe_layer_bwd_variant(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_down, wsh_gate,
+                          wsh_up, wsh_down, dout, dx, dw_router, dbias, dw_gate, dw_up, dw_down,
+                          dwsh_gate, dwsh_up, dwsh_down, ws, ws_bytes, variant, stream=None):
+    st = lib().moe_layer_bwd_variant(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(bias),
+                                     _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(wsh_gate),
+                                     _ptr(wsh_up), _ptr(wsh_down), _ptr(dout), _ptr(dx),
+                                     _ptr(dw_router), _ptr(dbias), _ptr(dw_gate), _ptr(dw_up),
+                                     _ptr(dw_down), _ptr(dwsh_gate), _ptr(dwsh_up),
+                                     _ptr(dwsh_down), _ptr(ws), int(ws_bytes), int(variant),
+                                     _stream(stream))
+    _check("moe_layer_bwd_variant", st)

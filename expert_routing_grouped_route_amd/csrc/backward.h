@@ -52,6 +52,8 @@ struct BwdArgs {
   int64_t T;
   int d, E, k, I, ns, Is;
   bool bf16;
+  bool valu;          // fp32 layers: products on the vector ALUs in fp32
+  bool force_global;  // bf16 layers: GEMM operands through 64-bit global loads
 };
 void launch_layer_bwd(const BwdArgs& a, hipStream_t stream);
 

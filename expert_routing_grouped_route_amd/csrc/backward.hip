@@ -17,14 +17,13 @@
 // the input gradients on the down kernel against transposed weight copies,
 // and the weight gradients, which reduce over an expert's ragged rows, on a
 // segment kernel over per-expert zero-padded transposed operands.  Each fp32
-// operand enters as a bf16 high part and a bf16 low part.  fp32 layers (and
-// MOE_BWD_VALU=1) use a grouped GEMM with free element strides, on the matrix
-// cores with split operands or on the VALU in fp32.  The router-weight
+// operand enters as a bf16 high part and a bf16 low part.  fp32 layers use a
+// grouped GEMM with free element strides, on the matrix cores with split
+// operands (or, in the vector-ALU variant, on the VALU in fp32).  The router-weight
 // gradient is a two-pass fixed-order reduction on the VALU.  Every output
 // element is summed in a fixed order and no atomics are used, so results are
 // reproducible bit for bit.
 #include <algorithm>
-#include <cstdlib>
 
 #include "common.h"
 #include "kernels.h"
@@ -1008,10 +1007,8 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   const int d = a.d, I = a.I, E = a.E;
   const bool bf = a.bf16;
   // products on the matrix cores (bf16 hi/lo parts), or on the VALU in fp32
-  // when MOE_BWD_VALU=1 is in the environment (read at every call, so that a
-  // test can compare both)
-  const char* valu = std::getenv("MOE_BWD_VALU");
-  const bool mf = !(valu && valu[0] == '1');
+  // (the caller's choice, for comparisons of the two)
+  const bool mf = !a.valu;
   const int tt = mf ? MT : GT;
   // M-tile prefix of the experts' row segments
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.offsets, E, tt, a.prefix);
@@ -1056,6 +1053,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     f.I = I;
     f.bf16 = true;
     f.part = kRoutedTiles;
+    f.force_global = a.force_global;
     launch_gate_up_raw_bf16(f, s);  // G, U and the bf16 A
   } else {
     ragged_m(a.xs, bf, d, a.wg, bf, 1, d, (int64_t)I * d, a.G, I, I, d, false);
@@ -1094,6 +1092,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     fd.E = E;
     fd.bf16 = true;
     fd.part = kRoutedTiles;
+    fd.force_global = a.force_global;
   }
   // out = sum over the `parts` K blocks of A's rows (K columns each) of block
   // b times weight block b / 2 (w_part elements apart): one launch of the
@@ -1208,6 +1207,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       f.Is = Is;
       f.bf16 = true;
       f.part = kSharedTiles;
+      f.force_global = a.force_global;
       launch_gate_up_raw_bf16(f, s);
     } else {
       for (int sh = 0; sh < ns; ++sh) {
@@ -1249,6 +1249,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       f1.E = 1;
       f1.bf16 = true;
       f1.part = kRoutedTiles;
+      f1.force_global = a.force_global;
       launch_transpose_bf16(a.wsd, ns, d, Is, a.wsdT, s);        // [ns*Is, d]
       launch_transpose_bf16(a.wsg, 1, (int)ld, d, a.wsgT, s);    // [d, ns*Is]
       launch_transpose_bf16(a.wsu, 1, (int)ld, d, a.wsuT, s);

@@ -38,7 +38,6 @@
 // being the longest); the expert of a routed tile is one lookup in the tile
 // table the dispatch scan wrote.
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 
 #include "grouped_gemm.h"
@@ -646,11 +645,9 @@ int64_t launch_slots(const FfnArgs& a, const GemmGrid& g) {
 // the gathered token rows span all of x (T*d*2 bytes); other A and weight
 // tiles span at most 256 rows of d, I or n_s*I_s elements plus one row; the
 // shared experts' down tiles walk across all their down weights.
-// MOE_GEMM_GLOBAL_LOADS=1 in the environment forces the global-load variant
-// (read at every launch, so that a test can compare both variants).
+// force_global asks for the global-load variant regardless.
 bool buffer_offsets_fit(const FfnArgs& a) {
-  const char* force = std::getenv("MOE_GEMM_GLOBAL_LOADS");
-  if (force && force[0] == '1') return false;
+  if (a.force_global) return false;
   const uint64_t lim = 1ull << 32;
   const uint64_t w = (uint64_t)std::max(std::max(a.d, a.I), a.ns * a.Is);
   const uint64_t tile = 514 * w;  // a tile's rows plus the K offset, with margin

@@ -97,6 +97,10 @@ struct FfnArgs {
   // launch_gate_up_raw_bf16 only: also the bf16 SwiGLU product, in the layout
   // of G and U (or null)
   uint16_t* a_bf16;
+  // take the operands through 64-bit global loads even where the buffer-load
+  // offsets fit in 32 bits (the variant the launchers otherwise use only for
+  // very large operands; same data in LDS, same results)
+  bool force_global;
 };
 constexpr int kAllTiles = 0, kRoutedTiles = 1, kSharedTiles = 2;
 void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream);

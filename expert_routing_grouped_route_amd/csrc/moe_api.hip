@@ -170,10 +170,11 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
                        int32_t* perm_out, void* ws, size_t ws_bytes, hipEvent_t* events,
                        int n_events, hipStream_t stream, hipStream_t side = nullptr,
                        hipEvent_t fork = nullptr, hipEvent_t join = nullptr,
-                       const CondenseIn* cond = nullptr) {
+                       const CondenseIn* cond = nullptr, int variant = 0) {
   moe_status_t st = check_dims(dims);
   if (st != MOE_OK) return st;
   const moe_dims_t& D = *dims;
+  if (variant & ~MOE_VARIANT_GLOBAL_LOADS) return MOE_ERR_INVALID_ARG;
   if (n_events < 0 || n_events > 6 || (n_events > 0 && !events)) return MOE_ERR_INVALID_ARG;
   const bool two_streams = side || fork || join;
   if (two_streams && (!side || !fork || !join || n_events)) return MOE_ERR_INVALID_ARG;
@@ -231,6 +232,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
   fa.ash = at<void>(ws, L.ash);
   fa.y = at<float>(ws, L.y);
   fa.ysh = sh ? at<float>(ws, L.ysh) : nullptr;
+  fa.force_global = (variant & MOE_VARIANT_GLOBAL_LOADS) != 0;
   if (two_streams) {
     // the shared experts depend on x alone: they run on the side stream from
     // the start, beside the gate, the dispatch and the routed experts
@@ -363,25 +365,17 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   return B;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t moe_backward_workspace_bytes(const moe_dims_t* dims) {
-  if (check_dims(dims) != MOE_OK) return 0;
-  return backward_layout_of(*dims).total;
-}
-
-moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_router,
-                           const float* bias, const void* w_gate, const void* w_up,
-                           const void* w_down, const void* wsh_gate, const void* wsh_up,
-                           const void* wsh_down, const float* dout, float* dx, float* dw_router,
-                           float* dbias, float* dw_gate, float* dw_up, float* dw_down,
-                           float* dwsh_gate, float* dwsh_up, float* dwsh_down, void* ws,
-                           size_t ws_bytes, hipStream_t stream) {
+moe_status_t layer_bwd(const moe_dims_t* dims, const void* x, const void* w_router,
+                       const float* bias, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* wsh_gate, const void* wsh_up,
+                       const void* wsh_down, const float* dout, float* dx, float* dw_router,
+                       float* dbias, float* dw_gate, float* dw_up, float* dw_down,
+                       float* dwsh_gate, float* dwsh_up, float* dwsh_down, void* ws,
+                       size_t ws_bytes, int variant, hipStream_t stream) {
   moe_status_t st = check_dims(dims);
   if (st != MOE_OK) return st;
   const moe_dims_t& D = *dims;
+  if (variant & ~(MOE_VARIANT_GLOBAL_LOADS | MOE_VARIANT_BWD_VALU)) return MOE_ERR_INVALID_ARG;
   const Layout L = layout_of(D);
   const BLayout B = backward_layout_of(D);
   const size_t es = elem_bytes(D), T = (size_t)D.T, R = T * D.k, E = D.E, d = D.d;
@@ -504,8 +498,44 @@ moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_
   ba.ns = D.n_shared;
   ba.Is = D.I_shared;
   ba.bf16 = D.dtype == MOE_BF16;
+  ba.valu = !ba.bf16 && (variant & MOE_VARIANT_BWD_VALU) != 0;
+  ba.force_global = (variant & MOE_VARIANT_GLOBAL_LOADS) != 0;
   launch_layer_bwd(ba, stream);
   return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_backward_workspace_bytes(const moe_dims_t* dims) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  return backward_layout_of(*dims).total;
+}
+
+moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const void* w_router,
+                           const float* bias, const void* w_gate, const void* w_up,
+                           const void* w_down, const void* wsh_gate, const void* wsh_up,
+                           const void* wsh_down, const float* dout, float* dx, float* dw_router,
+                           float* dbias, float* dw_gate, float* dw_up, float* dw_down,
+                           float* dwsh_gate, float* dwsh_up, float* dwsh_down, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  return layer_bwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down,
+                   dout, dx, dw_router, dbias, dw_gate, dw_up, dw_down, dwsh_gate, dwsh_up,
+                   dwsh_down, ws, ws_bytes, 0, stream);
+}
+
+moe_status_t moe_layer_bwd_variant(const moe_dims_t* dims, const void* x, const void* w_router,
+                                   const float* bias, const void* w_gate, const void* w_up,
+                                   const void* w_down, const void* wsh_gate, const void* wsh_up,
+                                   const void* wsh_down, const float* dout, float* dx,
+                                   float* dw_router, float* dbias, float* dw_gate, float* dw_up,
+                                   float* dw_down, float* dwsh_gate, float* dwsh_up,
+                                   float* dwsh_down, void* ws, size_t ws_bytes, int variant,
+                                   hipStream_t stream) {
+  return layer_bwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down,
+                   dout, dx, dw_router, dbias, dw_gate, dw_up, dw_down, dwsh_gate, dwsh_up,
+                   dwsh_down, ws, ws_bytes, variant, stream);
 }
 
 size_t moe_workspace_bytes(const moe_dims_t* dims) {
@@ -654,6 +684,18 @@ moe_status_t moe_layer_fwd(const moe_dims_t* dims, const void* x, const void* w_
   return layer_fwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down, out,
                    topk_ids_out, topk_w_out, counts_out, offsets_out, perm_out, ws, ws_bytes,
                    nullptr, 0, stream);
+}
+
+moe_status_t moe_layer_fwd_variant(const moe_dims_t* dims, const void* x, const void* w_router,
+                                   const float* bias, const void* w_gate, const void* w_up,
+                                   const void* w_down, const void* wsh_gate, const void* wsh_up,
+                                   const void* wsh_down, float* out, int32_t* topk_ids_out,
+                                   float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                                   int32_t* perm_out, void* ws, size_t ws_bytes, int variant,
+                                   hipStream_t stream) {
+  return layer_fwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down, out,
+                   topk_ids_out, topk_w_out, counts_out, offsets_out, perm_out, ws, ws_bytes,
+                   nullptr, 0, stream, nullptr, nullptr, nullptr, nullptr, variant);
 }
 
 moe_status_t moe_layer_fwd_timed(const moe_dims_t* dims, const void* x, const void* w_router,

@@ -6,7 +6,7 @@
  * routed SwiGLU experts run as a grouped GEMM, optional always-on shared
  * experts, and Combine back to token order.  The operator chain is the MoE
  * sub-block of the FarSkip-Collective review ("Core claim"; Fig. 2 caption,
- * "MoE layer main operator execution"; Fig. 11 caption: Dispatch, routed
+ * on the MoE layer's main operators; Fig. 11 caption: Dispatch, routed
  * experts, Combine, shared expert).  Top-k routing is the gate of the
  * expert-prototyping abstract on the "Daily Papers" search page; running each
  * expert as one dense product over its grouped tokens is the "Expert-Centric
@@ -98,6 +98,11 @@ MOE_API size_t moe_workspace_bytes(const moe_dims_t* dims);
 MOE_API const char* moe_status_str(moe_status_t status);
 
 /* Gate: router logits, top-k ids and renormalised softmax weights.
+ * Passage: top-k routing over the router's scores is the gate of the
+ * expert-prototyping abstract on the "Daily Papers" search page (top-2 in the
+ * ScMoE abstract there); its time is the T_gate term of the overlap window in
+ * the FarSkip-Collective review (axiom ledger, Eq. 9).  Softmax, renormalising
+ * over the kept k and the lower-index tie rule are readings (see the header).
  *   x [T,d], w_router [E,d] (dtype); bias [E] fp32 or NULL.
  *   logits_in [T,E] fp32 or NULL: when given, the top-k is taken on these
  *     logits and x, w_router and bias are not read (may be NULL).
@@ -112,6 +117,11 @@ MOE_API moe_status_t moe_route(const moe_dims_t* dims, const void* x, const void
                        int32_t* topk_ids, float* topk_w, hipStream_t stream);
 
 /* Dispatch: group the R = T*k assignments a = t*k + j by expert, stably.
+ * Passage: Dispatch, the token traffic that sends each token to its experts
+ * (FarSkip-Collective review, "Core claim" and Fig. 11 caption; the Luffy
+ * review, "Core claim", on dispatch and combine traffic).  On one GPU's share
+ * it is a stable counting sort plus a row gather; the row order inside a
+ * segment (ascending a) is a reading.
  *   topk_ids [T,k] int32 in [0,E).
  *   counts [E]: assignments per expert.  offsets [E+1]: exclusive prefix sum,
  *   offsets[E] = R.  perm [R]: perm[i] = assignment at sorted row i.
@@ -123,6 +133,12 @@ MOE_API moe_status_t moe_dispatch(const moe_dims_t* dims, const void* x, const i
                           void* x_sorted, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Routed experts as a grouped GEMM, plus the shared experts.
+ * Passage: the routed experts are the T_routed term of the FarSkip-Collective
+ * review's overlap window (axiom ledger, Eq. 9) and the always-on shared expert
+ * is the branch its Fig. 11 caption runs beside Combine; one dense product per
+ * expert over its grouped tokens is the "Expert-Centric Scheduling" of the
+ * OmniMoE abstract on the "Daily Papers" search page.  The SwiGLU form of the
+ * expert and the bf16 rounding of A are readings.
  *   x_sorted [R,d] (dtype) and offsets [E+1] as produced by moe_dispatch.
  *   w_gate, w_up [E,I,d], w_down [E,d,I] (dtype).
  *   x [T,d] and wsh_* : shared experts; NULL when n_shared == 0.
@@ -138,6 +154,9 @@ MOE_API moe_status_t moe_grouped_ffn(const moe_dims_t* dims, const void* x_sorte
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Combine: out[t] = sum_{j<k} topk_w[t,j] * y_sorted[inv_perm[t*k+j]] (+ y_shared[t]),
+ * Passage: Combine, the return of expert outputs to token order
+ * (FarSkip-Collective review, "Core claim" and Fig. 11 caption; the Luffy
+ * review, "Core claim").  The fp32 slot-order sum is a reading.
  * accumulated in fp32 in ascending j, shared term last.
  *   y_sorted [R,d], inv_perm [R], topk_w [T,k], y_shared [T,d] or NULL, out [T,d]. */
 MOE_API moe_status_t moe_combine(const moe_dims_t* dims, const float* y_sorted, const int32_t* inv_perm,
@@ -145,6 +164,9 @@ MOE_API moe_status_t moe_combine(const moe_dims_t* dims, const float* y_sorted, 
                          hipStream_t stream);
 
 /* The whole layer: route, dispatch, grouped FFN with shared experts, combine.
+ * Passage: the MoE sub-block as the FarSkip-Collective review lays out its
+ * operators ("Core claim"; Fig. 2 caption on the MoE layer's main operators;
+ * Fig. 11 caption: gate, Dispatch, routed experts, shared expert, Combine).
  *   Inputs as above (wsh_* NULL when n_shared == 0); out [T,d] fp32.
  *   topk_ids_out [T,k], topk_w_out [T,k], counts_out [E], offsets_out [E+1],
  *   perm_out [R]: optional copies of the intermediate results (NULL = skip).
@@ -155,6 +177,32 @@ MOE_API moe_status_t moe_layer_fwd(const moe_dims_t* dims, const void* x, const 
                            const void* wsh_down, float* out, int32_t* topk_ids_out,
                            float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
                            int32_t* perm_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Kernel variants, for tests and measurements that compare another kernel
+ * path with the default one on the same inputs (the default entry points
+ * take variant 0; the choice is always the caller's, never the environment's).
+ * MOE_VARIANT_GLOBAL_LOADS: the grouped GEMMs take their operands through
+ *   64-bit global loads, the form the library otherwise takes only when an
+ *   operand's byte offsets exceed 32 bits; same data in LDS, same MFMA order,
+ *   so results are bit-identical to variant 0.
+ * MOE_VARIANT_BWD_VALU (moe_layer_bwd_variant only): for fp32 layers the
+ *   gradient products run on the vector ALUs in fp32 instead of the matrix
+ *   cores with bf16 hi/lo operand parts; ignored for bf16 layers.
+ * Any other bit: MOE_ERR_INVALID_ARG. */
+#define MOE_VARIANT_GLOBAL_LOADS 1
+#define MOE_VARIANT_BWD_VALU 2
+
+/* moe_layer_fwd through the kernel variant `variant` (MOE_VARIANT_GLOBAL_LOADS
+ * or 0); every other argument and the result as moe_layer_fwd. */
+MOE_API moe_status_t moe_layer_fwd_variant(const moe_dims_t* dims, const void* x,
+                                           const void* w_router, const float* bias,
+                                           const void* w_gate, const void* w_up,
+                                           const void* w_down, const void* wsh_gate,
+                                           const void* wsh_up, const void* wsh_down, float* out,
+                                           int32_t* topk_ids_out, float* topk_w_out,
+                                           int32_t* counts_out, int32_t* offsets_out,
+                                           int32_t* perm_out, void* ws, size_t ws_bytes,
+                                           int variant, hipStream_t stream);
 
 /* moe_layer_fwd that also records HIP events on `stream` at its stage
  * boundaries, for per-stage timing.  events[0..n_events) are caller-created
@@ -266,8 +314,8 @@ MOE_API size_t moe_backward_workspace_bytes(const moe_dims_t* dims);
  * the inputs (nothing is carried over from a forward call).  The products
  * run on the bf16 matrix cores with fp32 accumulation, each fp32 operand
  * taken as bf16 parts hi = bf16(v), lo = bf16(v - hi) (|v - hi - lo| <=
- * 2^-16 |v|); with MOE_BWD_VALU=1 in the environment, fp32 layers run them
- * on the vector ALUs in fp32 instead.
+ * 2^-16 |v|) (moe_layer_bwd_variant with MOE_VARIANT_BWD_VALU runs them for
+ * fp32 layers on the vector ALUs in fp32 instead).
  * All other arithmetic is fp32 (bf16 inputs widened), and each output element
  * is summed in a fixed order: two calls give identical bits.
  *   x, w_router, bias, w_gate, w_up, w_down, wsh_*: as in moe_layer_fwd.
@@ -288,6 +336,20 @@ MOE_API moe_status_t moe_layer_bwd(const moe_dims_t* dims, const void* x, const 
                                    float* dw_down, float* dwsh_gate, float* dwsh_up,
                                    float* dwsh_down, void* ws, size_t ws_bytes,
                                    hipStream_t stream);
+
+/* moe_layer_bwd through the kernel variant `variant` (a combination of
+ * MOE_VARIANT_GLOBAL_LOADS and MOE_VARIANT_BWD_VALU, or 0); every other
+ * argument and the result as moe_layer_bwd. */
+MOE_API moe_status_t moe_layer_bwd_variant(const moe_dims_t* dims, const void* x,
+                                           const void* w_router, const float* bias,
+                                           const void* w_gate, const void* w_up,
+                                           const void* w_down, const void* wsh_gate,
+                                           const void* wsh_up, const void* wsh_down,
+                                           const float* dout, float* dx, float* dw_router,
+                                           float* dbias, float* dw_gate, float* dw_up,
+                                           float* dw_down, float* dwsh_gate, float* dwsh_up,
+                                           float* dwsh_down, void* ws, size_t ws_bytes,
+                                           int variant, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -8,12 +8,12 @@ What it computes is the MoE sub-block as the pages name its operators: a gate
 that picks experts per token, Dispatch of each token to its experts, the
 routed experts, an always-on shared expert, and Combine back to token order
 (FarSkip-Collective review: "Core claim" and "What carries the argument";
-Fig. 2 caption "MoE layer main operator execution"; Fig. 11 caption, where
+Fig. 2 caption, on the MoE layer's main operators; Fig. 11 caption, where
 Combine is overlapped with the shared expert).  Top-k routing is named in the
-expert-prototyping abstract of the "Daily Papers" search page ("number of
-sparsely activated experts k ... in top-k routing"), top-2 in the ScMoE
-abstract on the same page; uneven routing with experts that receive few or
-no tokens in the LLEP abstract there.  Grouping tokens by expert so that each
+expert-prototyping abstract of the "Daily Papers" search page (the count k of
+experts a token activates), top-2 in the ScMoE abstract on the same page;
+uneven routing with experts that receive few or no tokens in the LLEP
+abstract there.  Grouping tokens by expert so that each
 expert runs as a dense matrix product is the "Expert-Centric Scheduling" idea
 of the OmniMoE abstract on that page.
 

@@ -153,7 +153,8 @@ class Layer:
     def _f32(self, *shape):
         return torch.empty(shape, dtype=torch.float32, device="cuda")
 
-    def layer(self, w_down_scale=None):
+    def layer(self, w_down_scale=None, variant=0):
+        """moe_layer_fwd (or moe_layer_fwd_variant with a nonzero variant)."""
         c, t = self.cfg, self.t
         out = self._f32(c.T, c.d)
         ids, w = self._i32(c.T, c.k), self._f32(c.T, c.k)
@@ -162,9 +163,13 @@ class Layer:
         if w_down_scale is not None:
             wd = wd * w_down_scale
             wsd = wsd * w_down_scale if wsd is not None else None
-        moe.moe_layer_fwd(self.dims, t["x"], t["w_router"], t.get("bias"), t["w_gate"], t["w_up"],
-                          wd, t.get("wsh_gate"), t.get("wsh_up"), wsd, out, ids, w, counts,
-                          offsets, perm, self.ws, self.ws_bytes)
+        args = (self.dims, t["x"], t["w_router"], t.get("bias"), t["w_gate"], t["w_up"], wd,
+                t.get("wsh_gate"), t.get("wsh_up"), wsd, out, ids, w, counts, offsets, perm,
+                self.ws, self.ws_bytes)
+        if variant:
+            moe.moe_layer_fwd_variant(*args, variant)
+        else:
+            moe.moe_layer_fwd(*args)
         torch.cuda.synchronize()
         return dict(out=to_np(out), ids=to_np(ids), w=to_np(w), counts=to_np(counts),
                     offsets=to_np(offsets), perm=to_np(perm))

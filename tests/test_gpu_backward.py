@@ -9,8 +9,8 @@ Gradients are compared with the layer's rules scaled to each tensor's size:
 mean |g - r| <= 1e-3 rms(r) and max_i |g_i - r_i| / max(|r_i|, rms(r)) <=
 2e-2.  Experts without tokens must get exactly zero weight gradients; two
 calls must agree bit for bit.  The products run on the matrix cores (each
-fp32 operand as bf16 hi + lo parts); the fp32 VALU variant is held to the
-same bar."""
+fp32 operand as bf16 hi + lo parts); for fp32 layers the vector-ALU variant
+(moe_layer_bwd_variant with MOE_VARIANT_BWD_VALU) is held to the same bar."""
 import numpy as np
 import pytest
 import torch
@@ -33,6 +33,8 @@ CASES = {
                          seed=24),
     "bwd_one_token": MoEShape("bwd_one_token", T=1, d=64, E=8, k=2, I=64, seed=25),
     "bwd_k_equals_E": MoEShape("bwd_k_equals_E", T=70, d=64, E=4, k=4, I=64, seed=26),
+    "bwd_fp32_zipf": MoEShape("bwd_fp32_zipf", T=256, d=128, E=16, k=4, I=128, dtype="f32",
+                              seed=28, bias="zipf", zipf_alpha=1.5),
 }
 
 GRADS = ("dx", "dw_router", "dbias", "dw_gate", "dw_up", "dw_down", "dwsh_gate", "dwsh_up",
@@ -65,7 +67,8 @@ class Case:
         torch.cuda.synchronize()
         return _np(L)
 
-    def backward(self):
+    def backward(self, variant=0):
+        """moe_layer_bwd (moe_layer_bwd_variant for a nonzero variant)."""
         c, t = self.cfg, self.t
         f = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")
         g = dict(dx=f(c.T, c.d), dw_router=f(c.E, c.d), dbias=f(c.E), dw_gate=f(c.E, c.I, c.d),
@@ -81,10 +84,14 @@ class Case:
         dout = torch.from_numpy(self.dout).cuda()
         print(f"[bwd {c.name}] T={c.T} d={c.d} E={c.E} k={c.k} I={c.I} "
               f"shared={c.n_shared}x{c.I_shared} {c.dtype}", flush=True)
-        moe.moe_layer_bwd(self.dims, t["x"], t["w_router"], t.get("bias"), t["w_gate"], t["w_up"],
-                          t["w_down"], t.get("wsh_gate"), t.get("wsh_up"), t.get("wsh_down"), dout,
-                          g["dx"], g["dw_router"], g["dbias"], g["dw_gate"], g["dw_up"],
-                          g["dw_down"], g["dwsh_gate"], g["dwsh_up"], g["dwsh_down"], ws, wsb)
+        args = (self.dims, t["x"], t["w_router"], t.get("bias"), t["w_gate"], t["w_up"],
+                t["w_down"], t.get("wsh_gate"), t.get("wsh_up"), t.get("wsh_down"), dout,
+                g["dx"], g["dw_router"], g["dbias"], g["dw_gate"], g["dw_up"], g["dw_down"],
+                g["dwsh_gate"], g["dwsh_up"], g["dwsh_down"], ws, wsb)
+        if variant:
+            moe.moe_layer_bwd_variant(*args, variant)
+        else:
+            moe.moe_layer_bwd(*args)
         torch.cuda.synchronize()
         return {n: (None if v is None else _np(v)) for n, v in g.items()}
 
@@ -136,33 +143,37 @@ def test_backward_matches_oracle(name):
         assert np.all(got["dw_router"] == 0.0) and np.all(got["dbias"] == 0.0)
 
 
-@pytest.mark.parametrize("name", ["bwd_bf16_shared", "bwd_fp32_two_shared", "bwd_bf16_zipf"])
-def test_backward_vector_alu_variant_matches_oracle(name, monkeypatch):
-    """The products on the VALU in fp32 (MOE_BWD_VALU=1) instead of the matrix
-    cores' bf16 hi/lo parts: the same bar against the oracle."""
-    monkeypatch.setenv("MOE_BWD_VALU", "1")
+@pytest.mark.parametrize("name", ["bwd_fp32_two_shared", "bwd_fp32_zipf"])
+def test_backward_vector_alu_variant_matches_oracle(name):
+    """fp32 layers with every gradient product on the VALU in fp32
+    (MOE_VARIANT_BWD_VALU) instead of the matrix cores' bf16 hi/lo parts: the
+    same bar against the oracle, with two shared experts, and with Zipf-skewed
+    routing that leaves experts without tokens (their weight gradients must
+    be exactly zero).  bf16 layers ignore the variant."""
     c = get(name)
     L = c.logits()
-    got = c.backward()
+    got = c.backward(variant=moe.MOE_VARIANT_BWD_VALU)
     ref = c.reference(L)
+    empty = np.nonzero(np.diff(np.asarray(ref["offsets"])) == 0)[0]
+    for e in empty:
+        for n in ("dw_gate", "dw_up", "dw_down", "dw_router"):
+            assert np.all(got[n][e] == 0.0), (name, n, e)
     for n in GRADS:
         if ref[n] is not None:
             assert_grad_close(got[n], ref[n], f"{name}.{n} (VALU)")
 
 
 @pytest.mark.parametrize("name", ["bwd_bf16_shared", "bwd_bf16_zipf"])
-def test_backward_global_load_variant(name, monkeypatch):
+def test_backward_global_load_variant(name):
     """The GEMM operands through 64-bit global loads instead of buffer loads
-    (the variant taken when a product's offsets exceed 32 bits; forced here
-    through MOE_GEMM_GLOBAL_LOADS=1): the same bar against the oracle, and the
+    (the variant taken when a product's offsets exceed 32 bits; asked for here
+    with MOE_VARIANT_GLOBAL_LOADS): the same bar against the oracle, and the
     same gradients bit for bit as the buffer-load call (same data in LDS, same
     MFMA order)."""
     c = get(name)
     L = c.logits()
     base = c.backward()
-    monkeypatch.setenv("MOE_GEMM_GLOBAL_LOADS", "1")
-    got = c.backward()
-    monkeypatch.delenv("MOE_GEMM_GLOBAL_LOADS")
+    got = c.backward(variant=moe.MOE_VARIANT_GLOBAL_LOADS)
     ref = c.reference(L)
     for n in GRADS:
         if ref[n] is None:
@@ -171,8 +182,9 @@ def test_backward_global_load_variant(name, monkeypatch):
         assert np.array_equal(got[n], base[n]), n
 
 
-def test_backward_has_empty_experts_in_skewed_case():
-    c = get("bwd_bf16_zipf")
+@pytest.mark.parametrize("name", ["bwd_bf16_zipf", "bwd_fp32_zipf"])
+def test_backward_has_empty_experts_in_skewed_case(name):
+    c = get(name)
     ref = c.reference(c.logits())
     assert np.any(np.diff(np.asarray(ref["offsets"])) == 0)
 

@@ -201,20 +201,18 @@ def test_layer_is_deterministic(name):
 
 
 @pytest.mark.parametrize("name", ["med_bf16_shared", "med_bf16_zipf", "one_expert"])
-def test_gemm_load_variants_agree(name, monkeypatch):
+def test_gemm_load_variants_agree(name):
     """The bf16 grouped GEMMs have two operand-load variants: buffer loads with
     32-bit offsets (used whenever every offset fits) and 64-bit global loads
-    (otherwise; forced here through MOE_GEMM_GLOBAL_LOADS=1).  Both give the
-    same layer and grouped-FFN outputs bit for bit."""
+    (otherwise; asked for here through moe_layer_fwd_variant with
+    MOE_VARIANT_GLOBAL_LOADS).  Both give the same layer outputs bit for bit
+    (test_layer holds the default call to the oracle)."""
+    import expert_routing_grouped_route_amd as moe
     cfg, arrays, ref, lay = case(name)
-    a, fa = lay.layer(), lay.ffn(ref["x_sorted"], ref["offsets"])
-    monkeypatch.setenv("MOE_GEMM_GLOBAL_LOADS", "1")
-    b, fb = lay.layer(), lay.ffn(ref["x_sorted"], ref["offsets"])
-    monkeypatch.delenv("MOE_GEMM_GLOBAL_LOADS")
+    a = lay.layer()
+    b = lay.layer(variant=moe.MOE_VARIANT_GLOBAL_LOADS)
     for key in a:
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
-    for key in fa:
-        np.testing.assert_array_equal(fa[key], fb[key], err_msg=key)
 
 
 @pytest.mark.parametrize("name", ALL)

@@ -148,6 +148,73 @@ def test_lane_order_logits_within_dot_product_bound():
     assert np.any(L != exact.astype(np.float32))  # it is a genuinely different rounding order
 
 
+def _one_logit(xv, d, bias=None):
+    """Lane-order logit of one token against one all-ones router row, so that
+    the products are the x values themselves (exact)."""
+    x = np.zeros((1, d), np.float32)
+    for i, v in xv.items():
+        x[0, i] = v
+    w = np.ones((1, d), np.float32)
+    b = None if bias is None else np.array([bias], np.float32)
+    return float(oracle.router_logits_f32_lane_order(x, w, b)[0, 0])
+
+
+# Each case below is worked out by hand from the stated order (partial l
+# takes i = l, l+64, ... ascending; separate multiply and add; butterfly over
+# 32, 16, 8, 4, 2, 1; bias last) and chosen so that any other plausible order
+# rounds to a different float32.  2^24 + 1 is a tie between 2^24 and 2^24 + 2
+# and rounds to the even 2^24.
+B24 = float(2 ** 24)
+
+
+def test_lane_order_butterfly_runs_from_stride_32_down():
+    # partials: p0 = 2^24, p1 = 1, p32 = -2^24.  Stride 32 first: p0 + p32 = 0
+    # and p1 + p33 = 1; strides 16..2 add zeros; stride 1: 0 + 1 = 1.
+    # From stride 1 up instead: p0 + p1 = 2^24 + 1 -> 2^24, then + (-2^24) = 0.
+    got = _one_logit({0: B24, 1: 1.0, 32: -B24}, 64)
+    assert got == 1.0
+    exact = Fraction(int(B24)) + 1 - Fraction(int(B24))
+    assert exact == 1  # here the stated order happens to be exact
+    # a left-to-right sum loses the 1: (2^24 + 1) -> 2^24, minus 2^24
+    seq = np.float32(0)
+    for v in (B24, 1.0, -B24):
+        seq = np.float32(seq + np.float32(v))
+    assert float(seq) == 0.0
+
+
+def test_lane_order_partials_take_every_64th_element():
+    # d = 128.  Stated stride: partial 0 = p0 + p64 = 2^24 + 1 -> 2^24, partial
+    # 1 = p1 = -2^24; butterfly: 2^24 + (-2^24) = 0 (the 1 was lost in lane 0).
+    # Contiguous pairs (partial l = p_2l + p_2l+1) would give partial 0 =
+    # 2^24 - 2^24 = 0 and partial 32 = p64 = 1, i.e. 1.
+    got = _one_logit({0: B24, 64: 1.0, 1: -B24}, 128)
+    assert got == 0.0
+
+
+def test_lane_order_multiply_and_add_are_rounded_separately():
+    # d = 128, one lane: partial 0 = p0 + p64 with p0 = (-1 - 2^-11) * 1 and
+    # p64 = (1 + 2^-12)^2 = 1 + 2^-11 + 2^-24 exactly, which rounds to
+    # 1 + 2^-11 (a tie at half an ulp; 1 + 2^-11 is the even neighbour).  So
+    # the partial is 0.  A fused multiply-add would keep the 2^-24.
+    x = np.zeros((1, 128), np.float32)
+    w = np.ones((1, 128), np.float32)
+    x[0, 0] = -1.0 - 2.0 ** -11
+    x[0, 64] = 1.0 + 2.0 ** -12
+    w[0, 64] = 1.0 + 2.0 ** -12
+    got = float(oracle.router_logits_f32_lane_order(x, w, None)[0, 0])
+    assert got == 0.0
+    exact = Fraction(x[0, 0].item()) + Fraction(x[0, 64].item()) * Fraction(w[0, 64].item())
+    assert exact == Fraction(1, 2 ** 24)  # what a fused multiply-add would return
+
+
+def test_lane_order_bias_is_added_after_the_butterfly():
+    # partials p0 = p1 = 1: the butterfly gives 2, then + 2^24 = 2^24 + 2
+    # (representable).  Adding the bias to partial 0 first would give
+    # 2^24 + 1 -> 2^24, then + 1 -> 2^24.
+    got = _one_logit({0: 1.0, 1: 1.0}, 64, bias=B24)
+    assert got == B24 + 2.0
+
+
 # ---------------------------------------------------------------------------
 # Top-k gate
 # ---------------------------------------------------------------------------
