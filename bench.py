@@ -16,9 +16,12 @@ three passes of the same number of steps:
 second stream); all are reported.  For workloads with duplicated rows (or with
 ``--condense COS``) a fourth pass times ``moe_layer_fwd_condensed``, token
 condensation, an approximation of the layer: it is reported under
-``condensed`` with the rows it keeps, never as ``value``.  The default workload is the DeepSeek-V2-Lite-shaped layer
-(T=4096, d=2048, 64 experts top-6 + 2 shared, I=1408), bf16 inputs with fp32
-accumulation, synthetic seeded data.
+``condensed`` with the rows it keeps, never as ``value``.  The default
+workload is the largest one-GPU configuration, the prefill-scale layer
+(T=32768 tokens as 8 sequences of 4096, d=2048, 64 experts top-6 + 2 shared,
+I=1408, 30% near-duplicate token rows), bf16 inputs with fp32 accumulation,
+synthetic seeded data.  The DeepSeek-V2-Lite-shaped layer (T=4096, same
+experts) is timed too, more briefly, under ``other_workloads`` (``--also``).
 
 Prints one JSON line.  Per-stage times come from the third pass: HIP events
 that the library records on the layer's stream between its kernels, averaged
@@ -331,7 +334,111 @@ def cpu_baseline(cfg, arrays, budget_s=10.0, max_runs=7):
     return {"value": Ts / med, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {Ts} of {cfg.T} tokens, all {cfg.E} experts"
                       f"{' + shared' if cfg.n_shared else ''}, fp64 NumPy oracle; median of "
-                      f"{len(times)} run(s) of {med:.2f} s"}
+                      f"{len(times)} run(s) of {med:.2f} s",
+            "cpu_model": cpu_model(), "blas": blas_info(cores)}
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def blas_info(cores):
+    """The BLAS library NumPy runs on (threadpoolctl's view, under the same
+    thread limit as the timed runs)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    with threadpool_limits(limits=cores):
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    return [{"library": i.get("internal_api"), "version": i.get("version"),
+             "threads": i.get("num_threads"), "architecture": i.get("architecture")}
+            for i in libs]
+
+
+def quick_workload(cfg, args):
+    """Another workload's layer, timed more briefly than the headline one: the
+    one-stream call, the two-stream call (layers with shared experts) and a
+    pass with stage events, each args.warmup untimed and args.steps timed
+    calls after a 0.3 s device warm-up.  Reports the faster uninstrumented
+    timing, the stage times, the gate/up fraction of the bf16 peak and the
+    bandwidth stages' rates over their algorithmic bytes."""
+    import torch
+
+    import expert_routing_grouped_route_amd as moe
+    import moe_synth
+
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    arrays = moe_synth.generate(cfg, workers=min(16, len(os.sched_getaffinity(0))))
+    wdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = {n: (None if v is None else torch.from_numpy(v).to(
+        torch.float32 if n == "bias" else wdt).cuda()) for n, v in arrays.items()}
+    del arrays
+    d = moe.dims(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.I_shared, cfg.dtype)
+    ws_bytes = moe.moe_workspace_bytes(d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(cfg.T, cfg.d, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    lay = (d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"],
+           dev["wsh_gate"], dev["wsh_up"], dev["wsh_down"], out, None, None, None, None, None, ws,
+           ws_bytes)
+    side = torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+    fork.record(stream)
+    join.record(stream)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for ev in events:
+        for e in ev:
+            e.record(stream)
+
+    def passes(label, fn):
+        for _ in range(args.warmup):
+            fn(0)
+        torch.cuda.synchronize()
+        print(f"[bench] timing {args.steps} steps: {cfg.name} {label}", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < 0.3:
+        for _ in range(10):
+            moe.moe_layer_fwd(*lay, stream)
+        torch.cuda.synchronize()
+    walls = {"single_stream": passes("moe_layer_fwd", lambda i: moe.moe_layer_fwd(*lay, stream))}
+    if cfg.n_shared:
+        walls["shared_on_second_stream"] = passes(
+            "moe_layer_fwd_overlap",
+            lambda i: moe.moe_layer_fwd_overlap(*lay, side, fork, join, stream))
+    passes("moe_layer_fwd_timed", lambda i: moe.moe_layer_fwd_timed(
+        *lay, [e.cuda_event for e in events[i]], stream))
+    stage_ms = {s_: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps
+                for j, s_ in enumerate(STAGES)}
+    best = min(walls, key=walls.get)
+    ms = walls[best] * 1e3 / args.steps
+    fl_gu, fl_dn = gemm_flops(cfg)
+    gu_tf = fl_gu / (stage_ms["gate_up"] * 1e-3) / 1e12
+    sb = stage_bytes(cfg)
+    return {"config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k,
+                       "I": cfg.I, "n_shared": cfg.n_shared, "I_shared": cfg.I_shared,
+                       "dtype": cfg.dtype},
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+            "value_from": best,
+            "layer_variants_ms": {k_: round(v * 1e3 / args.steps, 4) for k_, v in walls.items()},
+            "stages_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
+            "gate_up": {"achieved_tflops": round(gu_tf, 1),
+                        "frac_bf16_peak": round(gu_tf / PEAK_BF16_TFLOPS, 4)},
+            "down_tflops": round(fl_dn / (stage_ms["down"] * 1e-3) / 1e12, 1),
+            "hbm": {s_: {"GB/s": round(sb[s_] / (stage_ms[s_] * 1e-3) / 1e9, 1),
+                         "frac_of_8TB/s": round(sb[s_] / (stage_ms[s_] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "bytes": sb[s_]} for s_ in sb}}
 
 
 def main():
@@ -341,7 +448,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="deepseek_v2_lite", choices=list(moe_synth.CONFIGS))
+    ap.add_argument("--workload", default="prefill_stress", choices=list(moe_synth.CONFIGS))
+    ap.add_argument("--also", default="deepseek_v2_lite",
+                    help="comma-separated workloads timed briefly after the headline one "
+                         "(one-stream and two-stream layer, stage events), reported under "
+                         "other_workloads; empty for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--condense", type=float, default=None, metavar="COS",
                     help="also time moe_layer_fwd_condensed with this cosine threshold (the "
@@ -629,6 +740,10 @@ def main():
         "backward": backward,
         "hbm": hbm,
     }
+    others = {}
+    for name in [n for n in args.also.split(",") if n and n != cfg.name]:
+        others[name] = quick_workload(moe_synth.CONFIGS[name], args)
+    rec["other_workloads"] = others
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host cores", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, arrays)

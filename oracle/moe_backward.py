@@ -37,7 +37,7 @@ import numpy as np
 from .moe_oracle import bf16_round, dispatch, gather_rows, router_logits, topk_route
 
 __all__ = ["silu_grad", "renormalised_softmax_grad", "swiglu_expert_backward",
-           "moe_layer_backward"]
+           "moe_layer_backward", "moe_layer_backward_parts"]
 
 
 def _sigmoid(z):
@@ -171,3 +171,99 @@ def moe_layer_backward(x, w_router, bias, w_gate, w_up, w_down, k: int, dout,
     return dict(dx=dx, dw_router=dWr, dbias=db, dw_gate=dWg, dw_up=dWu, dw_down=dWd,
                 dwsh_gate=dWsg, dwsh_up=dWsu, dwsh_down=dWsd, ids=ids, w=w, dw=dw,
                 dlogits_kept=dLk, perm=perm.astype(np.int32), offsets=offsets)
+
+
+def moe_layer_backward_parts(x, w_router, bias, w_gate, w_up, w_down, k: int, dout,
+                             wsh_gate=None, wsh_up=None, wsh_down=None, round_a: bool = True,
+                             logits=None, experts=(), tokens=()) -> dict:
+    """Parts of ``moe_layer_backward`` for layers too large for the whole of it:
+    the same readings and the same steps, restricted to
+      * the router gradients dw_router [E,d] and dbias [E] (whole: they need
+        every token's gate-weight gradient, hence every expert's output rows);
+      * the shared experts' weight gradients (whole);
+      * the routed weight gradients of the experts listed in ``experts``;
+      * dx of the tokens listed in ``tokens``: the input gradients of each
+        token's own k rows (an expert's input gradient of a row depends on
+        that row alone), summed in slot order, plus its router and shared
+        terms.
+    Returns dict(dw_router, dbias, dwsh_gate, dwsh_up, dwsh_down (None without
+    shared experts), dw_gate/dw_up/dw_down: {e: array}, dx [len(tokens), d],
+    tokens, ids, offsets), float64.  Pinned against moe_layer_backward on
+    small layers."""
+    from .moe_oracle import swiglu_expert
+
+    x = np.asarray(x, np.float64)
+    dout = np.asarray(dout, np.float64)
+    T, d = x.shape
+    E = np.asarray(w_gate).shape[0]
+    if logits is None:
+        logits = router_logits(x, w_router, bias)
+    ids, _ = topk_route(logits, k)
+    L = np.asarray(logits, np.float64)
+    kept = np.take_along_axis(L, ids.astype(np.int64), axis=1)
+    z = np.exp(kept - kept[:, :1])
+    w = z / z.sum(axis=1, keepdims=True)          # renormalised softmax, float64
+
+    counts, offsets, perm, inv_perm = dispatch(ids, E)
+    perm = perm.astype(np.int64)
+    inv = inv_perm.astype(np.int64).reshape(T, k)
+    x_sorted = gather_rows(x, perm, k)
+    tok = perm // k
+    w_rows = w.reshape(-1)[perm]
+    dY_sorted = w_rows[:, None] * dout[tok]
+
+    # every expert's output rows, for the gradient of the gate weights
+    y_sorted = np.zeros((perm.size, d), np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            _, y_sorted[r0:r1] = swiglu_expert(x_sorted[r0:r1], w_gate[e], w_up[e], w_down[e],
+                                               round_a)
+    dw = np.einsum("td,tjd->tj", dout, y_sorted[inv])
+    dLk = renormalised_softmax_grad(w, dw)
+    dL = np.zeros((T, E), np.float64)
+    np.put_along_axis(dL, ids.astype(np.int64), dLk, axis=1)
+    Wr = np.asarray(w_router, np.float64)
+    out = dict(dw_router=dL.T @ x, dbias=dL.sum(axis=0), ids=ids, offsets=offsets,
+               dw_gate={}, dw_up={}, dw_down={})
+
+    for e in experts:
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            I = np.asarray(w_gate).shape[1]
+            out["dw_gate"][e] = np.zeros((I, d))
+            out["dw_up"][e] = np.zeros((I, d))
+            out["dw_down"][e] = np.zeros((d, I))
+            continue
+        g = swiglu_expert_backward(x_sorted[r0:r1], w_gate[e], w_up[e], w_down[e],
+                                   dY_sorted[r0:r1], round_a)
+        out["dw_gate"][e], out["dw_up"][e], out["dw_down"][e] = g["dWg"], g["dWu"], g["dWd"]
+
+    tokens = np.asarray(tokens, np.int64)
+    rows = inv[tokens]                             # [n, k] sorted rows of the tokens
+    dX_rows = np.zeros(rows.shape + (d,), np.float64)
+    for e in np.unique(ids[tokens]):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        sel = np.nonzero((rows >= r0) & (rows < r1))
+        rr = rows[sel]
+        g = swiglu_expert_backward(x_sorted[rr], w_gate[e], w_up[e], w_down[e], dY_sorted[rr],
+                                   round_a)
+        dX_rows[sel] = g["dX"]
+    dx = np.zeros((tokens.size, d), np.float64)
+    for j in range(k):
+        dx += dX_rows[:, j]
+    dx += dL[tokens] @ Wr
+
+    out["dwsh_gate"] = out["dwsh_up"] = out["dwsh_down"] = None
+    if wsh_gate is not None and np.asarray(wsh_gate).shape[0] > 0:
+        ns = np.asarray(wsh_gate).shape[0]
+        out["dwsh_gate"] = np.zeros(np.asarray(wsh_gate).shape, np.float64)
+        out["dwsh_up"] = np.zeros_like(out["dwsh_gate"])
+        out["dwsh_down"] = np.zeros(np.asarray(wsh_down).shape, np.float64)
+        for s in range(ns):
+            g = swiglu_expert_backward(x, wsh_gate[s], wsh_up[s], wsh_down[s], dout, round_a)
+            out["dwsh_gate"][s], out["dwsh_up"][s], out["dwsh_down"][s] = g["dWg"], g["dWu"], g["dWd"]
+            dx += g["dX"][tokens]
+    out["dx"] = dx
+    out["tokens"] = tokens
+    return out

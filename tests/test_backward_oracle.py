@@ -145,3 +145,41 @@ def test_silu_grad_closed_form_and_finite_differences():
     eps = 1e-6
     fd = (oracle.silu(z + eps) - oracle.silu(z - eps)) / (2 * eps)
     np.testing.assert_allclose(mb.silu_grad(z), fd, rtol=1e-7, atol=1e-9)
+
+
+@pytest.mark.parametrize("k,ns,round_a", [(2, 1, True), (1, 0, False), (3, 2, True)])
+def test_backward_parts_agree_with_whole_backward(k, ns, round_a):
+    """moe_layer_backward_parts (the restriction used at full size) returns,
+    for the experts and tokens asked for, what the whole backward returns:
+    the router and shared gradients whole, the listed experts' weight
+    gradients (zero for an expert without tokens) and dx of the listed tokens
+    (a token twice, in any order).  Pinned through the whole backward, which
+    the finite-difference pins above tie to the dense forward."""
+    p = _params(40 + k, T=14, d=8, E=6, k=k, I=6, ns=ns)
+    p["bias"] = np.array([2.0, 1.5, 1.0, -1.0, -6.0, -9.0])  # experts 4, 5 get few or none
+    dout = np.random.default_rng(7).normal(size=(14, 8))
+    whole = mb.moe_layer_backward(p["x"], p["w_router"], p["bias"], p["w_gate"], p["w_up"],
+                                  p["w_down"], k, dout, p["wsh_gate"], p["wsh_up"], p["wsh_down"],
+                                  round_a=round_a)
+    counts = np.diff(np.asarray(whole["offsets"]))
+    empty = [int(e) for e in np.nonzero(counts == 0)[0]]
+    assert empty, "the case should leave an expert without tokens"
+    experts = [int(np.argmax(counts)), empty[0], 2]
+    tokens = [13, 0, 5, 5, 9]
+    part = mb.moe_layer_backward_parts(p["x"], p["w_router"], p["bias"], p["w_gate"], p["w_up"],
+                                       p["w_down"], k, dout, p["wsh_gate"], p["wsh_up"],
+                                       p["wsh_down"], round_a=round_a, experts=experts,
+                                       tokens=tokens)
+    close = dict(rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(part["dx"], whole["dx"][tokens], **close)
+    np.testing.assert_allclose(part["dw_router"], whole["dw_router"], **close)
+    np.testing.assert_allclose(part["dbias"], whole["dbias"], **close)
+    for e in experts:
+        for n in ("dw_gate", "dw_up", "dw_down"):
+            np.testing.assert_allclose(part[n][e], whole[n][e], **close)
+    assert np.all(part["dw_gate"][empty[0]] == 0.0)
+    for n in ("dwsh_gate", "dwsh_up", "dwsh_down"):
+        if ns:
+            np.testing.assert_allclose(part[n], whole[n], **close)
+        else:
+            assert part[n] is None and whole[n] is None

@@ -17,6 +17,7 @@ import torch
 
 import expert_routing_grouped_route_amd as moe
 import moe_synth
+import oracle
 from moe_synth import MoEShape
 from oracle import moe_backward as mb
 
@@ -241,3 +242,54 @@ def test_backward_zero_tokens_is_a_no_op():
     torch.cuda.synchronize()
     for t in (dx, dwr, dwg, dwu, dwd):
         assert torch.all(t == 7.0)
+
+
+@pytest.mark.parametrize("name", ["llama4_scout", "prefill_stress"])
+def test_backward_full_size_parts(name):
+    """The two largest layers at full size, in the configuration bench.py
+    times: the Llama-4-Scout shape (8192 tokens, d = 5120, 16 experts top-1 of
+    I = 8192 plus a shared expert; its W_u^T block sits about 1.3 GB past
+    W_g^T) and the prefill shape (32768 tokens, 64 experts top-6, two shared
+    experts; the weight-gradient products reduce over about 400 k columns and
+    the shared ones are split over K).  The whole fp64 backward would take
+    minutes of host time here, so the oracle computes parts of it
+    (moe_layer_backward_parts, pinned against the whole backward): the router
+    gradients and the shared experts' weight gradients whole, the weight
+    gradients of the busiest, the least busy and one random expert (and zeros
+    for an expert without tokens), and dx of 64 random tokens, the first and
+    last token and the least busy expert's tokens."""
+    cfg = moe_synth.CONFIGS[name]
+    c = Case(cfg)
+    L = c.logits()
+    got = c.backward()
+    print(f"[bwd {cfg.name}] GPU done; running the oracle's parts", flush=True)
+    ids, _ = oracle.topk_route(L, cfg.k)
+    counts = np.bincount(ids.ravel(), minlength=cfg.E)
+    nz = np.nonzero(counts)[0]
+    rng = np.random.default_rng(cfg.seed)
+    busiest, least = int(np.argmax(counts)), int(nz[np.argmin(counts[nz])])
+    experts = sorted({busiest, least, int(rng.integers(cfg.E))})
+    least_toks = np.nonzero(np.any(ids == least, axis=1))[0][:8]
+    tokens = np.unique(np.concatenate([rng.choice(cfg.T, 64, replace=False), [0, cfg.T - 1],
+                                       least_toks]))
+    a = c.a
+    ref = mb.moe_layer_backward_parts(a["x"], a["w_router"], a["bias"], a["w_gate"], a["w_up"],
+                                      a["w_down"], cfg.k, c.dout, a["wsh_gate"], a["wsh_up"],
+                                      a["wsh_down"], round_a=True, logits=L, experts=experts,
+                                      tokens=tokens)
+    assert_grad_close(got["dx"][tokens], ref["dx"], f"{name}.dx[{tokens.size} tokens]")
+    if cfg.k > 1:
+        assert_grad_close(got["dw_router"], ref["dw_router"], f"{name}.dw_router")
+        assert_grad_close(got["dbias"], ref["dbias"], f"{name}.dbias")
+    else:  # the kept weight is 1 whatever the logits
+        assert np.all(got["dw_router"] == 0.0) and np.all(got["dbias"] == 0.0)
+    for e in experts:
+        for n in ("dw_gate", "dw_up", "dw_down"):
+            assert_grad_close(got[n][e], ref[n][e], f"{name}.{n}[{e}]")
+    for n in ("dwsh_gate", "dwsh_up", "dwsh_down"):
+        assert_grad_close(got[n], ref[n], f"{name}.{n}")
+    for e in np.nonzero(counts == 0)[0]:
+        for n in ("dw_gate", "dw_up", "dw_down"):
+            assert np.all(got[n][e] == 0.0), (name, n, e)
+    print(f"[bwd {cfg.name}] experts {experts}, {tokens.size} tokens: all within tolerance",
+          flush=True)
