@@ -38,9 +38,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(5):
-        assert moe.moe_status_str(code).startswith(
-            ["MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP"][code])
+    names = ["MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
+             "MOE_ERR_HIP"]
+    for code, name in enumerate(names):
+        assert moe.moe_status_str(code).startswith(name)
     assert moe.moe_status_str(99) == "unknown moe_status_t"
 
 
@@ -271,3 +272,19 @@ def test_backward_validation():
     d0 = dims()
     assert _bwd_call(d0, p, need, wsh_gate=None, wsh_up=None, wsh_down=None, dwsh_gate=None,
                      dwsh_up=None, dwsh_down=None, ws=None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_variant_entry_points_reject_unknown_bits():
+    """Only the documented variant bits are accepted (checked before any launch)."""
+    d = dims()
+    a = layer_args(d)
+    lib = moe.lib()
+    fwd = [ctypes.byref(d), a["x"], a["w_router"], None, a["w_gate"], a["w_up"], a["w_down"],
+           a["wsh_gate"], a["wsh_up"], a["wsh_down"], a["out"], None, None, None, None, None,
+           a["ws"], a["ws_bytes"]]
+    assert lib.moe_layer_fwd_variant(*fwd, moe.MOE_VARIANT_BWD_VALU, 0) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_fwd_variant(*fwd, 8, 0) == moe.MOE_ERR_INVALID_ARG
+    b = Bufs()
+    bwd = [ctypes.byref(d)] + [b() for _ in range(20)] + [1 << 40]
+    assert lib.moe_layer_bwd_variant(*bwd, 4, 0) == moe.MOE_ERR_INVALID_ARG
+

@@ -35,7 +35,7 @@ CASES = {
     "bwd_one_token": MoEShape("bwd_one_token", T=1, d=64, E=8, k=2, I=64, seed=25),
     "bwd_k_equals_E": MoEShape("bwd_k_equals_E", T=70, d=64, E=4, k=4, I=64, seed=26),
     "bwd_fp32_zipf": MoEShape("bwd_fp32_zipf", T=256, d=128, E=16, k=4, I=128, dtype="f32",
-                              seed=28, bias="zipf", zipf_alpha=1.5),
+                              seed=29, bias="zipf", zipf_alpha=2.0),  # 2 experts get no token
 }
 
 GRADS = ("dx", "dw_router", "dbias", "dw_gate", "dw_up", "dw_down", "dwsh_gate", "dwsh_up",
