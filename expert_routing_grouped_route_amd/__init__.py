@@ -23,6 +23,8 @@ MOE_ERR_INVALID_ARG = 1
 MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
+MOE_ERR_SCRATCH = 5
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 
 MOE_VARIANT_GLOBAL_LOADS = 1
 MOE_VARIANT_BWD_VALU = 2
@@ -31,7 +33,7 @@ ENTRY_POINTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispa
                 "moe_grouped_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_fwd_timed",
                 "moe_layer_fwd_overlap", "moe_condensed_workspace_bytes",
                 "moe_layer_fwd_condensed", "moe_backward_workspace_bytes", "moe_layer_bwd",
-                "moe_layer_fwd_variant", "moe_layer_bwd_variant")
+                "moe_layer_fwd_variant", "moe_layer_bwd_variant", "moe_layer_fwd_static")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -84,6 +86,7 @@ _SIGS = {
                                                                    _P]),
     "moe_layer_bwd_variant": (ctypes.c_int, [_DIMS] + [_P] * 20 + [ctypes.c_size_t, ctypes.c_int,
                                                                    _P]),
+    "moe_layer_fwd_static": (ctypes.c_int, [_DIMS] + [_P] * 16),
 }
 
 
@@ -261,3 +264,15 @@ def moe_layer_bwd_variant(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_down
                                      _ptr(dwsh_down), _ptr(ws), int(ws_bytes), int(variant),
                                      _stream(stream))
     _check("moe_layer_bwd_variant", st)
+
+
+def moe_layer_fwd_static(d: moe_dims_t, x, w_router, bias, w_gate, w_up, w_down, wsh_gate,
+                         wsh_up, wsh_down, out, topk_ids_out, topk_w_out, counts_out, offsets_out,
+                         perm_out, stream=None):
+    """moe_layer_fwd on the library's static device scratch (no workspace)."""
+    st = lib().moe_layer_fwd_static(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(bias),
+                                    _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(wsh_gate),
+                                    _ptr(wsh_up), _ptr(wsh_down), _ptr(out), _ptr(topk_ids_out),
+                                    _ptr(topk_w_out), _ptr(counts_out), _ptr(offsets_out),
+                                    _ptr(perm_out), _stream(stream))
+    _check("moe_layer_fwd_static", st)

@@ -2,16 +2,45 @@
 // carving and launch sequencing on the caller's stream.  Declarations and
 // the contract of every entry point are in include/moe.h.
 #include <algorithm>
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "moe.h"
 #include "common.h"
 #include "kernels.h"
 #include "backward.h"
 
+// The workspace of moe_layer_fwd_static, for callers that cannot allocate:
+// one copy per GPU, alive until the process ends.  Host code never passes
+// this name to a kernel (on the host it is only a stand-in for the symbol);
+// it uses the device address static_scratch() looked up for the device.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace moe;
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current; null if the lookup fails.
+void* static_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex lock;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> guard(lock);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    addr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
 
 constexpr int64_t kI32Limit = int64_t(1) << 31;
 
@@ -550,6 +579,9 @@ const char* moe_status_str(moe_status_t status) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: sizes outside the supported limits";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_bytes()";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    case MOE_ERR_SCRATCH:
+      return "MOE_ERR_SCRATCH: these sizes need more workspace than moe_layer_fwd_static's "
+             "static scratch (MOE_STATIC_SCRATCH_BYTES) holds; use moe_layer_fwd with a workspace";
   }
   return "unknown moe_status_t";
 }
@@ -683,6 +715,23 @@ moe_status_t moe_layer_fwd(const moe_dims_t* dims, const void* x, const void* w_
                            int32_t* perm_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   return layer_fwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down, out,
                    topk_ids_out, topk_w_out, counts_out, offsets_out, perm_out, ws, ws_bytes,
+                   nullptr, 0, stream);
+}
+
+moe_status_t moe_layer_fwd_static(const moe_dims_t* dims, const void* x, const void* w_router,
+                                  const float* bias, const void* w_gate, const void* w_up,
+                                  const void* w_down, const void* wsh_gate, const void* wsh_up,
+                                  const void* wsh_down, float* out, int32_t* topk_ids_out,
+                                  float* topk_w_out, int32_t* counts_out, int32_t* offsets_out,
+                                  int32_t* perm_out, hipStream_t stream) {
+  const moe_status_t st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const size_t need = layout_of(*dims).total;
+  if (need > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = static_scratch();
+  if (!ws) return MOE_ERR_HIP;
+  return layer_fwd(dims, x, w_router, bias, w_gate, w_up, w_down, wsh_gate, wsh_up, wsh_down, out,
+                   topk_ids_out, topk_w_out, counts_out, offsets_out, perm_out, ws, need,
                    nullptr, 0, stream);
 }
 

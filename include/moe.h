@@ -77,7 +77,9 @@ typedef enum {
   MOE_ERR_INVALID_ARG = 1, /* null, misaligned or overlapping pointer; bad sizes */
   MOE_ERR_UNSUPPORTED = 2, /* sizes outside the limits above */
   MOE_ERR_WORKSPACE = 3,   /* ws_bytes below moe_workspace_bytes() */
-  MOE_ERR_HIP = 4          /* a kernel launch failed */
+  MOE_ERR_HIP = 4,         /* a kernel launch failed */
+  MOE_ERR_SCRATCH = 5      /* moe_layer_fwd_static: the sizes need more workspace
+                              than MOE_STATIC_SCRATCH_BYTES */
 } moe_status_t;
 
 /* Sizes of one layer call: T tokens, hidden size d, E routed experts, top-k,
@@ -203,6 +205,34 @@ MOE_API moe_status_t moe_layer_fwd_variant(const moe_dims_t* dims, const void* x
                                            int32_t* counts_out, int32_t* offsets_out,
                                            int32_t* perm_out, void* ws, size_t ws_bytes,
                                            int variant, hipStream_t stream);
+
+/* Bytes of the device scratch array behind moe_layer_fwd_static (one per GPU). */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_layer_fwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The workspace is a
+ * file-scope device array of MOE_STATIC_SCRATCH_BYTES (64 MiB) in the library,
+ * one per GPU, held from the first call on that GPU until the process ends;
+ * the call makes no hipMalloc, hipFree or other allocating call.
+ *   Sizes: moe_workspace_bytes(dims) must be at most MOE_STATIC_SCRATCH_BYTES,
+ *     else MOE_ERR_SCRATCH and nothing is enqueued (e.g. 4096 tokens of d =
+ *     2048, 64 experts top-6 of I = 1408 need about 320 MB: too many; the
+ *     same layer fits up to about 800 tokens).
+ *   Every call on one GPU shares that GPU's array and leaves its last
+ *   contents there (every part is written before it is read, so no clearing is
+ *   needed): calls that may overlap on one GPU (other streams, other host
+ *   threads) race and must be serialised by the caller.
+ * All other arguments, results, errors and the asynchrony are those of
+ * moe_layer_fwd. */
+MOE_API moe_status_t moe_layer_fwd_static(const moe_dims_t* dims, const void* x,
+                                          const void* w_router, const float* bias,
+                                          const void* w_gate, const void* w_up,
+                                          const void* w_down, const void* wsh_gate,
+                                          const void* wsh_up, const void* wsh_down, float* out,
+                                          int32_t* topk_ids_out, float* topk_w_out,
+                                          int32_t* counts_out, int32_t* offsets_out,
+                                          int32_t* perm_out, hipStream_t stream);
 
 /* moe_layer_fwd that also records HIP events on `stream` at its stage
  * boundaries, for per-stage timing.  events[0..n_events) are caller-created

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     names = ["MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
-             "MOE_ERR_HIP"]
+             "MOE_ERR_HIP", "MOE_ERR_SCRATCH"]
     for code, name in enumerate(names):
         assert moe.moe_status_str(code).startswith(name)
     assert moe.moe_status_str(99) == "unknown moe_status_t"
@@ -288,3 +288,15 @@ def test_variant_entry_points_reject_unknown_bits():
     bwd = [ctypes.byref(d)] + [b() for _ in range(20)] + [1 << 40]
     assert lib.moe_layer_bwd_variant(*bwd, 4, 0) == moe.MOE_ERR_INVALID_ARG
 
+
+def test_static_layer_refuses_sizes_beyond_its_scratch():
+    """moe_layer_fwd_static checks the workspace its sizes need against the
+    static scratch before touching the device (no GPU needed to refuse)."""
+    lib = moe.lib()
+    big = moe.dims(4096, 2048, 64, 6, 1408, 2, 1408, "bf16")
+    assert moe.moe_workspace_bytes(big) > moe.MOE_STATIC_SCRATCH_BYTES
+    b = Bufs()
+    args = [ctypes.byref(big)] + [b() for _ in range(15)] + [0]
+    assert lib.moe_layer_fwd_static(*args) == moe.MOE_ERR_SCRATCH
+    bad = moe.dims(16, 100, 4, 2, 64)  # d not a multiple of 64
+    assert lib.moe_layer_fwd_static(ctypes.byref(bad), *args[1:]) == moe.MOE_ERR_UNSUPPORTED
