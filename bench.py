@@ -122,6 +122,153 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib, workload, command):
     print(path)
 
 
+# kernels of the layer path by role (regular expressions on demangled names)
+KERNEL_ROLES = (
+    ("route", r"route_bf16_kernel|route_f32_kernel"),
+    ("dispatch_count", r"dispatch_count_kernel"),
+    ("dispatch_rank", r"dispatch_rank_kernel"),
+    ("gather", r"gather_rows_kernel"),
+    ("gate_up", r"grouped_gemm_bf16_kernel<true"),
+    ("down", r"grouped_gemm_bf16_kernel<false"),
+    ("combine", r"combine_k_kernel|combine_kernel"),
+)
+SIMD_NUM = 1024  # MI355X: 256 CUs x 4 SIMDs
+
+
+def kernel_role(name):
+    for role, rx in KERNEL_ROLES:
+        if re.search(rx, name):
+            return role
+    return None
+
+
+def algorithmic_bytes(cfg, counts):
+    """(read, write) bytes each kernel of the layer path has to move at the
+    least: every input it needs read once, every output written once.  The
+    gate/up kernel reads each routed assignment's token row once (R rows) and
+    only the weights of experts that received tokens; the gather (standalone
+    dispatch) reads x once."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    T, d, E, k, I, ns, Is = cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.I_shared
+    R = T * k
+    nz = int(sum(1 for c in counts if c > 0))
+    return {
+        "route": (T * d * es + E * d * es + E * 4, R * 8),
+        "dispatch_count": (R * 4, 0),
+        "dispatch_rank": (R * 4, R * 8 + (2 * E + 1) * 4),
+        "gather": (T * d * es + R * 4, R * d * es),
+        "gate_up": (nz * 2 * I * d * es + ns * 2 * Is * d * es + R * d * es + (T * d * es if ns else 0),
+                    R * I * es + T * ns * Is * es),
+        "down": (nz * d * I * es + ns * d * Is * es + R * I * es + T * ns * Is * es,
+                 R * d * 4 + (T * d * 4 if ns else 0)),
+        "combine": (R * d * 4 + R * 8 + (T * d * 4 if ns else 0), T * d * 4),
+    }
+
+
+def _counter_rows(csv_path):
+    with open(csv_path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_counters(trace_csv, counter_csvs, bench_log, copy_mib, workload, command):
+    """Per-kernel table of the layer path from one kernel-trace run and
+    counter runs (rocprofv3 CSV): average duration (trace), HBM-side bytes
+    from FETCH_SIZE and WRITE_SIZE (KiB per dispatch, each scaled by what it
+    reads for the copy_mib MiB device copy at the end of its run) against the
+    algorithmic bytes, the MFMA utilisation (MfmaUtil: MFMA-busy cycles over
+    GUI-active cycles x SIMDs), the MFMA work executed (bf16 MOPS x 512) and
+    the clock (GUI-active cycles over the traced duration).  Writes
+    profiles/counters_<workload>.md."""
+    import moe_synth
+    cfg = moe_synth.CONFIGS[workload]
+    info = None
+    for line in open(bench_log):
+        if line.startswith("{"):
+            info = json.loads(line)
+    counts = info["counts"]
+    last = int(info["profile_steps"])  # the profiled calls: the last ones of each kernel
+    alg = algorithmic_bytes(cfg, counts)
+    fl_gu, fl_dn = gemm_flops(cfg)
+    flops = {"gate_up": fl_gu, "down": fl_dn}
+    # durations per role from the kernel trace
+    dur = {}
+    for r in _counter_rows(trace_csv):
+        role = kernel_role(r["Kernel_Name"])
+        if role:
+            dur.setdefault(role, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    vals = {}   # role -> counter -> [per-dispatch values]
+    copy = {}   # counter -> KiB read for the calibration copy
+    for path in counter_csvs:
+        rows = _counter_rows(path)
+        last = max((int(r["Dispatch_Id"]) for r in rows if kernel_role(r["Kernel_Name"])), default=-1)
+        for r in rows:
+            role = kernel_role(r["Kernel_Name"])
+            name, v = r["Counter_Name"], float(r["Counter_Value"])
+            if role:
+                vals.setdefault(role, {}).setdefault(name, []).append(v)
+            elif "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) > last:
+                copy[name] = copy.get(name, 0.0) + v
+    scale = {n: copy_mib * 1024.0 / copy[n] for n in ("FETCH_SIZE", "WRITE_SIZE") if copy.get(n)}
+    mean = lambda xs: sum(xs[-last:]) / len(xs[-last:])
+    table = {}
+    for role, _ in KERNEL_ROLES:
+        if role not in dur:
+            continue
+        us = mean(dur[role]) / 1e3
+        c = {n: mean(v) for n, v in vals.get(role, {}).items()}
+        rd, wr = alg[role]
+        e = {"calls": min(last, len(dur[role])), "avg_us": round(us, 2),
+             "alg_read_MB": round(rd / 1e6, 2), "alg_write_MB": round(wr / 1e6, 2),
+             "alg_GB/s": round((rd + wr) / (us * 1e-6) / 1e9, 1)}
+        if "FETCH_SIZE" in c and "FETCH_SIZE" in scale:
+            f = c["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
+            e["fetch_MB"] = round(f / 1e6, 2)
+            e["fetch_over_alg_read"] = round(f / rd, 3) if rd else None
+        if "WRITE_SIZE" in c and "WRITE_SIZE" in scale:
+            w = c["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
+            e["write_MB"] = round(w / 1e6, 2)
+            e["write_over_alg_write"] = round(w / wr, 3) if wr else None
+        if "fetch_MB" in e and "write_MB" in e:
+            e["traffic_GB/s"] = round((e["fetch_MB"] + e["write_MB"]) * 1e6 / (us * 1e-6) / 1e9, 1)
+        if "MfmaUtil" in c:
+            e["mfma_util_pct"] = round(c["MfmaUtil"], 1)
+        if "GRBM_GUI_ACTIVE" in c:  # summed over the 8 XCDs
+            e["clock_GHz"] = round(c["GRBM_GUI_ACTIVE"] / 8 / (us * 1e3), 3)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c and role in flops:
+            ex = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            e["mfma_flop_executed_over_alg"] = round(ex / flops[role], 3)
+        if role in flops:
+            e["alg_TFLOP/s"] = round(flops[role] / (us * 1e-6) / 1e12, 1)
+            e["frac_bf16_peak"] = round(flops[role] / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        for n in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY",
+                  "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES", "TCC_HIT_sum", "TCC_MISS_sum",
+                  "TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_DRAM_sum"):
+            if n in c:
+                e[n] = c[n]
+        table[role] = e
+    rec = {"workload": workload, "copy_calibration_mib": copy_mib, "scale": scale,
+           "kernel_source_sha": gemm_source_sha(), "kernels": table}
+    path = os.path.join(PROFILES, f"counters_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write(f"# Counters of the layer path, {workload}\n\n")
+        fh.write("Commands (from the repository root; one counter set per run):\n\n")
+        for cmd in command:
+            fh.write(f"    {cmd}\n")
+        fh.write("\nDurations from the kernel trace. FETCH_SIZE and WRITE_SIZE (KiB per dispatch) "
+                 "are scaled by the copy size over what each counter reads for the "
+                 f"{copy_mib} MiB device copy at the end of its run; `alg` bytes are what the "
+                 "kernel has to move at the least. MfmaUtil is MFMA-busy cycles over "
+                 "GUI-active cycles times the 1024 SIMDs; clock = GUI-active cycles (summed over the 8 XCDs) / 8 / duration.\n\n")
+        cols = ["calls", "avg_us", "alg_read_MB", "fetch_MB", "fetch_over_alg_read", "alg_write_MB",
+                "write_MB", "alg_GB/s", "traffic_GB/s", "mfma_util_pct", "clock_GHz",
+                "frac_bf16_peak", "mfma_flop_executed_over_alg"]
+        fh.write("| kernel | " + " | ".join(cols) + " |\n|" + "---|" * (len(cols) + 1) + "\n")
+        for role, e in table.items():
+            fh.write(f"| {role} | " + " | ".join(str(e.get(k_, "")) for k_ in cols) + " |\n")
+        fh.write("\n```json\n" + json.dumps(rec, indent=1) + "\n```\n")
+    print(path)
+
+
 def kernel_label(name, limit=120):
     """Demangled kernel name without return type, anonymous namespace and
     arguments, cut to `limit` characters."""
@@ -441,6 +588,45 @@ def quick_workload(cfg, args):
                          "bytes": sb[s_]} for s_ in sb}}
 
 
+def profile_run(cfg, args, d, dev, wdt, out, ws, ws_bytes, stream):
+    """A short run for counter collection: 0.2 s of untimed layer calls, then
+    args.profile_steps calls of moe_layer_fwd and of the standalone
+    moe_dispatch (row gather included), then the copy calibration if asked.
+    Prints the expert counts (for the algorithmic bytes) as one JSON line."""
+    import torch
+
+    import expert_routing_grouped_route_amd as moe
+
+    lay = (d, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"], dev["w_down"],
+           dev["wsh_gate"], dev["wsh_up"], dev["wsh_down"], out)
+    R = cfg.T * cfg.k
+    ids = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < 0.2:
+        moe.moe_layer_fwd(*lay, ids, None, cnt, None, None, ws, ws_bytes, stream)
+        torch.cuda.synchronize()
+    i32 = lambda *sh: torch.empty(sh, dtype=torch.int32, device="cuda")
+    d_cnt, d_off, d_perm, d_inv = i32(cfg.E), i32(cfg.E + 1), i32(R), i32(R)
+    x_sorted = torch.empty(R, cfg.d, dtype=wdt, device="cuda")
+    print(f"[bench] profiling {args.profile_steps} calls of moe_layer_fwd and moe_dispatch",
+          file=sys.stderr, flush=True)
+    for _ in range(args.profile_steps):
+        moe.moe_layer_fwd(*lay, None, None, None, None, None, ws, ws_bytes, stream)
+    for _ in range(args.profile_steps):
+        moe.moe_dispatch(d, dev["x"], ids, d_cnt, d_off, d_perm, d_inv, x_sorted, ws, ws_bytes,
+                         stream)
+    torch.cuda.synchronize()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    print(json.dumps({"workload": cfg.name, "profile_steps": args.profile_steps,
+                      "counts": cnt.cpu().tolist()}), flush=True)
+
+
 def main():
     import moe_synth
 
@@ -470,9 +656,20 @@ def main():
     ap.add_argument("--bench-log", help="bench.py output of the profiled run (for --summarize-stats)")
     ap.add_argument("--summary-part", default="layer", choices=("layer", "backward"),
                     help="which summary --summarize-stats writes")
+    ap.add_argument("--profile-steps", type=int, default=0, metavar="N",
+                    help="profiling run: after a short warm-up, N calls of moe_layer_fwd and N "
+                         "of the standalone moe_dispatch, then the copy calibration if asked; "
+                         "prints the expert counts as JSON and skips every timing pass")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="write profiles/counters_<workload>.md from a kernel-trace CSV followed "
+                         "by counter-collection CSVs (needs --bench-log of the profiling run)")
     ap.add_argument("--command", action="append", default=[],
                     help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1:], args.bench_log,
+                           args.copy_calibration_mib, args.workload, args.command)
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.copy_calibration_mib, args.workload, args.command)
         return
@@ -504,6 +701,10 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     out = torch.empty(cfg.T, cfg.d, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+
+    if args.profile_steps:
+        profile_run(cfg, args, d, dev, wdt, out, ws, ws_bytes, stream)
+        return
 
     n_ev = 6
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]

@@ -18,7 +18,8 @@
 //           across waves from LDS counts; writes perm and inv_perm.  Block 0
 //           also writes counts, offsets and the M-tile table of the grouped
 //           GEMMs (M-tile prefix per expert and the expert of every M-tile).
-//   gather: one wave per sorted row, 16-byte vector copies of the token row
+//   scatter: one wave per token reads its row once (16-byte vectors) and
+//           writes it to the sorted rows of its k assignments
 #include "common.h"
 #include "kernels.h"
 
@@ -182,20 +183,50 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(
   }
 }
 
-// x_sorted[i] = x[perm[i] / k], one wave per row, 16-byte vectors.
-__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ x,
-                                                          const int32_t* __restrict__ perm,
-                                                          const int32_t* __restrict__ total_ptr,
-                                                          int k, int T, int vec_per_row,
-                                                          u32x4* __restrict__ xs) {
+// x_sorted[inv_perm[t*k + j]] = x[t] for every assignment with a valid expert:
+// one wave per token reads the row once, 16-byte vectors, up to four per lane
+// in flight, and writes it to its k sorted rows (so x is read once rather than
+// k times).  Assignments whose id is outside [0,E) have no row and are
+// skipped; a row index past the total is never written.
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const u32x4* __restrict__ x,
+                                                           const int32_t* __restrict__ ids,
+                                                           const int32_t* __restrict__ inv_perm,
+                                                           const int32_t* __restrict__ total_ptr,
+                                                           int T, int k, int E, int vec_per_row,
+                                                           u32x4* __restrict__ xs) {
   const int total = *total_ptr;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int i = blockIdx.x * 4 + wave; i < total; i += gridDim.x * 4) {
-    const int tok = perm[i] / k;
-    if ((unsigned)tok >= (unsigned)T) continue;
-    const u32x4* src = x + (size_t)tok * vec_per_row;
-    u32x4* dst = xs + (size_t)i * vec_per_row;
-    for (int c = lane; c < vec_per_row; c += 64) dst[c] = src[c];
+  for (int t = blockIdx.x * 4 + wave; t < T; t += gridDim.x * 4) {
+    int dst[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      dst[j] = -1;
+      if (j < k) {
+        const size_t a = (size_t)t * k + j;
+        const int e = ids[a];
+        const int r = (unsigned)e < (unsigned)E ? inv_perm[a] : -1;
+        dst[j] = (unsigned)r < (unsigned)total ? r : -1;
+      }
+    }
+    const u32x4* src = x + (size_t)t * vec_per_row;
+    for (int c0 = 0; c0 < vec_per_row; c0 += 256) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < vec_per_row) v[u] = src[c];
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (dst[j] < 0) continue;
+        u32x4* out = xs + (size_t)dst[j] * vec_per_row;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < vec_per_row) out[c] = v[u];
+        }
+      }
+    }
   }
 }
 
@@ -212,12 +243,12 @@ void launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
                      (int)R, a.E, chunk, a.rep, a.k, a.blk, nblk, a.counts, a.offsets, a.tiles, a.ctr, a.perm,
                      a.inv_perm);
   if (nblk == 0) return;
-  if (a.x_sorted) {
+  if (a.x_sorted) {  // (never asked for together with token condensation)
     const int vec = (int)((size_t)a.d * a.elem_bytes / 16);
-    const int64_t grid = (R + 3) / 4;
-    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)grid), block, 0, stream,
-                       static_cast<const u32x4*>(a.x), a.perm, a.offsets + a.E, a.k, (int)a.T, vec,
-                       static_cast<u32x4*>(a.x_sorted));
+    const int64_t grid = (a.T + 3) / 4;
+    hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)grid), block, 0, stream,
+                       static_cast<const u32x4*>(a.x), a.ids, a.inv_perm, a.offsets + a.E,
+                       (int)a.T, a.k, a.E, vec, static_cast<u32x4*>(a.x_sorted));
   }
 }
 

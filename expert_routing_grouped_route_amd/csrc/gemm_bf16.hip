@@ -32,11 +32,12 @@
 // conflicts.  The gate/up epilogue stores from registers; the down epilogue
 // stages its fp32 tile through LDS and stores whole rows.
 //
-// Work order: the routed tiles of expert 0, 1, ... (within an expert n-tile
-// outer, m-tile inner, so consecutive tiles share a weight slice), then the
-// shared experts' tiles (for the down product the shared tiles come first,
-// being the longest); the expert of a routed tile is one lookup in the tile
-// table the dispatch scan wrote.
+// Work order: the routed tiles of expert 0, 1, ... (within an expert groups of
+// 4 m-tiles, n-tile outer and m-tile inner within a group), then the shared
+// experts' tiles in the same raster (for the down product the shared tiles
+// come first, being the longest); the expert of a routed tile is one lookup in
+// the tile table the dispatch scan wrote.  Each XCD takes runs of 8
+// consecutive works, which share A-row tiles and weight slices in its L2.
 #include <algorithm>
 #include <type_traits>
 
@@ -65,7 +66,8 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int XLOADS = kBM / 8 / NWAVES;        // 1 KB direct loads per wave per stage: 4 of X
 constexpr int WLOADS = BN / 8 / NWAVES;         // and 4 of weights
 constexpr int LOADS = XLOADS + WLOADS;          // 8
-constexpr int XCD_RUN = 8;                      // consecutive work indices per XCD
+constexpr int XCD_RUN = 8;                      // consecutive works per XCD run
+constexpr int GROUP_M = 4;                      // m-tiles per group of the tile raster
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 
@@ -89,17 +91,29 @@ __device__ __forceinline__ void block_barrier() {
 // s_waitcnt vmcnt(0) lgkmcnt(0) (gfx9 encoding; expcnt untouched).
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x70); }
 
-// Routed tile t (experts in order; within an expert n-tile outer, m-tile
-// inner) -> expert e, m-tile m, n-tile n.  The expert comes from the tile
-// table: t / nt lies in the expert's M-tile range.
+// Tile l of an mt x nt grid in raster order: groups of GROUP_M m-tiles, and
+// within a group n-tile outer, m-tile inner.  So a run of 8 consecutive
+// tiles of a large expert spans 4 m-tiles (A rows) and 2 n-tiles (weight
+// slices): 6 operand tiles for 8 output tiles, where a run along one n-tile
+// would need 9.
+__device__ __forceinline__ void raster(int l, int mt, int nt, int& m, int& n) {
+  const int gsize = GROUP_M * nt;
+  const int q = l / gsize, r = l - q * gsize;
+  const int gm = min(GROUP_M, mt - q * GROUP_M);
+  n = r / gm;
+  m = q * GROUP_M + (r - n * gm);
+}
+
+// Routed tile t (experts in order; within an expert the raster above) ->
+// expert e, m-tile m, n-tile n.  An expert's tiles are [m0 * nt, (m0 + mt) *
+// nt) for its M-tile range [m0, m0 + mt), so the tile table's entry t / nt
+// names the expert.
 __device__ __forceinline__ void routed_decode(const FfnArgs& p, const GemmGrid& g, int t, int& e,
                                               int& m, int& n) {
   e = p.tile_off[p.E + 1 + t / g.nt_r];
   const int m0 = p.tile_off[e];
   const int mt = p.tile_off[e + 1] - m0;
-  const int local = t - m0 * g.nt_r;
-  n = local / mt;
-  m = local - n * mt;
+  raster(t - m0 * g.nt_r, mt, g.nt_r, m, n);
 }
 
 struct BTile {
@@ -147,8 +161,9 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
   } else {
     const int sb = L - n_routed;
     const int per_s = g.mt_s * g.nt_s;
-    const int s = sb / per_s, rem = sb - s * per_s;
-    const int n = rem / g.mt_s, m = rem - n * g.mt_s;
+    const int s = sb / per_s;
+    int m, n;
+    raster(sb - s * per_s, g.mt_s, g.nt_s, m, n);
     const int r0 = m * kBM;
     t.rows = (int)min((int64_t)kBM, p.T - r0);
     t.X = static_cast<const uint8_t*>(p.x) + (size_t)r0 * p.d * 2;
@@ -192,9 +207,8 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     t.w_seg = parts > 1 ? (size_t)p.w_part * 2 : 0;
     t.Out = reinterpret_cast<uint8_t*>(p.y + (size_t)r0 * p.d + (size_t)n * BN);
   } else {
-    const int sb = L - n_routed;
-    n = sb / g.mt_s;
-    const int m = sb - n * g.mt_s;
+    int m;
+    raster(L - n_routed, g.mt_s, g.nt_r, m, n);
     r0 = m * kBM;
     t.rows = (int)min((int64_t)kBM, p.T - r0);
     const size_t ld = (size_t)p.ns * p.Is;
@@ -311,67 +325,75 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // One K-step.  The deep operand (three buffers) is loaded two steps ahead,
-  // the other (two buffers) one step ahead; during step kt this wave issues
-  // the shallow loads of step kt+1 first (MS), then the deep loads of step
-  // kt+2 (MD), spread between its MFMAs.  WD: the deep loads of step kt+1 may
-  // still be in flight at the top of step kt.
+  // K loop.  The A rows are loaded into three buffers, the weight rows into
+  // two.  The block barrier that makes step kt+1's operands visible to every
+  // wave sits inside step kt, before its last 8 MFMAs: each wave first waits
+  // for its own loads of step kt+1 and for its fragment reads of step kt, then
+  // passes the barrier, issues the fragment reads of step kt+1's first
+  // sub-step, and only then runs step kt's last MFMAs, which cover the
+  // barrier's skew and the LDS read latency.  Past that barrier every read of
+  // step kt is done, so step kt's buffers take the next loads at once.  Loads
+  // issued in step kt, two per sub-step between the MFMAs:
+  //   sub-step 0: weight rows of step kt+1, second half;
+  //   sub-steps 1, 2: A rows of step kt+2;
+  //   sub-step 3 (after the barrier): weight rows of step kt+2, first half.
+  // So a weight load has three to four sub-steps to land and an A-row load
+  // five to six.
+  // MS: there is a step kt+1 (its loads, the barrier, its first reads);
+  // MD: there is a step kt+2 (its loads).
   // XL: this wave's 32 A rows hold valid rows, so it loads them; MM: its 128
   // output rows hold valid rows, so it computes.  Rows past the tile's valid
   // ones cost neither loads nor, in 128-row halves, matrix-core time.
-  constexpr int NS_LOADS = DEEP_X ? WLOADS : XLOADS;  // shallow loads per wave and step
-  auto step = [&](int kt, auto ms_c, auto md_c, auto wd_c, auto xl_c, auto mm_c) {
-    constexpr bool MS = decltype(ms_c)::value;
-    constexpr bool MD = decltype(md_c)::value;
-    constexpr bool WD = decltype(wd_c)::value;
-    constexpr bool XL = decltype(xl_c)::value;
-    constexpr bool MM = decltype(mm_c)::value;
-    constexpr int NDEEP = DEEP_X ? (XL ? XLOADS : 0) : WLOADS;  // this wave's deep loads per step
-    const size_t wnext = (DEEP_X ? MS : MD) ? w_step(kt + (DEEP_X ? 1 : 2)) : 0;
-    if (WD) __builtin_amdgcn_s_waitcnt((NDEEP & 0xF) | (0x7 << 4));  // vmcnt(NDEEP) lgkmcnt(0)
-    else wait_all_loads();
-    block_barrier();  // everyone's loads of step kt have landed; step kt-1's buffers are free
+  static_assert(DEEP_X && XLOADS == 4 && WLOADS == 4, "the K loop's load slots");
+  bf16x8 F[2][6];
+  auto rd = [&](int kt, int ks, bf16x8 (&f)[6]) {
     const uint8_t* xs_ = smem + (kt % NXB) * X_BYTES;
     const uint8_t* ws_ = smem + W_BASE + (kt % NWB) * W_BYTES;
-    bf16x8 F[2][6];
-    auto rd = [&](int ks, bf16x8 (&f)[6]) {
-      const int c = (((ks * 2 + kg) ^ cx) << 4);
+    const int c = (((ks * 2 + kg) ^ cx) << 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = as_bf16x8(ld_u32x4(xs_ + a_off[i] + c));
+    for (int i = 0; i < 4; ++i) f[i] = as_bf16x8(ld_u32x4(xs_ + a_off[i] + c));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) f[4 + j] = as_bf16x8(ld_u32x4(ws_ + b_off[j] + c));
-    };
-    if (MM) rd(0, F[0]);
-    __builtin_amdgcn_sched_barrier(0);  // sub-step 0's reads issue before any prefetch
+    for (int j = 0; j < 2; ++j) f[4 + j] = as_bf16x8(ld_u32x4(ws_ + b_off[j] + c));
+  };
+  auto step = [&](int kt, auto ms_c, auto md_c, auto xl_c, auto mm_c) {
+    constexpr bool MS = decltype(ms_c)::value;
+    constexpr bool MD = decltype(md_c)::value;
+    constexpr bool XL = decltype(xl_c)::value;
+    constexpr bool MM = decltype(mm_c)::value;
+    // loads this wave may still have in flight at step kt+1's barrier: the A
+    // rows of step kt+2
+    constexpr int PENDING = MD && XL ? XLOADS : 0;
+    const size_t w1 = MS ? w_step(kt + 1) : 0;
+    const size_t w2 = MD ? w_step(kt + 2) : 0;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      if (ks == 3 && MS) {
+        __builtin_amdgcn_s_waitcnt(PENDING | (0x7 << 4));  // vmcnt(PENDING) lgkmcnt(0)
+        block_barrier();  // step kt+1's operands are in LDS; every read of step kt is done
+        if (MM) rd(kt + 1, 0, F[0]);
+      }
       if (MM) {
-        if (ks < 3) rd(ks + 1, F[(ks + 1) & 1]);
+        if (ks < 3) rd(kt, ks + 1, F[(ks + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = mfma_32x32x16_bf16(F[ks & 1][4 + j], F[ks & 1][i], acc[i][j]);
       }
-      // sub-steps 0, 1: the shallow loads; 2, 3: the deep loads (two each)
       bool has[2] = {false, false};
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int q = (ks & 1) * 2 + u;
-        if (ks < 2) {
-          if (MS) {
-            if (DEEP_X) { issue_w(kt + 1, wnext, q); has[u] = true; }
-            else if (XL) { issue_x(kt + 1, q); has[u] = true; }
-          }
-        } else {
-          if (MD) {
-            if (DEEP_X) { if (XL) { issue_x(kt + 2, q); has[u] = true; } }
-            else { issue_w(kt + 2, wnext, q); has[u] = true; }
-          }
+        if (ks == 0) {
+          if (MS) { issue_w(kt + 1, w1, 2 + u); has[u] = true; }
+        } else if (ks < 3) {
+          if (MD && XL) { issue_x(kt + 2, (ks - 1) * 2 + u); has[u] = true; }
+        } else if (MD) {
+          issue_w(kt + 2, w2, u);
+          has[u] = true;
         }
       }
       if (MM) {
-        if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        if (ks < 3 || MS) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -384,27 +406,37 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   const int nk = t.nk;
   auto k_loop = [&](auto xl_c, auto mm_c) {
     constexpr bool XL = decltype(xl_c)::value;
+    constexpr bool MM = decltype(mm_c)::value;
     using T_ = std::true_type;
     using F_ = std::false_type;
-    // prologue: shallow loads of step 0, deep loads of steps 0 and 1 (last)
+    // prologue: the weight and A rows of step 0, then the A rows of step 1 and
+    // the first half of its weight rows
 #pragma unroll
-    for (int q = 0; q < NS_LOADS; ++q) {
-      if (DEEP_X) issue_w(0, 0, q);
-      else if (XL) issue_x(0, q);
+    for (int q = 0; q < WLOADS; ++q) issue_w(0, 0, q);
+#pragma unroll
+    for (int q = 0; q < XLOADS; ++q)
+      if (XL) issue_x(0, q);
+    if (nk >= 2) {
+#pragma unroll
+      for (int q = 0; q < XLOADS; ++q)
+        if (XL) issue_x(1, q);
+      const size_t w1 = w_step(1);
+      issue_w(1, w1, 0);
+      issue_w(1, w1, 1);
     }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      if (s2 == 1 && nk < 2) break;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (DEEP_X) { if (XL) issue_x(s2, q); }
-        else issue_w(s2, w_step(s2), q);
-      }
+    // step 0's operands: only the loads of step 1 may still be in flight
+    if (nk >= 2) {
+      if (XL) __builtin_amdgcn_s_waitcnt((XLOADS + 2) | (0x7 << 4));  // vmcnt(6) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(2 | (0x7 << 4));                // vmcnt(2) lgkmcnt(0)
+    } else {
+      wait_all_loads();
     }
+    block_barrier();
+    if (MM) rd(0, 0, F[0]);
     int kt = 0;
-    for (; kt + 2 < nk; ++kt) step(kt, T_{}, T_{}, T_{}, xl_c, mm_c);
-    if (kt + 1 < nk) { step(kt, T_{}, F_{}, T_{}, xl_c, mm_c); ++kt; }
-    step(kt, F_{}, F_{}, F_{}, xl_c, mm_c);
+    for (; kt + 2 < nk; ++kt) step(kt, T_{}, T_{}, xl_c, mm_c);
+    if (kt + 1 < nk) { step(kt, T_{}, F_{}, xl_c, mm_c); ++kt; }
+    step(kt, F_{}, F_{}, xl_c, mm_c);
   };
   const bool mm = wm * 128 < t.rows;  // wave-uniform
   if (wave * (8 * XLOADS) < t.rows) k_loop(std::true_type{}, std::true_type{});
@@ -505,12 +537,16 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   }
 }
 
-// Launch slot -> work index: blocks are dealt to the 8 XCDs round-robin, so
-// slot b runs on XCD b % 8; each XCD receives runs of XCD_RUN consecutive work
-// indices, tiles that share weight slices, in its own L2.
-__device__ __forceinline__ int xcd_remap(int bid) {
-  const int run = 8 * XCD_RUN;
-  const int base = bid / run * run, w = bid - base;
+// Launch slot -> work index.  Blocks are dealt to the 8 XCDs round-robin, so
+// slot b runs on XCD b % 8; within each group of 64 slots XCD x receives the
+// run of XCD_RUN consecutive works 8x .. 8x + 7, neighbours in the raster that
+// share A rows and weight slices in its L2.  Longer runs (32 works, one per CU
+// of an XCD) halve the L2 misses again but leave the XCDs unevenly loaded
+// where tile costs differ (shared-expert tiles, ragged last M-tiles), which
+// measured slower.
+__device__ __forceinline__ int slot_work(int b) {
+  constexpr int RUN = 8 * XCD_RUN;
+  const int base = b / RUN * RUN, w = b - base;
   return base + (w & 7) * XCD_RUN + (w >> 3);
 }
 
@@ -524,7 +560,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, 
   const int n_routed = p.part == kSharedTiles ? 0 : p.tile_off[p.E] * g.nt_r;
   const int ns_t = p.part == kRoutedTiles ? 0 : g.n_shared;
   const int end = n_routed + ns_t;
-  const int L0 = xcd_remap(blockIdx.x);
+  const int L0 = slot_work(blockIdx.x);
   if (L0 >= end) return;
   // The down product takes the shared experts' tiles first: their K runs over
   // all shared experts (n_s * I_s, twice a routed tile's I for two shared
@@ -544,7 +580,7 @@ __global__ __launch_bounds__(NTHREADS) void gate_up_raw_bf16_kernel(FfnArgs p, G
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int n_routed = p.part == kSharedTiles ? 0 : p.tile_off[p.E] * g.nt_r;
   const int ns_t = p.part == kRoutedTiles ? 0 : g.n_shared;
-  const int L = xcd_remap(blockIdx.x);
+  const int L = slot_work(blockIdx.x);
   if (L >= n_routed + ns_t) return;
   BTile t;
   gate_up_tile<true>(p, g, L, n_routed, t);
@@ -556,7 +592,7 @@ template <bool BUF>
 __global__ __launch_bounds__(NTHREADS) void down_routed_bf16_kernel(FfnArgs p, GemmGrid g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int n_routed = p.tile_off[p.E] * g.nt_r;
-  const int L = xcd_remap(blockIdx.x);
+  const int L = slot_work(blockIdx.x);
   if (L >= n_routed) return;
   BTile t;
   down_tile<true>(p, g, L, n_routed, t);
@@ -570,7 +606,7 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_bf16_kernel(SegGemmArgs p) 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int mt = (p.M + kBM - 1) / kBM, ntl = (p.N + BN - 1) / BN;
   const int per_e = mt * ntl;
-  const int L = xcd_remap(blockIdx.x);
+  const int L = slot_work(blockIdx.x);
   if (L >= p.E * per_e) return;
   const int e = L / per_e, rem = L - e * per_e;
   const int m0 = (rem / ntl) * kBM, n0 = (rem % ntl) * BN;

@@ -2,11 +2,12 @@
 //
 // M-tiles of kBM = 256 rows per expert come from the tile table that the
 // dispatch scan writes (tile_off[e] = M-tiles of the experts before e).
-// Within an expert the tiles run n-tile outer, m-tile inner, so the tiles
-// that share a weight slice are adjacent.  The grid is sized by an upper
-// bound of the routed tiles (no host read-back of the counts); slots past the
-// device-side count return at once.  Shared-expert tiles follow the routed
-// slots.
+// For the fp32 kernels (routed_tile below) the tiles of an expert run n-tile
+// outer, m-tile inner, so the tiles that share a weight slice are adjacent;
+// the bf16 kernels use a grouped raster of their own (gemm_bf16.hip).  The
+// grid is sized by an upper bound of the routed tiles (no host read-back of
+// the counts); slots past the device-side count return at once.
+// Shared-expert tiles follow the routed slots.
 #pragma once
 
 #include "common.h"

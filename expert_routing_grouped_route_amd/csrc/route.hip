@@ -119,14 +119,16 @@ __device__ __forceinline__ void topk_row16(const float* L, int E, int k, bool va
 // cut the router-weight traffic on long inputs.
 constexpr int kRouteWaves = 8;
 
-template <int NET, int NTT>  // 16-expert column tiles (E <= 16 * NET); 16-token row tiles
+// NET 16-expert column tiles (E <= 16 * NET); NTT 16-token row tiles; BP pairs
+// of K-steps whose loads each wave has in flight at once (it only changes when
+// loads are issued, not the order of the sums)
+template <int NET, int NTT, int BP = (NTT >= 4 ? 1 : 2)>
 __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int T, int d, int E, int k,
     float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ wts) {
   constexpr int TB = 16 * NTT;                  // tokens per block
   constexpr int EP = NET * 16 + 1;
-  constexpr int BATCH = NTT >= 4 ? 2 : 4 / NTT;  // K-steps in flight per wave (in pairs)
   __shared__ float part[kRouteWaves][TB][EP];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * TB;
@@ -152,7 +154,6 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
   // block, so results are reproducible.
   const int npair = d >> 6;
   const int rot = (int)((blockIdx.x >> 3) % (unsigned)npair);
-  constexpr int BP = BATCH >= 2 ? BATCH / 2 : 1;  // pairs in flight per wave
   for (int p0 = wave; p0 < npair; p0 += kRouteWaves * BP) {
     u32x4 av[BP][NTT][2], bv[BP][NET][2];
 #pragma unroll
