@@ -49,7 +49,7 @@ METRIC = "MoE-layer tokens/sec + grouped-GEMM % bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 STAGES = ("route", "dispatch", "gate_up", "down", "combine")
-GATE_UP_KERNEL = "grouped_gemm_bf16_kernel<true, true>"  # gate/up, buffer-load variant
+GATE_UP_KERNEL = "grouped_gemm_bf16_kernel<true, true, false>"  # gate/up, buffer-load variant
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the gate/up kernel: a change to any of them voids stored counter readings
 GEMM_SOURCES = ("gemm_bf16.hip", "grouped_gemm.h", "kernels.h", "common.h")

@@ -241,7 +241,10 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
 // 32 bits.
 // RAW (gate/up): store G and U as fp32 (and, with a_raw, the SwiGLU product
 // in bf16 at the same element offsets).
-template <bool GATE_UP, bool BUF, bool RAW = false, bool PARTS = false>
+// NT (down): store the fp32 output with non-temporal stores, for outputs larger
+// than the MALL (they stream to memory instead of filling the L2 with dirty
+// lines; smaller outputs stay cached for the combine that reads them next).
+template <bool GATE_UP, bool BUF, bool RAW = false, bool PARTS = false, bool NT = false>
 __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g_raw = nullptr,
                                          float* u_raw = nullptr, uint16_t* a_raw = nullptr) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -526,7 +529,8 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
         {
           f32x4* o = reinterpret_cast<f32x4*>(out + (size_t)grow * t.out_ld + lane * 4);
           const f32x4 v = *reinterpret_cast<const f32x4*>(sm + row * 256 + ((lane ^ (row & 63)) << 2));
-          *o = v;
+          if (NT) __builtin_nontemporal_store(v, o);
+          else *o = v;
         }
       }
       if (h == 0) {
@@ -554,7 +558,7 @@ __device__ __forceinline__ int slot_work(int b) {
 // launch of the shared experts' tiles alone reads nothing the dispatch writes
 // (it may run before the dispatch); a launch of the routed tiles alone has no
 // shared ones.
-template <bool GATE_UP, bool BUF>
+template <bool GATE_UP, bool BUF, bool NT = false>
 __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, GemmGrid g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int n_routed = p.part == kSharedTiles ? 0 : p.tile_off[p.E] * g.nt_r;
@@ -570,7 +574,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, 
   BTile t;
   if (GATE_UP) gate_up_tile(p, g, L, n_routed, t);
   else down_tile(p, g, L, n_routed, t);
-  run_tile<GATE_UP, BUF>(t, smem);
+  run_tile<GATE_UP, BUF, false, false, NT>(t, smem);
 }
 
 // Gate/up tiles with G and U stored as fp32 (RAW epilogue): the routed
@@ -734,8 +738,12 @@ void launch_seg_gemm_bf16(const SegGemmArgs& a, hipStream_t stream) {
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream) {
   const int64_t slots = launch_slots(a, bf16_down_grid(a));
   if (slots == 0) return;
-  auto kern = buffer_offsets_fit(a) ? grouped_gemm_bf16_kernel<false, true>
-                                    : grouped_gemm_bf16_kernel<false, false>;
+  // outputs (y and the shared experts' sum) larger than the 256 MB MALL take
+  // non-temporal stores
+  const bool nt = ((uint64_t)a.R + (a.ns ? (uint64_t)a.T : 0)) * a.d * 4 > (256ull << 20);
+  const bool buf = buffer_offsets_fit(a);
+  auto kern = buf ? (nt ? grouped_gemm_bf16_kernel<false, true, true> : grouped_gemm_bf16_kernel<false, true>)
+                  : (nt ? grouped_gemm_bf16_kernel<false, false, true> : grouped_gemm_bf16_kernel<false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a,
                      bf16_down_grid(a));
 }

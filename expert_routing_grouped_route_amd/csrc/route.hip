@@ -2,8 +2,8 @@
 // renormalised softmax weights.
 //
 // Top-k routing over the router's scores is the gate the expert-prototyping
-// abstract of the "Daily Papers" search page speaks of ("k ... in top-k
-// routing"); it is the T_gate term of the overlap window in the
+// abstract of the "Daily Papers" search page speaks of (k experts activated
+// per token); it is the T_gate term of the overlap window in the
 // FarSkip-Collective review (axiom ledger, Eq. 9).  Softmax, renormalisation
 // over the kept k and the tie rule are readings: the pages name none of them.
 //
@@ -30,14 +30,13 @@ __device__ __forceinline__ int row16_swap(int v) {
 }
 
 // Keep the larger of (bv, bi) and (ov, oi): larger value first, then the lower
-// index; bi == kNone marks no candidate.
+// index; bi == kNone marks no candidate.  Bitwise logic and selects only, so
+// the comparison compiles without branches.
 constexpr int kNone = 0x7fffffff;
 __device__ __forceinline__ void keep_better(float& bv, int& bi, float ov, int oi) {
-  const bool take = oi != kNone && (bi == kNone || ov > bv || (ov == bv && oi < bi));
-  if (take) {
-    bv = ov;
-    bi = oi;
-  }
+  const bool take = (oi != kNone) & ((bi == kNone) | (ov > bv) | ((ov == bv) & (oi < bi)));
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
 }
 
 template <int CTRL>
@@ -50,8 +49,8 @@ __device__ __forceinline__ void row16_step(float& bv, int& bi) {
 // Top-k of one token per 16-lane row.  The token's E logits sit in LDS at `L`;
 // lane c of the row considers experts c, c+16, ... (ascending, so a strict '>'
 // keeps the lowest index among equal values), and each slot is one row-wide
-// arg-max.  Lane c < k of the row writes slot c.  All 16 lanes of a row call
-// this together; `valid` false (a row past T) writes nothing.
+// arg-max; lane c keeps slot c.  All 16 lanes of a row call this together;
+// `valid` false (a row past T) writes nothing.  Lane c < k writes slot c.
 template <int NV>  // E <= 16 * NV
 __device__ __forceinline__ void topk_row16(const float* L, int E, int k, bool valid,
                                            int32_t* __restrict__ ids_out,
@@ -66,49 +65,41 @@ __device__ __forceinline__ void topk_row16(const float* L, int E, int k, bool va
     v[i] = live[i] ? L[e] : 0.0f;
   }
   float selv[kMaxK];
-  int seli[kMaxK];
+  float my_v = 0.0f;
+  int my_i = 0;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     selv[j] = 0.0f;
-    seli[j] = 0;
-    if (j < k) {
+    if (j < k) {  // uniform across the row
       float bv = 0.0f;
       int bi = kNone;
 #pragma unroll
-      for (int i = 0; i < NV; ++i)
-        if (live[i] && (bi == kNone || v[i] > bv)) {
-          bv = v[i];
-          bi = c + 16 * i;
-        }
+      for (int i = 0; i < NV; ++i) {
+        const bool take = live[i] & ((bi == kNone) | (v[i] > bv));
+        bv = take ? v[i] : bv;
+        bi = take ? c + 16 * i : bi;
+      }
       row16_step<0xB1>(bv, bi);
       row16_step<0x4E>(bv, bi);
       row16_step<0x141>(bv, bi);
       row16_step<0x140>(bv, bi);
       selv[j] = bv;
-      seli[j] = bi;
+      my_v = c == j ? bv : my_v;
+      my_i = c == j ? bi : my_i;
 #pragma unroll
-      for (int i = 0; i < NV; ++i)
-        if (bi == c + 16 * i) live[i] = false;
+      for (int i = 0; i < NV; ++i) live[i] = live[i] & (bi != c + 16 * i);
     }
   }
   // w_j = exp(L_j - L_0) / sum_j' exp(L_j' - L_0): the softmax over all E
-  // restricted to the kept k and renormalised (the full denominator cancels).
-  float z[kMaxK];
+  // restricted to the kept k and renormalised (the full denominator cancels);
+  // the sum runs over j in order in every lane.
   float s = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    z[j] = 0.0f;
-    if (j < k) {
-      z[j] = expf(selv[j] - selv[0]);
-      s += z[j];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (valid && j < k && c == j) {
-      ids_out[j] = seli[j];
-      w_out[j] = z[j] / s;
-    }
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < k) s += expf(selv[j] - selv[0]);
+  if (valid && c < k) {
+    ids_out[c] = my_i;
+    w_out[c] = expf(my_v - selv[0]) / s;
   }
 }
 
@@ -300,25 +291,28 @@ void launch_route(const RouteArgs& a, hipStream_t stream) {
   const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
   // tokens per block: 16 while that still gives a block per CU, more on long
   // inputs (each block reads all of W_r), within the LDS of the partial sums
+  // (for up to 64 experts a block of 16 tokens keeps all of a wave's K-step
+  // pairs in flight at once for d = 2048, which measured fastest; the larger
+  // token blocks keep fewer)
   const int net = a.E <= 16 ? 1 : a.E <= 32 ? 2 : a.E <= 64 ? 4 : a.E <= 128 ? 8 : 16;
   int ntt = a.T <= 4096 ? 1 : a.T <= 16384 ? 2 : 4;
   if (net == 8) ntt = ntt < 2 ? ntt : 2;
   if (net == 16) ntt = 1;
   const int grid_tb = (int)((a.T + 16 * ntt - 1) / (16 * ntt));
-#define MOE_ROUTE_CASE(N, M)                                                                     \
-  hipLaunchKernelGGL((route_bf16_kernel<N, M>), dim3(grid_tb), dim3(64 * kRouteWaves), 0, stream, \
+#define MOE_ROUTE_CASE(N, M, B)                                                                     \
+  hipLaunchKernelGGL((route_bf16_kernel<N, M, B>), dim3(grid_tb), dim3(64 * kRouteWaves), 0, stream, \
                      x, wr, a.bias, (int)a.T, a.d, a.E, a.k, a.logits_out, a.ids, a.wts)
-#define MOE_ROUTE_NTT(N)                   \
-  if (ntt == 1) MOE_ROUTE_CASE(N, 1);      \
-  else if (ntt == 2) MOE_ROUTE_CASE(N, 2); \
-  else MOE_ROUTE_CASE(N, 4)
+#define MOE_ROUTE_NTT(N)                      \
+  if (ntt == 1) MOE_ROUTE_CASE(N, 1, N == 4 ? 4 : 2); \
+  else if (ntt == 2) MOE_ROUTE_CASE(N, 2, 2); \
+  else MOE_ROUTE_CASE(N, 4, 1)
   if (net == 1) { MOE_ROUTE_NTT(1); }
   else if (net == 2) { MOE_ROUTE_NTT(2); }
   else if (net == 4) { MOE_ROUTE_NTT(4); }
   else if (net == 8) {
-    if (ntt == 1) MOE_ROUTE_CASE(8, 1);
-    else MOE_ROUTE_CASE(8, 2);
-  } else MOE_ROUTE_CASE(16, 1);
+    if (ntt == 1) MOE_ROUTE_CASE(8, 1, 2);
+    else MOE_ROUTE_CASE(8, 2, 2);
+  } else MOE_ROUTE_CASE(16, 1, 2);
 #undef MOE_ROUTE_NTT
 #undef MOE_ROUTE_CASE
 }
