@@ -127,7 +127,7 @@ KERNEL_ROLES = (
     ("route", r"route_bf16_kernel|route_f32_kernel"),
     ("dispatch_count", r"dispatch_count_kernel"),
     ("dispatch_rank", r"dispatch_rank_kernel"),
-    ("gather", r"gather_rows_kernel"),
+    ("row_scatter", r"scatter_rows_kernel"),
     ("gate_up", r"grouped_gemm_bf16_kernel<true"),
     ("down", r"grouped_gemm_bf16_kernel<false"),
     ("combine", r"combine_k_kernel|combine_kernel"),
@@ -147,7 +147,7 @@ def algorithmic_bytes(cfg, counts):
     least: every input it needs read once, every output written once.  The
     gate/up kernel reads each routed assignment's token row once (R rows) and
     only the weights of experts that received tokens; the gather (standalone
-    dispatch) reads x once."""
+    dispatch) reads x once, with the ids and inv_perm."""
     es = 2 if cfg.dtype == "bf16" else 4
     T, d, E, k, I, ns, Is = cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.n_shared, cfg.I_shared
     R = T * k
@@ -156,7 +156,7 @@ def algorithmic_bytes(cfg, counts):
         "route": (T * d * es + E * d * es + E * 4, R * 8),
         "dispatch_count": (R * 4, 0),
         "dispatch_rank": (R * 4, R * 8 + (2 * E + 1) * 4),
-        "gather": (T * d * es + R * 4, R * d * es),
+        "row_scatter": (T * d * es + R * 8, R * d * es),
         "gate_up": (nz * 2 * I * d * es + ns * 2 * Is * d * es + R * d * es + (T * d * es if ns else 0),
                     R * I * es + T * ns * Is * es),
         "down": (nz * d * I * es + ns * d * Is * es + R * I * es + T * ns * Is * es,
@@ -197,16 +197,19 @@ def summarize_counters(trace_csv, counter_csvs, bench_log, copy_mib, workload, c
         if role:
             dur.setdefault(role, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     vals = {}   # role -> counter -> [per-dispatch values]
+    cdur = {}   # role -> [duration of each dispatch in the counter runs]
     copy = {}   # counter -> KiB read for the calibration copy
     for path in counter_csvs:
         rows = _counter_rows(path)
-        last = max((int(r["Dispatch_Id"]) for r in rows if kernel_role(r["Kernel_Name"])), default=-1)
+        last_id = max((int(r["Dispatch_Id"]) for r in rows if kernel_role(r["Kernel_Name"])), default=-1)
         for r in rows:
             role = kernel_role(r["Kernel_Name"])
             name, v = r["Counter_Name"], float(r["Counter_Value"])
             if role:
                 vals.setdefault(role, {}).setdefault(name, []).append(v)
-            elif "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) > last:
+                if name == "GRBM_GUI_ACTIVE":
+                    cdur.setdefault(role, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            elif "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) > last_id:
                 copy[name] = copy.get(name, 0.0) + v
     scale = {n: copy_mib * 1024.0 / copy[n] for n in ("FETCH_SIZE", "WRITE_SIZE") if copy.get(n)}
     mean = lambda xs: sum(xs[-last:]) / len(xs[-last:])
@@ -232,8 +235,8 @@ def summarize_counters(trace_csv, counter_csvs, bench_log, copy_mib, workload, c
             e["traffic_GB/s"] = round((e["fetch_MB"] + e["write_MB"]) * 1e6 / (us * 1e-6) / 1e9, 1)
         if "MfmaUtil" in c:
             e["mfma_util_pct"] = round(c["MfmaUtil"], 1)
-        if "GRBM_GUI_ACTIVE" in c:  # summed over the 8 XCDs
-            e["clock_GHz"] = round(c["GRBM_GUI_ACTIVE"] / 8 / (us * 1e3), 3)
+        if "GRBM_GUI_ACTIVE" in c and role in cdur and us > 100:  # summed over the 8 XCDs
+            e["clock_GHz"] = round(c["GRBM_GUI_ACTIVE"] / 8 / mean(cdur[role]), 3)
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c and role in flops:
             ex = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
             e["mfma_flop_executed_over_alg"] = round(ex / flops[role], 3)
@@ -258,7 +261,7 @@ def summarize_counters(trace_csv, counter_csvs, bench_log, copy_mib, workload, c
                  "are scaled by the copy size over what each counter reads for the "
                  f"{copy_mib} MiB device copy at the end of its run; `alg` bytes are what the "
                  "kernel has to move at the least. MfmaUtil is MFMA-busy cycles over "
-                 "GUI-active cycles times the 1024 SIMDs; clock = GUI-active cycles (summed over the 8 XCDs) / 8 / duration.\n\n")
+                 "GUI-active cycles times the 1024 SIMDs; clock = GUI-active cycles (summed over the 8 XCDs) / 8 / the dispatch's duration in the same counter run (kernels over 100 us only).\n\n")
         cols = ["calls", "avg_us", "alg_read_MB", "fetch_MB", "fetch_over_alg_read", "alg_write_MB",
                 "write_MB", "alg_GB/s", "traffic_GB/s", "mfma_util_pct", "clock_GHz",
                 "frac_bf16_peak", "mfma_flop_executed_over_alg"]
@@ -283,6 +286,45 @@ def kernel_label(name, limit=120):
             name = name[:i]
             break
     return name if len(name) <= limit else name[:limit] + "..."
+
+
+def summarize_trace(trace_csv, workload, command, bench_log=None):
+    """Kernel time from a rocprofv3 --kernel-trace CSV of a bench.py run,
+    grouped by kernel and grid size (so the launches of the headline workload
+    and of the other workloads timed in the same run stay apart): calls,
+    average and total time, share.  With the run's JSON line (bench_log), the
+    same run's HIP-event stage times and roofline are appended for comparison.
+    Writes profiles/kernels_<workload>.md."""
+    groups = {}
+    for r in _counter_rows(trace_csv):
+        key = (kernel_label(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    total = sum(sum(v) for v in groups.values())
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    path = os.path.join(PROFILES, f"kernels_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write(f"# Kernel time, bench.py run on {workload} (rocprofv3 --kernel-trace)\n\n")
+        fh.write("Command (from the repository root):\n\n")
+        for c in command:
+            fh.write(f"    {c}\n")
+        fh.write("\nEvery launch of the run (warm-up, the timed passes, the other workloads, the "
+                 "backward pass), grouped by kernel and grid (workgroups).\n\n")
+        fh.write("| kernel | workgroups | calls | average us | total ms | share |\n|---|---|---|---|---|---|\n")
+        for (name, grid), d in rows:
+            if sum(d) < 1e-4 * total:
+                continue
+            fh.write(f"| `{name}` | {grid} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | "
+                     f"{sum(d) / 1e6:.3f} | {100.0 * sum(d) / total:.1f}% |\n")
+        if bench_log:
+            for line in open(bench_log):
+                if line.startswith("{"):
+                    rec = json.loads(line)
+                    fh.write("\nThe same run's JSON line: HIP-event stage times (ms per layer call) " +
+                             ", ".join(f"{k} {v}" for k, v in rec["stages_ms"].items()) +
+                             f"; roofline kernel `{rec['roofline']['kernel']}` average launch "
+                             f"{rec['roofline']['avg_launch_ms']} ms, {rec['roofline']['achieved']} "
+                             f"TFLOP/s.\n")
+    print(path)
 
 
 def summarize_stats(stats_csv, workload, command, bench_log=None, part="layer"):
@@ -660,12 +702,17 @@ def main():
                     help="profiling run: after a short warm-up, N calls of moe_layer_fwd and N "
                          "of the standalone moe_dispatch, then the copy calibration if asked; "
                          "prints the expert counts as JSON and skips every timing pass")
+    ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                    help="write profiles/kernels_<workload>.md from a rocprofv3 kernel-trace CSV")
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="write profiles/counters_<workload>.md from a kernel-trace CSV followed "
                          "by counter-collection CSVs (needs --bench-log of the profiling run)")
     ap.add_argument("--command", action="append", default=[],
                     help="command line recorded in a summary (repeatable)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, args.command, args.bench_log)
+        return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1:], args.bench_log,
                            args.copy_calibration_mib, args.workload, args.command)
