@@ -358,11 +358,15 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
 #pragma unroll
     for (int j = 0; j < 2; ++j) f[4 + j] = as_bf16x8(ld_u32x4(ws_ + b_off[j] + c));
   };
-  auto step = [&](int kt, auto ms_c, auto md_c, auto xl_c, auto mm_c) {
+  // PART: only the first ni of this wave's four 32-row blocks hold valid rows
+  // (the last M-tile of an expert), so the products of the others are skipped
+  const int ni = min(4, max(0, (t.rows - wm * 128 + 31) / 32));  // wave-uniform
+  auto step = [&](int kt, auto ms_c, auto md_c, auto xl_c, auto mm_c, auto part_c) {
     constexpr bool MS = decltype(ms_c)::value;
     constexpr bool MD = decltype(md_c)::value;
     constexpr bool XL = decltype(xl_c)::value;
     constexpr bool MM = decltype(mm_c)::value;
+    constexpr bool PART = decltype(part_c)::value;
     // loads this wave may still have in flight at step kt+1's barrier: the A
     // rows of step kt+2
     constexpr int PENDING = MD && XL ? XLOADS : 0;
@@ -378,10 +382,12 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
       if (MM) {
         if (ks < 3) rd(kt, ks + 1, F[(ks + 1) & 1]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          if (PART && i >= ni) continue;
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = mfma_32x32x16_bf16(F[ks & 1][4 + j], F[ks & 1][i], acc[i][j]);
+        }
       }
       bool has[2] = {false, false};
 #pragma unroll
@@ -395,7 +401,7 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
           has[u] = true;
         }
       }
-      if (MM) {
+      if (MM && !PART) {
         if (ks < 3 || MS) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -407,7 +413,7 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   };
 
   const int nk = t.nk;
-  auto k_loop = [&](auto xl_c, auto mm_c) {
+  auto k_loop = [&](auto xl_c, auto mm_c, auto part_c) {
     constexpr bool XL = decltype(xl_c)::value;
     constexpr bool MM = decltype(mm_c)::value;
     using T_ = std::true_type;
@@ -437,14 +443,21 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
     block_barrier();
     if (MM) rd(0, 0, F[0]);
     int kt = 0;
-    for (; kt + 2 < nk; ++kt) step(kt, T_{}, T_{}, xl_c, mm_c);
-    if (kt + 1 < nk) { step(kt, T_{}, F_{}, xl_c, mm_c); ++kt; }
-    step(kt, F_{}, F_{}, xl_c, mm_c);
+    for (; kt + 2 < nk; ++kt) step(kt, T_{}, T_{}, xl_c, mm_c, part_c);
+    if (kt + 1 < nk) { step(kt, T_{}, F_{}, xl_c, mm_c, part_c); ++kt; }
+    step(kt, F_{}, F_{}, xl_c, mm_c, part_c);
   };
   const bool mm = wm * 128 < t.rows;  // wave-uniform
-  if (wave * (8 * XLOADS) < t.rows) k_loop(std::true_type{}, std::true_type{});
-  else if (mm) k_loop(std::false_type{}, std::true_type{});
-  else k_loop(std::false_type{}, std::false_type{});
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (wave * (8 * XLOADS) < t.rows) {
+    if (ni == 4) k_loop(T_{}, T_{}, F_{});
+    else k_loop(T_{}, T_{}, T_{});
+  } else if (mm) {  // its A rows are past the tile's rows, so ni < 4
+    k_loop(F_{}, T_{}, T_{});
+  } else {
+    k_loop(F_{}, F_{}, F_{});
+  }
 
   // ---- epilogue.  Lane l holds, for A-block i and weight block j, row
   // wm*128 + i*32 + l%32 and the four columns 8q + 4(l/32) + 0..3 of the block
