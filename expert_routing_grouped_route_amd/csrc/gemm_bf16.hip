@@ -29,8 +29,10 @@
 // MFMAs that use them.
 // Each 128-byte LDS row holds its eight 16-byte K-chunks in an order permuted
 // by (row / 2 mod 8), which keeps the 32-row fragment reads free of bank
-// conflicts.  The gate/up epilogue stores from registers; the down epilogue
-// stages its fp32 tile through LDS and stores whole rows.
+// conflicts.  The forward epilogues stage their tiles through LDS and store
+// whole rows: the gate/up's bf16 A in one pass, the down's fp32 y in two
+// halves; the raw gate/up epilogue of the backward pass stores fp32 G and U
+// from registers.
 //
 // Work order: the routed tiles of expert 0, 1, ... (within an expert groups of
 // 4 m-tiles, n-tile outer and m-tile inner within a group), then the shared
@@ -461,9 +463,9 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
 
   // ---- epilogue.  Lane l holds, for A-block i and weight block j, row
   // wm*128 + i*32 + l%32 and the four columns 8q + 4(l/32) + 0..3 of the block
-  // in acc[i][j][4q..4q+3].  The fp32 output of the down product goes through
+  // in acc[i][j][4q..4q+3].  The outputs of the forward products go through
   // LDS (free once every wave's fragment reads are done), so that each store
-  // instruction writes a whole row; staged rows keep their 16-byte pieces at
+  // instruction writes whole rows; staged rows keep their 16-byte pieces at
   // position (piece ^ row), which spreads both the column writes and the row
   // reads over the banks.  Waves without valid rows write nothing but take
   // part in every barrier.
@@ -492,23 +494,38 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
       }
     }
   } else if (GATE_UP) {
-    // bf16 output is small: each lane stores its four columns (8 bytes) directly
-    if (!mm || wn * 32 >= t.out_cols) return;  // no valid rows, or columns past I
+    // bf16 A [256 rows][128 columns] goes through LDS as 16 pieces of 16 bytes
+    // per row, piece p of row r at position p ^ (r & 15), so that each store
+    // instruction writes 4 whole rows (8 full cache lines) instead of 16-byte
+    // parts of 32 rows
+    block_barrier();  // every wave's fragment reads are done: the LDS is free
+    if (mm) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + r32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = silu_times_rcp(acc[i][0][4 * q + r], acc[i][1][4 * q + r]);
+          uint2 v;
+          v.x = pack_bf16x2_rne(h[0], h[1]);
+          v.y = pack_bf16x2_rne(h[2], h[3]);
+          const int piece = wn * 4 + q;  // columns 8 * piece .. + 7; this lane's half: kg
+          *reinterpret_cast<uint2*>(smem + row * 256 + ((piece ^ (row & 15)) << 4) + kg * 8) = v;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    block_barrier();
     uint16_t* out = reinterpret_cast<uint16_t*>(t.Out);
+    const int piece = lane & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 128 + i * 32 + r32;
-      if (row >= t.rows) continue;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = wn * 32 + 8 * q + 4 * kg;
-        float h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = silu_times_rcp(acc[i][0][4 * q + r], acc[i][1][4 * q + r]);
-        uint2 v;
-        v.x = pack_bf16x2_rne(h[0], h[1]);
-        v.y = pack_bf16x2_rne(h[2], h[3]);
-        *reinterpret_cast<uint2*>(out + (size_t)row * t.out_ld + col) = v;
+    for (int u = 0; u < 8; ++u) {  // rows wave*32 .. +31, four per instruction
+      const int row = wave * 32 + u * 4 + (lane >> 4);
+      if (row < t.rows && piece * 8 < t.out_cols) {
+        const u32x4 v = ld_u32x4(smem + row * 256 + ((piece ^ (row & 15)) << 4));
+        *reinterpret_cast<u32x4*>(out + (size_t)row * t.out_ld + piece * 8) = v;
       }
     }
   } else {

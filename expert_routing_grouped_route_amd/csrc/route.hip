@@ -7,13 +7,21 @@
 // FarSkip-Collective review (axiom ledger, Eq. 9).  Softmax, renormalisation
 // over the kept k and the tie rule are readings: the pages name none of them.
 //
-// One block handles 16, 32 or 64 tokens.  bf16 logits run on the matrix
-// cores: eight waves split the hidden dimension (pairs of K-steps of 32 taken
-// round-robin, in an order rotated per block), each wave holding the block's
-// tokens x E experts of fp32 partial sums; the partials meet in LDS in a
-// fixed order.  fp32 logits run on the vector ALUs in a fixed
-// lane order.  The top-k then takes one token per 16-lane row, each slot a
-// row-wide arg-max through the VALU's cross-lane data-parallel moves.
+// bf16 logits run on the matrix cores, eight waves splitting the hidden
+// dimension, each wave holding its tokens x E experts of fp32 partial sums;
+// the partials meet in LDS in a fixed order.  Two kernels:
+//   * one block per 16, 32 or 64 tokens, the waves taking pairs of K-steps of
+//     32 round-robin (in an order rotated per block) and reading both x and
+//     W_r as they go;
+//   * for inputs with more 16-token groups than the GPU has CUs (and up to 64
+//     experts, d a power of two from 256 to 2048), one block per CU that keeps
+//     its share of W_r in registers and walks 16-token groups, loading the
+//     next group's x rows while the current one is reduced and routed.
+// fp32 logits run on the vector ALUs in a fixed lane order.  The top-k then
+// takes one token per 16-lane row, each slot a row-wide arg-max through the
+// VALU's cross-lane data-parallel moves.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -64,12 +72,14 @@ __device__ __forceinline__ void topk_row16(const float* L, int E, int k, bool va
     live[i] = e < E;
     v[i] = live[i] ? L[e] : 0.0f;
   }
-  float selv[kMaxK];
+  // w_j = exp(L_j - L_0) / sum_j' exp(L_j' - L_0): the softmax over all E
+  // restricted to the kept k and renormalised (the full denominator cancels);
+  // the sum runs over j in order in every lane.
+  float v0 = 0.0f, s = 0.0f;
   float my_v = 0.0f;
   int my_i = 0;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    selv[j] = 0.0f;
     if (j < k) {  // uniform across the row
       float bv = 0.0f;
       int bi = kNone;
@@ -83,23 +93,17 @@ __device__ __forceinline__ void topk_row16(const float* L, int E, int k, bool va
       row16_step<0x4E>(bv, bi);
       row16_step<0x141>(bv, bi);
       row16_step<0x140>(bv, bi);
-      selv[j] = bv;
+      if (j == 0) v0 = bv;
+      s += expf(bv - v0);
       my_v = c == j ? bv : my_v;
       my_i = c == j ? bi : my_i;
 #pragma unroll
       for (int i = 0; i < NV; ++i) live[i] = live[i] & (bi != c + 16 * i);
     }
   }
-  // w_j = exp(L_j - L_0) / sum_j' exp(L_j' - L_0): the softmax over all E
-  // restricted to the kept k and renormalised (the full denominator cancels);
-  // the sum runs over j in order in every lane.
-  float s = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    if (j < k) s += expf(selv[j] - selv[0]);
   if (valid && c < k) {
     ids_out[c] = my_i;
-    w_out[c] = expf(my_v - selv[0]) / s;
+    w_out[c] = expf(my_v - v0) / s;
   }
 }
 
@@ -204,6 +208,120 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
   }
 }
 
+// Barrier for LDS traffic only: waits for this wave's LDS accesses, not for
+// its global loads, which stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Logits and top-k of 16-token groups by a grid of at most one block per CU
+// that holds the router weights in registers: wave w keeps W_r's columns
+// [w d/8, (w+1) d/8) of every expert as MFMA fragments, loaded once, and the
+// block walks the groups g = blockIdx.x, blockIdx.x + gridDim.x, ...  A
+// group's x rows are loaded while the group before it is reduced and routed
+// (the barriers wait for LDS traffic only).  Each wave's partial sums over its
+// columns meet in LDS in wave order, then the bias; two LDS buffers let a
+// group's partials be written while the previous group's top-k still reads.
+template <int NET, int KS>  // E <= 16 * NET; d == 256 * KS
+__global__ __launch_bounds__(64 * kRouteWaves) void route_resident_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int d, int E, int k,
+    float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ wts) {
+  constexpr int EP = NET * 16 + 1;
+  constexpr int NR = (16 * 16 * NET + 64 * kRouteWaves - 1) / (64 * kRouteWaves);
+  __shared__ float part[2][kRouteWaves][16][EP];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, kq = (lane >> 4) * 8;
+  const int k0 = wave * (KS * 32) + kq;     // this wave's columns, plus the lane's 8
+  const int ngroups = (T + 15) >> 4;
+  if ((int)blockIdx.x >= ngroups) return;  // block-uniform
+  // experts past E read a valid row; their results are dropped
+  bf16x8 w[KS][NET];
+#pragma unroll
+  for (int et = 0; et < NET; ++et) {
+    const uint16_t* wp = wr + (size_t)min(et * 16 + r, E - 1) * d + k0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) w[ks][et] = as_bf16x8(ld_u32x4(wp + ks * 32));
+  }
+  // the (token, expert) entries this thread sums: idx = tid + 512 j
+  int rt[NR], re[NR];
+  float rb[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int idx = (int)threadIdx.x + j * 64 * kRouteWaves;
+    rt[j] = idx < 16 * E ? idx / E : -1;
+    re[j] = idx < 16 * E ? idx - rt[j] * E : 0;
+    rb[j] = (bias && rt[j] >= 0) ? bias[re[j]] : 0.0f;
+  }
+  auto load_x = [&](int g, bf16x8 (&xv)[KS]) {
+    // rows past T read a valid row; their results are dropped
+    const uint16_t* xp = x + (size_t)min(g * 16 + r, T - 1) * d + k0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) xv[ks] = as_bf16x8(ld_u32x4(xp + ks * 32));
+    __builtin_amdgcn_sched_barrier(0);  // issue them here, before this group's products
+  };
+  auto group = [&](int g, int b, const bf16x8 (&xv)[KS]) {
+    f32x4 acc[NET];
+#pragma unroll
+    for (int et = 0; et < NET; ++et) acc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int et = 0; et < NET; ++et) acc[et] = mfma_16x16x32_bf16(xv[ks], w[ks][et], acc[et]);
+#pragma unroll
+    for (int et = 0; et < NET; ++et)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) part[b][wave][(lane >> 4) * 4 + q][et * 16 + r] = acc[et][q];
+    lds_barrier();
+    const int t0 = g * 16;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      if (rt[j] >= 0) {
+        const int t = rt[j], e = re[j];
+        float pv[kRouteWaves];
+#pragma unroll
+        for (int w2 = 0; w2 < kRouteWaves; ++w2) pv[w2] = part[b][w2][t][e];
+        float v = pv[0];
+#pragma unroll
+        for (int w2 = 1; w2 < kRouteWaves; ++w2) v += pv[w2];
+        if (bias) v += rb[j];
+        part[b][0][t][e] = v;
+        if (logits_out && t0 + t < T) logits_out[(size_t)(t0 + t) * E + e] = v;
+      }
+    }
+    lds_barrier();
+    if (wave < 4) {  // one token per 16-lane row: waves 0..3 hold the group's 16 rows
+      const int t = wave * 4 + (lane >> 4);
+      const size_t tg = (size_t)min(t0 + t, T - 1);
+      topk_row16<NET>(&part[b][0][t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
+    }
+    // the next group writes the other buffer; the one after passes that
+    // group's first barrier, which every wave reaches only after this top-k
+  };
+  // Two groups per trip, so that the register buffers swap without copies.
+  // The next group's loads are issued on every path (the last group of a
+  // block reads its own rows again, from cache), so the wait before a
+  // group's products leaves exactly the next group's loads in flight.
+  bf16x8 xa[KS], xb[KS];
+  int g = blockIdx.x;
+  load_x(g, xa);
+  for (;;) {
+    int gn = g + (int)gridDim.x;
+    load_x(gn < ngroups ? gn : g, xb);
+    group(g, 0, xa);
+    if (gn >= ngroups) break;
+    g = gn;
+    gn = g + (int)gridDim.x;
+    load_x(gn < ngroups ? gn : g, xa);
+    group(g, 1, xb);
+    if (gn >= ngroups) break;
+    g = gn;
+  }
+}
+
 // fp32 logits on the vector ALUs in a fixed order: lane l sums the rounded
 // products of i = l, l+64, ... in ascending i (no fused multiply-add), a xor
 // butterfly over 32..1 combines the 64 partials, then the bias is added.
@@ -289,6 +407,27 @@ void launch_route(const RouteArgs& a, hipStream_t stream) {
   }
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
+  const int ngroups = (int)((a.T + 15) / 16);
+  // router weights held in registers: up to 64 experts, d / 256 K-steps of 32
+  // per wave within the register budget of two waves per SIMD
+  const int n_cu = device_cu_count();
+  if (ngroups > n_cu && a.E <= 64 && (a.d == 256 || a.d == 512 || a.d == 1024 || a.d == 2048)) {
+    const int grid_r = n_cu;
+#define MOE_ROUTE_RES(N, K)                                                                      \
+  hipLaunchKernelGGL((route_resident_bf16_kernel<N, K>), dim3(grid_r), dim3(64 * kRouteWaves), 0, \
+                     stream, x, wr, a.bias, (int)a.T, a.d, a.E, a.k, a.logits_out, a.ids, a.wts)
+#define MOE_ROUTE_RES_D(N)            \
+  if (a.d == 256) MOE_ROUTE_RES(N, 1); \
+  else if (a.d == 512) MOE_ROUTE_RES(N, 2); \
+  else if (a.d == 1024) MOE_ROUTE_RES(N, 4); \
+  else MOE_ROUTE_RES(N, 8)
+    if (a.E <= 16) { MOE_ROUTE_RES_D(1); }
+    else if (a.E <= 32) { MOE_ROUTE_RES_D(2); }
+    else { MOE_ROUTE_RES_D(4); }
+    return;
+#undef MOE_ROUTE_RES_D
+#undef MOE_ROUTE_RES
+  }
   // tokens per block: 16 while that still gives a block per CU, more on long
   // inputs (each block reads all of W_r), within the LDS of the partial sums
   // (for up to 64 experts a block of 16 tokens keeps all of a wave's K-step

@@ -101,6 +101,40 @@ def test_route_computed_logits(name):
     assert np.abs(w[same].astype(np.float64) - ref["w"][same]).max() <= tol
 
 
+# Shapes for the router that holds W_r in registers (bf16, E <= 64, d one of
+# 256, 512, 1024, 2048), each with more 16-token groups than the GPU has CUs,
+# so that blocks walk several groups and the last group is ragged.
+RESIDENT_ROUTE = {
+    "res_e40_d512": MoEShape("res_e40_d512", T=4500, d=512, E=40, k=4, I=64, seed=31,
+                             bias="normal"),
+    "res_e16_d1024": MoEShape("res_e16_d1024", T=9001, d=1024, E=16, k=2, I=64, seed=32),
+    "res_e32_d256": MoEShape("res_e32_d256", T=4205, d=256, E=32, k=3, I=64, seed=33,
+                             bias="normal"),
+    "res_e64_d2048": MoEShape("res_e64_d2048", T=8200, d=2048, E=64, k=6, I=64, seed=34),
+}
+
+
+@pytest.mark.parametrize("name", list(RESIDENT_ROUTE))
+def test_route_register_resident(name):
+    """Logits within the dot-product bound of the oracle's, ids the oracle's
+    top-k up to certified near ties, weights within tolerance elsewhere."""
+    import gpu_helpers as gh
+    cfg = RESIDENT_ROUTE[name]
+    print(f"[route {name}] T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k}", flush=True)
+    arrays = moe_synth.generate(cfg, workers=16)
+    lay = gh.Layer(cfg, arrays)
+    ids, w, L = lay.route()
+    gh.check_topk_of_own_logits(L, ids, cfg.k)
+    L_ref = oracle.router_logits(arrays["x"], arrays["w_router"], arrays["bias"])
+    ids_ref, w_ref = oracle.topk_route(L_ref, cfg.k)
+    bound = gh.logits_bound(arrays["x"], arrays["w_router"], arrays["bias"], L_ref)
+    dL = np.abs(L.astype(np.float64) - L_ref)
+    assert np.all(dL <= bound), f"logits outside the dot-product bound: {(dL / bound).max():.2f}x"
+    differ = gh.certify_routing(ids, ids_ref, L_ref, bound)
+    same = np.setdiff1d(np.arange(cfg.T), differ)
+    assert np.abs(w[same].astype(np.float64) - w_ref[same]).max() <= 2e-6 + 2.0 * dL.max()
+
+
 @pytest.mark.parametrize("name", ALL)
 def test_dispatch_bit_exact(name):
     cfg, arrays, ref, lay = case(name)
