@@ -68,8 +68,12 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int XLOADS = kBM / 8 / NWAVES;        // 1 KB direct loads per wave per stage: 4 of X
 constexpr int WLOADS = BN / 8 / NWAVES;         // and 4 of weights
 constexpr int LOADS = XLOADS + WLOADS;          // 8
-constexpr int XCD_RUN = 8;                      // consecutive works per XCD run
-constexpr int GROUP_M = 4;                      // m-tiles per group of the tile raster
+// Work placement (measured on the prefill-scale and DeepSeek-V2-Lite layers):
+// the gate/up product takes runs of 16 consecutive works per XCD over a
+// raster of 8 m-tiles, the down product runs of 8 over a raster of 4.
+constexpr int GU_RUN = 16, GU_GROUP_M = 8;
+constexpr int DN_RUN = 8, DN_GROUP_M = 4;
+constexpr int SEG_RUN = 8;                      // the backward's segment products
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 
@@ -93,17 +97,17 @@ __device__ __forceinline__ void block_barrier() {
 // s_waitcnt vmcnt(0) lgkmcnt(0) (gfx9 encoding; expcnt untouched).
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x70); }
 
-// Tile l of an mt x nt grid in raster order: groups of GROUP_M m-tiles, and
-// within a group n-tile outer, m-tile inner.  So a run of 8 consecutive
-// tiles of a large expert spans 4 m-tiles (A rows) and 2 n-tiles (weight
-// slices): 6 operand tiles for 8 output tiles, where a run along one n-tile
-// would need 9.
-__device__ __forceinline__ void raster(int l, int mt, int nt, int& m, int& n) {
-  const int gsize = GROUP_M * nt;
+// Tile l of an mt x nt grid in raster order: groups of GM m-tiles, and
+// within a group n-tile outer, m-tile inner.  So with GM = 4 a run of 8
+// consecutive tiles of a large expert spans 4 m-tiles (A rows) and 2 n-tiles
+// (weight slices): 6 operand tiles for 8 output tiles, where a run along one
+// n-tile would need 9.
+__device__ __forceinline__ void raster(int l, int mt, int nt, int GM, int& m, int& n) {
+  const int gsize = GM * nt;
   const int q = l / gsize, r = l - q * gsize;
-  const int gm = min(GROUP_M, mt - q * GROUP_M);
+  const int gm = min(GM, mt - q * GM);
   n = r / gm;
-  m = q * GROUP_M + (r - n * gm);
+  m = q * GM + (r - n * gm);
 }
 
 // Routed tile t (experts in order; within an expert the raster above) ->
@@ -115,7 +119,7 @@ __device__ __forceinline__ void routed_decode(const FfnArgs& p, const GemmGrid& 
   e = p.tile_off[p.E + 1 + t / g.nt_r];
   const int m0 = p.tile_off[e];
   const int mt = p.tile_off[e + 1] - m0;
-  raster(t - m0 * g.nt_r, mt, g.nt_r, m, n);
+  raster(t - m0 * g.nt_r, mt, g.nt_r, g.gm, m, n);
 }
 
 struct BTile {
@@ -165,7 +169,7 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
     const int per_s = g.mt_s * g.nt_s;
     const int s = sb / per_s;
     int m, n;
-    raster(sb - s * per_s, g.mt_s, g.nt_s, m, n);
+    raster(sb - s * per_s, g.mt_s, g.nt_s, g.gm, m, n);
     const int r0 = m * kBM;
     t.rows = (int)min((int64_t)kBM, p.T - r0);
     t.X = static_cast<const uint8_t*>(p.x) + (size_t)r0 * p.d * 2;
@@ -210,7 +214,7 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     t.Out = reinterpret_cast<uint8_t*>(p.y + (size_t)r0 * p.d + (size_t)n * BN);
   } else {
     int m;
-    raster(L - n_routed, g.mt_s, g.nt_r, m, n);
+    raster(L - n_routed, g.mt_s, g.nt_r, g.gm, m, n);
     r0 = m * kBM;
     t.rows = (int)min((int64_t)kBM, p.T - r0);
     const size_t ld = (size_t)p.ns * p.Is;
@@ -572,16 +576,16 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
 }
 
 // Launch slot -> work index.  Blocks are dealt to the 8 XCDs round-robin, so
-// slot b runs on XCD b % 8; within each group of 64 slots XCD x receives the
-// run of XCD_RUN consecutive works 8x .. 8x + 7, neighbours in the raster that
-// share A rows and weight slices in its L2.  Longer runs (32 works, one per CU
-// of an XCD) halve the L2 misses again but leave the XCDs unevenly loaded
-// where tile costs differ (shared-expert tiles, ragged last M-tiles), which
-// measured slower.
-__device__ __forceinline__ int slot_work(int b) {
-  constexpr int RUN = 8 * XCD_RUN;
-  const int base = b / RUN * RUN, w = b - base;
-  return base + (w & 7) * XCD_RUN + (w >> 3);
+// slot b runs on XCD b % 8; within each group of 8 * run slots XCD x receives
+// the run of consecutive works run * x .. run * x + run - 1, neighbours in the
+// raster that share A rows and weight slices in its L2.  Longer runs (32
+// works, one per CU of an XCD) halve the L2 misses again but leave the XCDs
+// unevenly loaded where tile costs differ (shared-expert tiles, ragged last
+// M-tiles), which measured slower.
+__device__ __forceinline__ int slot_work(int b, int run) {
+  const int group = 8 * run;
+  const int base = b / group * group, w = b - base;
+  return base + (w & 7) * run + (w >> 3);
 }
 
 // One block per work slot; slots past the device-side tile count return.  A
@@ -594,7 +598,7 @@ __global__ __launch_bounds__(NTHREADS) void grouped_gemm_bf16_kernel(FfnArgs p, 
   const int n_routed = p.part == kSharedTiles ? 0 : p.tile_off[p.E] * g.nt_r;
   const int ns_t = p.part == kRoutedTiles ? 0 : g.n_shared;
   const int end = n_routed + ns_t;
-  const int L0 = slot_work(blockIdx.x);
+  const int L0 = slot_work(blockIdx.x, g.run);
   if (L0 >= end) return;
   // The down product takes the shared experts' tiles first: their K runs over
   // all shared experts (n_s * I_s, twice a routed tile's I for two shared
@@ -614,7 +618,7 @@ __global__ __launch_bounds__(NTHREADS) void gate_up_raw_bf16_kernel(FfnArgs p, G
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int n_routed = p.part == kSharedTiles ? 0 : p.tile_off[p.E] * g.nt_r;
   const int ns_t = p.part == kRoutedTiles ? 0 : g.n_shared;
-  const int L = slot_work(blockIdx.x);
+  const int L = slot_work(blockIdx.x, g.run);
   if (L >= n_routed + ns_t) return;
   BTile t;
   gate_up_tile<true>(p, g, L, n_routed, t);
@@ -626,7 +630,7 @@ template <bool BUF>
 __global__ __launch_bounds__(NTHREADS) void down_routed_bf16_kernel(FfnArgs p, GemmGrid g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int n_routed = p.tile_off[p.E] * g.nt_r;
-  const int L = slot_work(blockIdx.x);
+  const int L = slot_work(blockIdx.x, g.run);
   if (L >= n_routed) return;
   BTile t;
   down_tile<true>(p, g, L, n_routed, t);
@@ -640,7 +644,7 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_bf16_kernel(SegGemmArgs p) 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int mt = (p.M + kBM - 1) / kBM, ntl = (p.N + BN - 1) / BN;
   const int per_e = mt * ntl;
-  const int L = slot_work(blockIdx.x);
+  const int L = slot_work(blockIdx.x, SEG_RUN);
   if (L >= p.E * per_e) return;
   const int e = L / per_e, rem = L - e * per_e;
   const int m0 = (rem / ntl) * kBM, n0 = (rem % ntl) * BN;
@@ -681,10 +685,12 @@ GemmGrid bf16_gate_up_grid(const FfnArgs& a) {
   g.n_shared = a.ns * g.nt_s * g.mt_s;
   g.routed = (int64_t)g.mtb * g.nt_r;
   g.total = g.routed + g.n_shared;
+  g.run = GU_RUN;
+  g.gm = GU_GROUP_M;
   return g;
 }
 
-int64_t pad_slots(int64_t n) { return (n + 8 * XCD_RUN - 1) / (8 * XCD_RUN) * (8 * XCD_RUN); }
+int64_t pad_slots(int64_t n, int run) { return (n + 8 * run - 1) / (8 * run) * (8 * run); }
 
 GemmGrid bf16_down_grid(const FfnArgs& a) {
   GemmGrid g;
@@ -695,20 +701,22 @@ GemmGrid bf16_down_grid(const FfnArgs& a) {
   g.n_shared = a.ns ? g.nt_r * g.mt_s : 0;
   g.routed = (int64_t)g.mtb * g.nt_r;
   g.total = g.routed + g.n_shared;
+  g.run = DN_RUN;
+  g.gm = DN_GROUP_M;
   return g;
 }
 
 }  // namespace
 
-int64_t gate_up_grid_bf16(const FfnArgs& a) { return pad_slots(bf16_gate_up_grid(a).total); }
-int64_t down_grid_bf16(const FfnArgs& a) { return pad_slots(bf16_down_grid(a).total); }
+int64_t gate_up_grid_bf16(const FfnArgs& a) { return pad_slots(bf16_gate_up_grid(a).total, GU_RUN); }
+int64_t down_grid_bf16(const FfnArgs& a) { return pad_slots(bf16_down_grid(a).total, DN_RUN); }
 
 // Slots of one launch: all tiles, the routed tiles (an upper bound) or the
 // shared experts' tiles.
 int64_t launch_slots(const FfnArgs& a, const GemmGrid& g) {
   const int64_t n = a.part == kRoutedTiles ? g.routed
                   : a.part == kSharedTiles ? (int64_t)g.n_shared : g.total;
-  return n ? pad_slots(n) : 0;
+  return n ? pad_slots(n, g.run) : 0;
 }
 
 // Whether every byte offset a tile adds to its operand bases fits in 32 bits:
@@ -749,7 +757,7 @@ void launch_gate_up_raw_bf16(const FfnArgs& a, hipStream_t stream) {
 
 void launch_down_routed_bf16(const FfnArgs& a, hipStream_t stream) {
   const GemmGrid g = bf16_down_grid(a);
-  const int64_t slots = g.routed ? pad_slots(g.routed) : 0;
+  const int64_t slots = g.routed ? pad_slots(g.routed, g.run) : 0;
   if (slots == 0) return;
   const bool buf = buffer_offsets_fit(a);
   auto kern = buf ? down_routed_bf16_kernel<true> : down_routed_bf16_kernel<false>;
@@ -762,7 +770,7 @@ void launch_seg_gemm_bf16(const SegGemmArgs& a, hipStream_t stream) {
   // buffer loads when a tile's offsets (256 rows of ld elements) fit in 32 bits
   const bool buf = (uint64_t)(kBM + 2) * (uint64_t)a.ld * 2 < (1ull << 32);
   auto kern = buf ? seg_gemm_bf16_kernel<true> : seg_gemm_bf16_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)pad_slots(tiles)), dim3(NTHREADS), 0, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)pad_slots(tiles, SEG_RUN)), dim3(NTHREADS), 0, stream, a);
 }
 
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream) {

@@ -44,6 +44,8 @@ struct GemmGrid {
   int n_shared;    // shared-expert tiles
   int64_t routed;  // routed tile slots (an upper bound)
   int64_t total;   // all slots (routed + shared), before any padding
+  int run = 8;     // bf16 kernels: consecutive works per XCD run
+  int gm = 4;      // bf16 kernels: m-tiles per group of the tile raster
 };
 
 }  // namespace moe
