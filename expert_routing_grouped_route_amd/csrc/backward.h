@@ -25,8 +25,6 @@ struct BwdArgs {
   int32_t* tile_off;                       // bf16: the dispatch's M-tile table
   int32_t* ctr;                            // bf16: the GEMM counters (zeroed by the dispatch)
   uint16_t* Abf;                           // bf16: [R,I] the SwiGLU product in bf16
-  uint16_t *wdT, *wgT, *wuT;               // bf16: [E,I,d], [E,d,I], [E,d,I] transposed weights
-                                           // (wuT after wgT in the same allocation)
   uint16_t* dGU;                           // bf16: [R, 4I] rows [dG hi | dG lo | dU hi | dU lo]
   int32_t* poff;                           // bf16: [E+1] padded per-expert parts (seg_offsets_kernel)
   int64_t seg_ld;                          // bf16: row length of tA and tB (>= poff[E])

@@ -1075,15 +1075,12 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
                        a.dw, a.inv, (int)T, a.k, a.dl, a.dls);
   }
   // bf16 layers run the input-gradient products dA = dY W_d[e] and
-  // dX = dG W_g[e] + dU W_u[e] on the forward down kernel: they have its
-  // shape once the weights are transposed (W_d^T [I,d], W_g^T and W_u^T
-  // [d,I]) and the fp32 operand is split into bf16 hi and lo rows, one
-  // launch per part, the later ones adding to the output.
+  // dX = dG W_g[e] + dU W_u[e] on the forward down kernel with the fp32
+  // operand split into bf16 hi and lo rows; the kernel reads the weights in
+  // their stored layout (W_d [d,I], W_g and W_u [I,d]: the reduction index
+  // outer) and forms their MFMA fragments with transposing LDS reads.
   FfnArgs fd = {};
   if (bf) {
-    launch_transpose_bf16(a.wd, E, d, I, a.wdT, s);
-    launch_transpose_bf16(a.wg, E, I, d, a.wgT, s);
-    launch_transpose_bf16(a.wu, E, I, d, a.wuT, s);
     fd.offsets = a.offsets;
     fd.tile_off = a.tile_off;
     fd.ctr = a.ctr;
@@ -1095,27 +1092,30 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     fd.force_global = a.force_global;
   }
   // out = sum over the `parts` K blocks of A's rows (K columns each) of block
-  // b times weight block b / 2 (w_part elements apart): one launch of the
-  // down kernel, which reduces over its I and writes d columns
-  // (rows_perm: A holds token rows, sorted row r reading token rows_perm[r] / k)
-  auto down_parts = [&](const uint16_t* A, int parts, const void* wT, int64_t w_part, int K,
-                        int N, float* out, const int32_t* rows_perm) {
+  // b times weight block b / 2 (w for block 0, w2 for block 1), the weights
+  // [E, K, N]: one launch of the down kernel, which reduces over its K and
+  // writes N columns (rows_perm: A holds token rows, sorted row r reading
+  // token row rows_perm[r] / k)
+  auto down_parts = [&](const uint16_t* A, int parts, const void* w, const void* w2, int K, int N,
+                        float* out, const int32_t* rows_perm) {
     fd.perm = rows_perm;
     fd.k = a.k;
-    fd.wd = wT;
+    fd.wd = w;
+    fd.wd2 = w2;
+    fd.wt = true;
     fd.I = K;
     fd.d = N;
     fd.y = out;
     fd.a = const_cast<uint16_t*>(A);
     fd.a_parts = parts;
-    fd.w_part = w_part;
+    fd.w_part = 0;
     launch_down_routed_bf16(fd, s);
   };
 
   // dA = dY W_d[e] (bf16 layers: dA' = dout W_d[e], the gate weight applied
   // in the SwiGLU backward); dW_d[e] = dY_e^T A_e
   if (bf) {
-    down_parts(a.dOp, 2, a.wdT, 0, d, I, a.dA, a.perm);
+    down_parts(a.dOp, 2, a.wd, nullptr, d, I, a.dA, a.perm);
   } else {
     ragged_m(a.dY, false, d, a.wd, bf, I, 1, (int64_t)d * I, a.dA, I, I, d, false);
   }
@@ -1159,7 +1159,7 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     ragged_k(a.U, false, I, a.xs, bf, d, a.dw_up, d, (int64_t)I * d, I, d);
   }
   if (bf) {
-    down_parts(a.dGU, 4, a.wgT, (int64_t)(a.wuT - a.wgT), I, d, a.dXs, nullptr);
+    down_parts(a.dGU, 4, a.wg, a.wu, I, d, a.dXs, nullptr);
   } else {
     ragged_m(a.G, false, I, a.wg, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, false);
     ragged_m(a.U, false, I, a.wu, bf, d, 1, (int64_t)I * d, a.dXs, d, d, I, true);

@@ -86,6 +86,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base)
 // Position permutation of the 16-byte chunks of LDS row `row`.
 __device__ __forceinline__ int chunk_xor(int row) { return (row >> 1) & 7; }
 
+// gfx950 transposing LDS read of 16-bit elements (ds_read_b64_tr_b16).
+// Within each group of 16 lanes, lane j = 4m + q passes the address of 4
+// consecutive elements; lane i of the group receives element i % 4 of the
+// reads of lanes 4m + i / 4, m = 0..3.  So if lane 4m + q points at row
+// k0 + m, columns c0 + 4q .. +3 of a row-major tile, lane i receives rows
+// k0 .. k0 + 3 of column c0 + i.
+// Two such reads per operand fragment, at a0 and a0 + 2048 (rows k0 + 4 ..),
+// for two fragments, then a wait for them in the same block (the outputs are
+// complete when it ends).  Written out because the compiler puts a wait for
+// every outstanding global load before its builtin form (it cannot tell the
+// read from the direct-to-LDS loads still in flight into other buffers); the
+// LDS stage read here is made visible by the K loop's own waits and barrier.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_read_tr16_frags(uint32_t a0, uint32_t a1, bf16x8& f0,
+                                                    bf16x8& f1) {
+  u32x2 l0, h0, l1, h1;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %5\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
+      : "v"(a0), "v"(a1)
+      : "memory");
+  f0 = __builtin_bit_cast(bf16x8, u32x4{l0.x, l0.y, h0.x, h0.y});
+  f1 = __builtin_bit_cast(bf16x8, u32x4{l1.x, l1.y, h1.x, h1.y});
+}
+
 // Hardware barrier with compiler-only fences: the waits that make LDS data
 // visible are issued explicitly before it.
 __device__ __forceinline__ void block_barrier() {
@@ -192,7 +221,8 @@ __device__ __forceinline__ void gate_up_tile(const FfnArgs& p, const GemmGrid& g
 }
 
 // PARTS: the routed rows of `a` may hold a_parts K blocks (FfnArgs::a_parts).
-template <bool PARTS = false>
+// WT (routed tiles): weights in their stored layout (FfnArgs::wt).
+template <bool PARTS = false, bool WT = false>
 __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, int L, int n_routed,
                                           BTile& t) {
   int n, r0;
@@ -211,6 +241,12 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     t.kps = parts > 1 ? p.I / BK : 0;
     if (PARTS) t.wsh = 1;  // the hi and lo blocks of one operand share a weight
     t.w_seg = parts > 1 ? (size_t)p.w_part * 2 : 0;
+    if (WT) {  // expert e's [I][d] block (K-rows of d elements), from column n * BN
+      const size_t eo = ((size_t)e * p.I * p.d + (size_t)n * BN) * 2;
+      w0 = static_cast<const uint8_t*>(p.wd) + eo;
+      t.w_ld = (size_t)p.d * 2;
+      t.w_seg = 0;
+    }
     t.Out = reinterpret_cast<uint8_t*>(p.y + (size_t)r0 * p.d + (size_t)n * BN);
   } else {
     int m;
@@ -235,6 +271,8 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
     t.rdiv = p.k;
   }
   t.W[0] = t.W[1] = w0;
+  if (WT && L < n_routed && p.wd2)
+    t.W[1] = static_cast<const uint8_t*>(p.wd2) + (w0 - static_cast<const uint8_t*>(p.wd));
   t.wrows = min(BN, p.d - n * BN);
   t.out_ld = p.d;
   t.out_cols = t.wrows;
@@ -250,9 +288,14 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
 // NT (down): store the fp32 output with non-temporal stores, for outputs larger
 // than the MALL (they stream to memory instead of filling the L2 with dirty
 // lines; smaller outputs stay cached for the combine that reads them next).
-template <bool GATE_UP, bool BUF, bool RAW = false, bool PARTS = false, bool NT = false>
+// WT (down product only): the weight tile arrives as 64 K-rows of 256 output
+// columns (the weights' stored layout, reduction index outer) and its MFMA
+// fragments come out of LDS through transposing reads.
+template <bool GATE_UP, bool BUF, bool RAW = false, bool PARTS = false, bool NT = false,
+          bool WT = false>
 __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g_raw = nullptr,
                                          float* u_raw = nullptr, uint16_t* a_raw = nullptr) {
+  static_assert(!WT || !GATE_UP, "k-major weights: down product only");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
 
@@ -281,12 +324,23 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   uint32_t woff[WLOADS];  // byte offsets from wbase, rows clamped to the valid ones
 #pragma unroll
   for (int q = 0; q < WLOADS; ++q) {
-    const int r = wfirst + q * 8 + sub;  // its LDS row kBM + wave*32 + q*8 + sub has the same row mod 16
-    woff[q] = (uint32_t)((size_t)min(r, t.wrows - 1) * t.w_ld) + ((pos ^ chunk_xor(r)) << 4);
+    if (WT) {
+      // load q fills K-rows 2 (wave*WLOADS + q) + L/32 of the stage (512 bytes
+      // each): lane L writes chunk position L % 32, which holds the chunk of
+      // 8 columns (L % 32) ^ (4 (row % 4)); columns past the valid ones read
+      // the last valid chunk (their outputs are not stored)
+      const int kr = 2 * (wave * WLOADS + q) + (lane >> 5);
+      const int cl = min((lane & 31) ^ ((kr & 3) << 2), (t.wrows >> 3) - 1);
+      woff[q] = (uint32_t)((size_t)kr * t.w_ld) + (cl << 4);
+    } else {
+      const int r = wfirst + q * 8 + sub;  // its LDS row kBM + wave*32 + q*8 + sub has the same row mod 16
+      woff[q] = (uint32_t)((size_t)min(r, t.wrows - 1) * t.w_ld) + ((pos ^ chunk_xor(r)) << 4);
+    }
   }
   // weight byte offset of K-step kt (the shared down tiles' K runs over the
   // shared experts' blocks one after the other)
   auto w_step = [&](int kt) -> size_t {
+    if (WT) return (size_t)(t.kps ? kt % t.kps : kt) * BK * t.w_ld;  // K-rows within the weight block
     return t.kps ? (size_t)(PARTS ? (kt / t.kps) >> t.wsh : kt / t.kps) * t.w_seg +
                        (size_t)(kt % t.kps) * ROW_BYTES
                  : (size_t)kt * ROW_BYTES;
@@ -294,6 +348,10 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   // direct loads of K-step kt: X load q (0..XLOADS-1), weight load q (0..WLOADS-1)
   const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(t.X);
   const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(wbase);
+  // WT: K-steps from kb1 on read weight block 1 (t.W[1]): with up to four K
+  // blocks of A, blocks 2 and 3 share weight block 1
+  const uint8_t* const wbase1 = WT ? t.W[1] : wbase;
+  const int kb1 = t.kps ? (t.kps << (PARTS ? t.wsh : 0)) : (1 << 30);
   auto issue_x = [&](int kt, int q) {
     const lds_void_t dst =
         (lds_void_t)(smem + (kt % NXB) * X_BYTES + (wave * (8 * XLOADS) + q * 8) * ROW_BYTES);
@@ -306,10 +364,18 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   auto issue_w = [&](int kt, size_t wstep, int q) {
     const lds_void_t dst = (lds_void_t)(smem + W_BASE + (kt % NWB) * W_BYTES +
                                         (wave * (8 * WLOADS) + q * 8) * ROW_BYTES);
-    if (BUF)
+    if (WT) {
+      const uint8_t* wb = kt >= kb1 ? wbase1 : wbase;  // wave-uniform
+      if (BUF)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(wb), dst, 16, woff[q], (uint32_t)wstep,
+                                                 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(wb + wstep + woff[q], dst, 16, 0, 0);
+    } else if (BUF) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 16, woff[q], (uint32_t)wstep, 0, 0);
-    else
+    } else {
       __builtin_amdgcn_global_load_lds(wbase + wstep + woff[q], dst, 16, 0, 0);
+    }
   };
 
   // ---- fragments (bytes within a stage).  MFMA 32x32x16: lane l reads row
@@ -323,7 +389,18 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int wrow = GATE_UP ? j * GU_COLS + wn * 32 : wn * 64 + j * 32;
-    b_off[j] = (wrow + r32) * ROW_BYTES;
+    if (WT) {
+      // transposing reads of the K-major stage (512-byte rows): lane l needs
+      // columns wrow + l % 32 at K-rows 16 s + 8 (l / 32) + 0..7 of sub-step s,
+      // two reads of 4 rows each; as a source lane it points at K-row
+      // 8 (l / 32) + (l % 16) / 4 (+ 16 s, + 4 for the second read), columns
+      // wrow + 16 ((l / 16) % 2) + 4 (l % 4) .. +3, in the row's swizzled chunk
+      const int mq = (lane & 15) >> 2, qq = lane & 3, g2 = (lane >> 4) & 1;
+      const int chunk = (wrow >> 3) + 2 * g2 + (qq >> 1);
+      b_off[j] = (8 * kg + mq) * (BN * 2) + ((chunk ^ (mq << 2)) << 4) + (qq & 1) * 8;
+    } else {
+      b_off[j] = (wrow + r32) * ROW_BYTES;
+    }
   }
 
   f32x16 acc[4][2];
@@ -361,8 +438,13 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
     const int c = (((ks * 2 + kg) ^ cx) << 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = as_bf16x8(ld_u32x4(xs_ + a_off[i] + c));
+    if (WT) {
+      const uint32_t base = (uint32_t)(uintptr_t)ws_ + ks * 16 * (BN * 2);  // LDS byte address
+      lds_read_tr16_frags(base + b_off[0], base + b_off[1], f[4], f[5]);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) f[4 + j] = as_bf16x8(ld_u32x4(ws_ + b_off[j] + c));
+      for (int j = 0; j < 2; ++j) f[4 + j] = as_bf16x8(ld_u32x4(ws_ + b_off[j] + c));
+    }
   };
   // PART: only the first ni of this wave's four 32-row blocks hold valid rows
   // (the last M-tile of an expert), so the products of the others are skipped
@@ -408,7 +490,7 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
         }
       }
       if (MM && !PART) {
-        if (ks < 3 || MS) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        if (ks < 3 || MS) __builtin_amdgcn_sched_group_barrier(0x100, WT ? 8 : 6, 0);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -625,16 +707,17 @@ __global__ __launch_bounds__(NTHREADS) void gate_up_raw_bf16_kernel(FfnArgs p, G
   run_tile<true, BUF, true>(t, smem, static_cast<float*>(p.a), p.u_raw, p.a_bf16);
 }
 
-// The routed down tiles alone (PARTS: A rows of several K blocks).
-template <bool BUF>
+// The routed down tiles alone (PARTS: A rows of several K blocks; WT:
+// weights in their stored layout).
+template <bool BUF, bool WT>
 __global__ __launch_bounds__(NTHREADS) void down_routed_bf16_kernel(FfnArgs p, GemmGrid g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int n_routed = p.tile_off[p.E] * g.nt_r;
   const int L = slot_work(blockIdx.x, g.run);
   if (L >= n_routed) return;
   BTile t;
-  down_tile<true>(p, g, L, n_routed, t);
-  run_tile<false, BUF, false, true>(t, smem);
+  down_tile<true, WT>(p, g, L, n_routed, t);
+  run_tile<false, BUF, false, true, false, WT>(t, smem);
 }
 
 // Weight-gradient tiles: expert e, 256-row m-tile, 256-column n-tile; K runs
@@ -734,8 +817,10 @@ bool buffer_offsets_fit(const FfnArgs& a) {
   const uint64_t parts = a.a_parts > 1 ? (uint64_t)a.a_parts : 1;
   const uint64_t xrows = (a.perm ? (uint64_t)a.T + 2 : 258) * parts * (uint64_t)a.I * 2;
   const uint64_t wpart = parts > 1 ? (uint64_t)a.w_part * 2 * (parts / 2) : 0;
+  // k-major weights: an expert's block of I K-rows of d elements
+  const bool wt_fits = !a.wt || (uint64_t)a.I * a.d * 2 + 1024 < lim;
   return (uint64_t)a.T * a.d * 2 + tile < lim && (uint64_t)a.ns * a.d * a.Is * 2 + tile < lim &&
-         xrows < lim && wpart + tile < lim;
+         xrows < lim && wpart + tile < lim && wt_fits;
 }
 
 void launch_gate_up_bf16(const FfnArgs& a, hipStream_t stream) {
@@ -760,7 +845,8 @@ void launch_down_routed_bf16(const FfnArgs& a, hipStream_t stream) {
   const int64_t slots = g.routed ? pad_slots(g.routed, g.run) : 0;
   if (slots == 0) return;
   const bool buf = buffer_offsets_fit(a);
-  auto kern = buf ? down_routed_bf16_kernel<true> : down_routed_bf16_kernel<false>;
+  auto kern = a.wt ? (buf ? down_routed_bf16_kernel<true, true> : down_routed_bf16_kernel<false, true>)
+                   : (buf ? down_routed_bf16_kernel<true, false> : down_routed_bf16_kernel<false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a, g);
 }
 

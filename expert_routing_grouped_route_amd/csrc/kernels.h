@@ -94,6 +94,13 @@ struct FfnArgs {
   // row perm[r] / k.
   int a_parts;
   int64_t w_part;
+  // launch_down_routed_bf16 only: with wt set, the weights are read in their
+  // stored layout, reduction index outer: expert e's element (k, n) at
+  // wd[(e * I + k) * d + n] (I = K and d = N here) rather than [E, d, I], and
+  // weight block 1 of the a_parts blocks (block b / 2 == 1) comes from wd2
+  // (same layout; w_part is then unused).
+  bool wt;
+  const void* wd2;
   // launch_gate_up_raw_bf16 only: also the bf16 SwiGLU product, in the layout
   // of G and U (or null)
   uint16_t* a_bf16;

@@ -327,7 +327,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // forward layout, then the backward scratch.
 struct BLayout {
   size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, rpart, Gs, Us, As, Asbf, dAs, dxs,
-      wdT, wgT, wuT, dGU, poff, tA, tB, off1, poff1, tiles1, off2, tiles2, wsdT,
+      dGU, poff, tA, tB, off1, poff1, tiles1, off2, tiles2, wsdT,
       wsgT, wsuT, dOp, sGU, poffS, kpart, total;
   int64_t seg_ld;
   int ksplit;
@@ -364,10 +364,6 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.dAs = take(ts * 4);
   B.dxs = take(D.n_shared ? (D.dtype == MOE_BF16 ? 2 : 1) * T * d * 4 : 0);
   const bool bf = D.dtype == MOE_BF16;
-  const size_t wsz = bf ? (size_t)D.E * I * d * 2 : 0;
-  B.wdT = take(wsz);
-  B.wgT = take(wsz);
-  B.wuT = take(wsz);
   B.dOp = take(bf ? T * d * 4 : 0);
   B.dGU = take(bf ? R * I * 8 : 0);
   // weight-gradient operands: per expert 2 * roundup(n_e, 64) columns
@@ -477,9 +473,6 @@ moe_status_t layer_bwd(const moe_dims_t* dims, const void* x, const void* w_rout
   ba.ctr = at<int32_t>(ws, L.ctr);
   ba.Abf = D.dtype == MOE_BF16 ? at<uint16_t>(ws, B.Abf) : nullptr;
   if (D.dtype == MOE_BF16) {
-    ba.wdT = at<uint16_t>(ws, B.wdT);
-    ba.wgT = at<uint16_t>(ws, B.wgT);
-    ba.wuT = at<uint16_t>(ws, B.wuT);
     ba.dOp = at<uint16_t>(ws, B.dOp);
     ba.dGU = at<uint16_t>(ws, B.dGU);
     ba.poff = at<int32_t>(ws, B.poff);
