@@ -828,6 +828,37 @@ void launch_split_rows(const float* v, int64_t rows, int cols, uint16_t* out, in
                      dim3(256), 0, s, v, rows, cols, out, out_ld, hi_col, lo_col);
 }
 
+// Sorted row r of the gate-weighted dout, w[perm[r]] * v[perm[r] / k], as its
+// bf16 hi parts (columns 0..cols-1 of out row r) and lo parts (cols..2 cols-1),
+// rounded as split_rows_bf16_kernel rounds.
+__global__ __launch_bounds__(256) void gather_split_rows_kernel(const float* __restrict__ v,
+                                                                const int32_t* __restrict__ perm,
+                                                                const float* __restrict__ w, int k,
+                                                                int64_t rows, int cols,
+                                                                uint16_t* __restrict__ out) {
+#pragma clang fp contract(off)  // the lo parts come from the rounded products
+  const int c4 = cols / 4;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const int a = perm[r];
+    const float sc = w[a];
+    const f32x4* src = reinterpret_cast<const f32x4*>(v + (int64_t)(a / k) * cols);
+    uint16_t* o = out + r * 2 * cols;
+    for (int c = threadIdx.x; c < c4; c += 256) {
+      const f32x4 x0 = src[c];
+      const float x[4] = {sc * x0[0], sc * x0[1], sc * x0[2], sc * x0[3]};
+      uint32_t h[2], l[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        h[j] = pack_bf16x2_rne(x[2 * j], x[2 * j + 1]);
+        l[j] = pack_bf16x2_rne(x[2 * j] - __uint_as_float(h[j] << 16),
+                               x[2 * j + 1] - __uint_as_float(h[j] & 0xffff0000u));
+      }
+      *reinterpret_cast<uint2*>(o + 4 * c) = make_uint2(h[0], h[1]);
+      *reinterpret_cast<uint2*>(o + cols + 4 * c) = make_uint2(l[0], l[1]);
+    }
+  }
+}
+
 // Padded part of each expert along the reduction index of a weight-gradient
 // product: 2 * roundup(n_e, 64) columns (the hi half, then the lo half, or
 // twice the same bf16 rows), starting at poff[e].
@@ -901,6 +932,7 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(const void* __restri
                                                             const int32_t* __restrict__ off,
                                                             const int32_t* __restrict__ poff, int E,
                                                             int64_t ld, uint16_t* __restrict__ dst) {
+#pragma clang fp contract(off)  // the lo parts come from the rounded products
   __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // [j][c]
   const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   if (j0 >= poff[E]) return;
@@ -1122,7 +1154,21 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   // weight gradients.  bf16 layers: the operands transposed into per-expert
   // zero-padded parts (an fp32 operand as its hi half then its lo half, the
   // bf16 one twice), then one product per weight on the forward tile loop.
-  if (bf) {
+  // With the buffer loads, the routed weight gradients read their operands in
+  // row layout (the gate-weighted dout rows formed once as hi and lo parts,
+  // in tA); otherwise through the transposed, zero-padded parts.
+  const bool km = bf && !a.force_global &&
+                  seg_gemm_km_fits(SegKmArgs{nullptr, std::max<int64_t>(4 * (int64_t)I, 2 * (int64_t)d),
+                                             0, nullptr, std::max<int64_t>(I, d), nullptr, nullptr,
+                                             E, 0, 0},
+                                   R);
+  if (km) {
+    if (R > 0)
+      hipLaunchKernelGGL(gather_split_rows_kernel, dim3((unsigned)std::min<int64_t>(R, 16384)),
+                         dim3(256), 0, s, a.dout, a.perm, a.w, a.k, R, d, a.tA);
+    launch_seg_gemm_km_bf16(
+        SegKmArgs{a.tA, 2 * (int64_t)d, d, a.Abf, I, a.offsets, a.dw_down, E, d, I}, s);
+  } else if (bf) {
     hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(64), 0, s, a.offsets, E, a.poff);
     launch_seg_transpose_gather(a.dout, d, a.perm, a.w, a.k, a.offsets, a.poff, E, a.seg_ld,
                                 a.tA, s);
@@ -1144,7 +1190,16 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nRI)), dim3(256), 0, s, a.G, a.U, a.dA,
                        nRI);
   }
-  if (bf) {
+  if (km) {  // dGU rows: dG hi, dG lo, dU hi, dU lo
+    const int64_t ld4 = 4 * (int64_t)I;
+    launch_seg_gemm_km_bf16(
+        SegKmArgs{a.dGU, ld4, I, static_cast<const uint16_t*>(a.xs), d, a.offsets, a.dw_gate, E, I, d},
+        s);
+    launch_seg_gemm_km_bf16(SegKmArgs{a.dGU + 2 * (size_t)I, ld4, I,
+                                      static_cast<const uint16_t*>(a.xs), d, a.offsets, a.dw_up, E,
+                                      I, d},
+                            s);
+  } else if (bf) {
     launch_seg_transpose(a.xs, false, d, a.offsets, a.poff, E, a.seg_ld, a.tB, s);
     const int64_t ld4 = 4 * (int64_t)I;  // dGU rows: dG hi, dG lo, dU hi, dU lo
     launch_seg_transpose(a.dGU, false, I, a.offsets, a.poff, E, a.seg_ld, a.tA, s, ld4, I);

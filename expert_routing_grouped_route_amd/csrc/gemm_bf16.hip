@@ -82,6 +82,11 @@ typedef __attribute__((address_space(3))) void* lds_void_t;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, -1, 0x00020000);
 }
+// The same with a byte range: loads at offsets past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, __builtin_bit_cast(int, bytes),
+                                           0x00020000);
+}
 
 // Position permutation of the 16-byte chunks of LDS row `row`.
 __device__ __forceinline__ int chunk_xor(int row) { return (row >> 1) & 7; }
@@ -168,6 +173,10 @@ struct BTile {
   size_t out_ld;          // elements between output rows
   int out_cols;           // valid output columns (a multiple of 64)
   int64_t raw_off;        // gate/up RAW: element offset of the tile's (0, 0) in G and U
+  // K-major A (KX tiles): bytes between its K blocks, and the byte ranges of
+  // the A and weight buffer descriptors (loads past them read zeros)
+  size_t x_seg;
+  uint32_t x_bytes, w_bytes;
 };
 
 template <bool RAW = false>  // RAW: also the tile's offset in the raw G and U arrays
@@ -291,11 +300,15 @@ __device__ __forceinline__ void down_tile(const FfnArgs& p, const GemmGrid& g, i
 // WT (down product only): the weight tile arrives as 64 K-rows of 256 output
 // columns (the weights' stored layout, reduction index outer) and its MFMA
 // fragments come out of LDS through transposing reads.
+// KX (with WT and BUF): the A tile too arrives as 64 K-rows of 256 rows of
+// the output (an operand stored with the reduction index outer), K blocks
+// t.x_seg bytes apart, and loads past t.x_bytes / t.w_bytes read zeros.
 template <bool GATE_UP, bool BUF, bool RAW = false, bool PARTS = false, bool NT = false,
-          bool WT = false>
+          bool WT = false, bool KX = false>
 __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g_raw = nullptr,
                                          float* u_raw = nullptr, uint16_t* a_raw = nullptr) {
   static_assert(!WT || !GATE_UP, "k-major weights: down product only");
+  static_assert(!KX || (WT && BUF && !PARTS), "k-major A: with k-major weights, buffer loads");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
 
@@ -307,10 +320,16 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   size_t xoff[XLOADS];  // byte offsets from t.X (below 2^32 with BUF)
 #pragma unroll
   for (int q = 0; q < XLOADS; ++q) {
-    const int row = wave * (8 * XLOADS) + q * 8 + sub;
-    const int rr = min(row, t.rows - 1);
-    const size_t xrow = t.rmap ? (size_t)(t.rmap[rr] / t.rdiv) : (size_t)rr;
-    xoff[q] = xrow * t.x_ld + ((pos ^ chunk_xor(row)) << 4);
+    if (KX) {  // as the K-major weight tile below, over the tile's 256 A rows
+      const int kr = 2 * (wave * XLOADS + q) + (lane >> 5);
+      const int cl = min((lane & 31) ^ ((kr & 3) << 2), (t.rows >> 3) - 1);
+      xoff[q] = (size_t)kr * t.x_ld + (cl << 4);
+    } else {
+      const int row = wave * (8 * XLOADS) + q * 8 + sub;
+      const int rr = min(row, t.rows - 1);
+      const size_t xrow = t.rmap ? (size_t)(t.rmap[rr] / t.rdiv) : (size_t)rr;
+      xoff[q] = xrow * t.x_ld + ((pos ^ chunk_xor(row)) << 4);
+    }
   }
   const uint8_t* wbase;  // wave-uniform
   int wfirst;            // first weight row of this wave within its half (gate/up) or tile (down)
@@ -346,8 +365,8 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
                  : (size_t)kt * ROW_BYTES;
   };
   // direct loads of K-step kt: X load q (0..XLOADS-1), weight load q (0..WLOADS-1)
-  const __amdgpu_buffer_rsrc_t x_rsrc = make_rsrc(t.X);
-  const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(wbase);
+  const __amdgpu_buffer_rsrc_t x_rsrc = KX ? make_rsrc_n(t.X, t.x_bytes) : make_rsrc(t.X);
+  const __amdgpu_buffer_rsrc_t w_rsrc = KX ? make_rsrc_n(wbase, t.w_bytes) : make_rsrc(wbase);
   // WT: K-steps from kb1 on read weight block 1 (t.W[1]): with up to four K
   // blocks of A, blocks 2 and 3 share weight block 1
   const uint8_t* const wbase1 = WT ? t.W[1] : wbase;
@@ -355,9 +374,17 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   auto issue_x = [&](int kt, int q) {
     const lds_void_t dst =
         (lds_void_t)(smem + (kt % NXB) * X_BYTES + (wave * (8 * XLOADS) + q * 8) * ROW_BYTES);
-    if (BUF)
+    if (KX) {
+      // K block kt / kps, its K-rows (kt % kps) * 64 ..: the whole offset in
+      // the lane offset, which the descriptor's range check covers
+      const uint32_t ks_off =
+          (uint32_t)((size_t)(kt / t.kps) * t.x_seg + (size_t)(kt % t.kps) * BK * t.x_ld);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, dst, 16, (uint32_t)xoff[q] + ks_off, 0, 0,
+                                               0);
+    } else if (BUF) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, dst, 16, (uint32_t)xoff[q],
                                                (uint32_t)(kt * ROW_BYTES), 0, 0);
+    }
     else
       __builtin_amdgcn_global_load_lds(t.X + xoff[q] + (size_t)kt * ROW_BYTES, dst, 16, 0, 0);
   };
@@ -366,7 +393,10 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
                                         (wave * (8 * WLOADS) + q * 8) * ROW_BYTES);
     if (WT) {
       const uint8_t* wb = kt >= kb1 ? wbase1 : wbase;  // wave-uniform
-      if (BUF)
+      if (KX)  // one weight block, through the ranged descriptor, offset in the lane
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 16, woff[q] + (uint32_t)wstep, 0, 0,
+                                                 0);
+      else if (BUF)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(wb), dst, 16, woff[q], (uint32_t)wstep,
                                                  0, 0);
       else
@@ -384,8 +414,18 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   const int r32 = lane & 31, kg = lane >> 5;
   const int cx = chunk_xor(r32);
   int a_off[4], b_off[2];
+  // transposing-read lane roles (KX and WT tiles): source row (l % 16) / 4,
+  // column group l % 4, half-group (l / 16) % 2
+  const int mq = (lane & 15) >> 2, qq = lane & 3, g2 = (lane >> 4) & 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_off[i] = (wm * 128 + i * 32 + r32) * ROW_BYTES;
+  for (int i = 0; i < 4; ++i) {
+    if (KX) {  // as b_off below, for the 32 A rows wm*128 + i*32 ..
+      const int chunk = ((wm * 128 + i * 32) >> 3) + 2 * g2 + (qq >> 1);
+      a_off[i] = (8 * kg + mq) * (kBM * 2) + ((chunk ^ (mq << 2)) << 4) + (qq & 1) * 8;
+    } else {
+      a_off[i] = (wm * 128 + i * 32 + r32) * ROW_BYTES;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int wrow = GATE_UP ? j * GU_COLS + wn * 32 : wn * 64 + j * 32;
@@ -395,7 +435,6 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
       // two reads of 4 rows each; as a source lane it points at K-row
       // 8 (l / 32) + (l % 16) / 4 (+ 16 s, + 4 for the second read), columns
       // wrow + 16 ((l / 16) % 2) + 4 (l % 4) .. +3, in the row's swizzled chunk
-      const int mq = (lane & 15) >> 2, qq = lane & 3, g2 = (lane >> 4) & 1;
       const int chunk = (wrow >> 3) + 2 * g2 + (qq >> 1);
       b_off[j] = (8 * kg + mq) * (BN * 2) + ((chunk ^ (mq << 2)) << 4) + (qq & 1) * 8;
     } else {
@@ -436,8 +475,14 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
     const uint8_t* xs_ = smem + (kt % NXB) * X_BYTES;
     const uint8_t* ws_ = smem + W_BASE + (kt % NWB) * W_BYTES;
     const int c = (((ks * 2 + kg) ^ cx) << 4);
+    if (KX) {
+      const uint32_t xb = (uint32_t)(uintptr_t)xs_ + ks * 16 * (kBM * 2);  // LDS byte address
+      lds_read_tr16_frags(xb + a_off[0], xb + a_off[1], f[0], f[1]);
+      lds_read_tr16_frags(xb + a_off[2], xb + a_off[3], f[2], f[3]);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = as_bf16x8(ld_u32x4(xs_ + a_off[i] + c));
+      for (int i = 0; i < 4; ++i) f[i] = as_bf16x8(ld_u32x4(xs_ + a_off[i] + c));
+    }
     if (WT) {
       const uint32_t base = (uint32_t)(uintptr_t)ws_ + ks * 16 * (BN * 2);  // LDS byte address
       lds_read_tr16_frags(base + b_off[0], base + b_off[1], f[4], f[5]);
@@ -490,7 +535,10 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
         }
       }
       if (MM && !PART) {
-        if (ks < 3 || MS) __builtin_amdgcn_sched_group_barrier(0x100, WT ? 8 : 6, 0);
+        // the fragment reads of the next sub-step (the transposing ones are
+        // asm blocks, outside the scheduler's DS-read class)
+        constexpr int NDS = (KX ? 0 : 4) + (WT ? 0 : 2);
+        if (NDS && (ks < 3 || MS)) __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -538,7 +586,11 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   const bool mm = wm * 128 < t.rows;  // wave-uniform
   using T_ = std::true_type;
   using F_ = std::false_type;
-  if (wave * (8 * XLOADS) < t.rows) {
+  if (KX) {  // every wave loads K-rows of A; only waves with valid A rows compute
+    if (!mm) k_loop(T_{}, F_{}, F_{});
+    else if (ni == 4) k_loop(T_{}, T_{}, F_{});
+    else k_loop(T_{}, T_{}, T_{});
+  } else if (wave * (8 * XLOADS) < t.rows) {
     if (ni == 4) k_loop(T_{}, T_{}, F_{});
     else k_loop(T_{}, T_{}, T_{});
   } else if (mm) {  // its A rows are past the tile's rows, so ni < 4
@@ -759,6 +811,54 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_bf16_kernel(SegGemmArgs p) 
   run_tile<false, BUF>(t, smem);
 }
 
+// Weight-gradient tiles with both operands in their row layout: out[e] =
+// sum over expert e's sorted rows r of the outer products X[r] (x) W[r], the
+// reduction running over the rows twice, X's first K block (columns 0..M-1,
+// the hi parts of an fp32 operand) and then its second (x_part columns on, the
+// lo parts), against the same W rows.  Both tiles arrive as 64 rows of 256
+// columns and their fragments come out of LDS through transposing reads;
+// rows past the expert's last read zeros through the descriptors' ranges.
+__global__ __launch_bounds__(NTHREADS) void seg_gemm_km_bf16_kernel(SegKmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+  const int mt = (p.M + kBM - 1) / kBM, ntl = (p.N + BN - 1) / BN;
+  const int per_e = mt * ntl;
+  const int L = slot_work(blockIdx.x, SEG_RUN);
+  if (L >= p.E * per_e) return;
+  const int e = L / per_e, rem = L - e * per_e;
+  const int m0 = (rem / ntl) * kBM, n0 = (rem % ntl) * BN;
+  const int s0 = p.offsets[e], ne = p.offsets[e + 1] - s0;
+  BTile t;
+  t.rows = min(kBM, p.M - m0);
+  t.wrows = min(BN, p.N - n0);
+  float* out = p.out + (size_t)e * p.M * p.N + (size_t)m0 * p.N + n0;
+  if (ne == 0) {  // no rows: the gradient is zero
+    for (int i = threadIdx.x; i < t.rows * (t.wrows / 4); i += NTHREADS) {
+      const int r = i / (t.wrows / 4), c = (i % (t.wrows / 4)) * 4;
+      *reinterpret_cast<f32x4*>(out + (size_t)r * p.N + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  const int kpe = (ne + BK - 1) / BK;  // K-steps per K block
+  t.X = reinterpret_cast<const uint8_t*>(p.X + (size_t)s0 * p.x_ld + m0);
+  t.x_ld = (size_t)p.x_ld * 2;
+  t.x_seg = (size_t)p.x_part * 2;
+  t.x_bytes = (uint32_t)((size_t)ne * p.x_ld * 2);
+  t.rmap = nullptr;
+  t.rdiv = 1;
+  t.W[0] = t.W[1] = reinterpret_cast<const uint8_t*>(p.W + (size_t)s0 * p.w_ld + n0);
+  t.w_ld = (size_t)p.w_ld * 2;
+  t.w_bytes = (uint32_t)((size_t)ne * p.w_ld * 2);
+  t.nk = 2 * kpe;
+  t.kps = kpe;
+  t.wsh = 0;
+  t.w_seg = 0;
+  t.Out = reinterpret_cast<uint8_t*>(out);
+  t.out_ld = p.N;
+  t.out_cols = t.wrows;
+  t.raw_off = 0;
+  run_tile<false, true, false, false, false, true, true>(t, smem);
+}
+
 GemmGrid bf16_gate_up_grid(const FfnArgs& a) {
   GemmGrid g;
   g.mtb = (int)routed_mtile_bound(a.R, a.E);
@@ -857,6 +957,19 @@ void launch_seg_gemm_bf16(const SegGemmArgs& a, hipStream_t stream) {
   const bool buf = (uint64_t)(kBM + 2) * (uint64_t)a.ld * 2 < (1ull << 32);
   auto kern = buf ? seg_gemm_bf16_kernel<true> : seg_gemm_bf16_kernel<false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)pad_slots(tiles, SEG_RUN)), dim3(NTHREADS), 0, stream, a);
+}
+
+bool seg_gemm_km_fits(const SegKmArgs& a, int64_t max_rows) {
+  // descriptor ranges and offsets of one expert's rows (at most max_rows)
+  const uint64_t lim = 1ull << 32;
+  return (uint64_t)max_rows * a.x_ld * 2 + 1024 < lim && (uint64_t)max_rows * a.w_ld * 2 + 1024 < lim;
+}
+
+void launch_seg_gemm_km_bf16(const SegKmArgs& a, hipStream_t stream) {
+  const int64_t tiles = (int64_t)a.E * ((a.M + kBM - 1) / kBM) * ((a.N + BN - 1) / BN);
+  if (tiles == 0) return;
+  hipLaunchKernelGGL(seg_gemm_km_bf16_kernel, dim3((unsigned)pad_slots(tiles, SEG_RUN)),
+                     dim3(NTHREADS), 0, stream, a);
 }
 
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream) {

@@ -134,6 +134,22 @@ struct SegGemmArgs {
   int E, M, N;
 };
 void launch_seg_gemm_bf16(const SegGemmArgs& a, hipStream_t stream);
+// Weight gradients from operands in their row layout: out[e][m][n] =
+// sum over expert e's rows r in [offsets[e], offsets[e+1]) and h in {0, 1} of
+// X[r][h * x_part + m] * W[r][n] (X: the bf16 hi and lo parts of an fp32
+// operand side by side; W: a bf16 operand).  Needs the buffer loads:
+// seg_gemm_km_fits() with the largest expert's row count.
+struct SegKmArgs {
+  const uint16_t* X;      // [rows, x_ld]
+  int64_t x_ld, x_part;   // elements between rows; between the hi and lo parts
+  const uint16_t* W;      // [rows, w_ld]
+  int64_t w_ld;
+  const int32_t* offsets; // [E+1] rows of each expert
+  float* out;             // [E, M, N] fp32
+  int E, M, N;
+};
+bool seg_gemm_km_fits(const SegKmArgs& a, int64_t max_rows);
+void launch_seg_gemm_km_bf16(const SegKmArgs& a, hipStream_t stream);
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream);
 void launch_gate_up_f32(const FfnArgs& a, hipStream_t stream);
 void launch_down_f32(const FfnArgs& a, hipStream_t stream);
