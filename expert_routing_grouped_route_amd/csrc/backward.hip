@@ -1330,7 +1330,28 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
         launch_seg_gemm_bf16(g1, s);
       }
     };
-    if (bf) {
+    // the same product from row-layout operands (one segment of T rows,
+    // the same K-step slices, so the same sums)
+    const bool kms = km && seg_gemm_km_fits(SegKmArgs{nullptr, 2 * std::max<int64_t>(ld, d), 0,
+                                                      nullptr, std::max<int64_t>(ld, d), nullptr,
+                                                      nullptr, 1, 0, 0, 0},
+                                            T);
+    auto seg1_km = [&](const uint16_t* X_, int64_t x_ld, int64_t x_part, const uint16_t* W_,
+                       int64_t w_ld, float* out, int M, int N) {
+      const int S = a.ksplit > 1 ? a.ksplit : 1;
+      launch_seg_gemm_km_bf16(
+          SegKmArgs{X_, x_ld, x_part, W_, w_ld, a.off1, S > 1 ? a.kpart : out, S, M, N, S}, s);
+      if (S > 1) {
+        const int64_t n = (int64_t)M * N;
+        hipLaunchKernelGGL(sum_slices_kernel, dim3(ew_grid(n / 4)), dim3(256), 0, s, a.kpart, S,
+                           n, out);
+      }
+    };
+    if (kms) {  // dOp: dout's hi and lo parts, formed for the routed part
+      for (int sh = 0; sh < ns; ++sh)
+        seg1_km(a.dOp, 2 * (int64_t)d, d, a.Asbf + (size_t)sh * Is, ld,
+                a.dwsh_down + (size_t)sh * d * Is, d, Is);
+    } else if (bf) {
       if (a.ksplit > 1)
         hipLaunchKernelGGL(split_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.ksplit,
                            a.poffS);
@@ -1345,7 +1366,19 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       }
     }
     hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(ew_grid(nT)), dim3(256), 0, s, a.Gs, a.Us, a.dAs, nT);
+    // sGU: rows 0..T-1 [dG_s hi | lo], rows T..2T-1 [dU_s hi | lo]
     if (bf) {
+      launch_split_rows(a.Gs, T, (int)ld, a.sGU, 2 * ld, 0, (int)ld, s);
+      launch_split_rows(a.Us, T, (int)ld, a.sGU + (size_t)T * 2 * ld, 2 * ld, 0, (int)ld, s);
+    }
+    if (kms) {
+      const uint16_t* xb = static_cast<const uint16_t*>(a.x);
+      for (int sh = 0; sh < ns; ++sh) {
+        seg1_km(a.sGU + (size_t)sh * Is, 2 * ld, ld, xb, d, a.dwsh_gate + (size_t)sh * Is * d, Is, d);
+        seg1_km(a.sGU + (size_t)T * 2 * ld + (size_t)sh * Is, 2 * ld, ld, xb, d,
+                a.dwsh_up + (size_t)sh * Is * d, Is, d);
+      }
+    } else if (bf) {
       launch_seg_transpose(a.x, false, d, a.off1, a.poff1, 1, a.seg_ld, a.tB, s);
       launch_seg_transpose(a.Gs, true, (int)ld, a.off1, a.poff1, 1, a.seg_ld, a.tA, s);
       for (int sh = 0; sh < ns; ++sh)
@@ -1366,8 +1399,6 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       // [dG_s hi | lo] against W_sg^T, rows T..2T-1 [dU_s hi | lo] against
       // W_su^T (the group-1 weight, d*ld elements after W_sg^T); their
       // products go to the two slabs of dxs, added in bwd_dx_kernel
-      launch_split_rows(a.Gs, T, (int)ld, a.sGU, 2 * ld, 0, (int)ld, s);
-      launch_split_rows(a.Us, T, (int)ld, a.sGU + (size_t)T * 2 * ld, 2 * ld, 0, (int)ld, s);
       hipLaunchKernelGGL(two_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.off2);
       launch_tile_table(a.off2, 2, a.tiles2, a.ctr, s);
       f1.offsets = a.off2;

@@ -177,6 +177,7 @@ struct BTile {
   // the A and weight buffer descriptors (loads past them read zeros)
   size_t x_seg;
   uint32_t x_bytes, w_bytes;
+  int kt0;                // KX tiles: K-step of the operands' layout where this tile starts
 };
 
 template <bool RAW = false>  // RAW: also the tile's offset in the raw G and U arrays
@@ -359,6 +360,7 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
   // weight byte offset of K-step kt (the shared down tiles' K runs over the
   // shared experts' blocks one after the other)
   auto w_step = [&](int kt) -> size_t {
+    if (KX) return (size_t)((kt + t.kt0) % t.kps) * BK * t.w_ld;
     if (WT) return (size_t)(t.kps ? kt % t.kps : kt) * BK * t.w_ld;  // K-rows within the weight block
     return t.kps ? (size_t)(PARTS ? (kt / t.kps) >> t.wsh : kt / t.kps) * t.w_seg +
                        (size_t)(kt % t.kps) * ROW_BYTES
@@ -377,8 +379,9 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
     if (KX) {
       // K block kt / kps, its K-rows (kt % kps) * 64 ..: the whole offset in
       // the lane offset, which the descriptor's range check covers
+      const int g = kt + t.kt0;
       const uint32_t ks_off =
-          (uint32_t)((size_t)(kt / t.kps) * t.x_seg + (size_t)(kt % t.kps) * BK * t.x_ld);
+          (uint32_t)((size_t)(g / t.kps) * t.x_seg + (size_t)(g % t.kps) * BK * t.x_ld);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, dst, 16, (uint32_t)xoff[q] + ks_off, 0, 0,
                                                0);
     } else if (BUF) {
@@ -557,7 +560,7 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
     // prologue: the weight and A rows of step 0, then the A rows of step 1 and
     // the first half of its weight rows
 #pragma unroll
-    for (int q = 0; q < WLOADS; ++q) issue_w(0, 0, q);
+    for (int q = 0; q < WLOADS; ++q) issue_w(0, w_step(0), q);
 #pragma unroll
     for (int q = 0; q < XLOADS; ++q)
       if (XL) issue_x(0, q);
@@ -826,19 +829,24 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_km_bf16_kernel(SegKmArgs p)
   if (L >= p.E * per_e) return;
   const int e = L / per_e, rem = L - e * per_e;
   const int m0 = (rem / ntl) * kBM, n0 = (rem % ntl) * BN;
-  const int s0 = p.offsets[e], ne = p.offsets[e + 1] - s0;
+  // with slices, all "experts" share segment 0 and take slices of its K-steps
+  const int sg = p.slices > 1 ? 0 : e;
+  const int s0 = p.offsets[sg], ne = p.offsets[sg + 1] - s0;
+  const int kpe = (ne + BK - 1) / BK;  // K-steps per K block
+  const int nks = 2 * kpe;
+  const int g0 = p.slices > 1 ? (int)((int64_t)e * nks / p.slices) : 0;
+  const int g1 = p.slices > 1 ? (int)((int64_t)(e + 1) * nks / p.slices) : nks;
   BTile t;
   t.rows = min(kBM, p.M - m0);
   t.wrows = min(BN, p.N - n0);
   float* out = p.out + (size_t)e * p.M * p.N + (size_t)m0 * p.N + n0;
-  if (ne == 0) {  // no rows: the gradient is zero
+  if (g1 <= g0) {  // no rows (or an empty slice): the product is zero
     for (int i = threadIdx.x; i < t.rows * (t.wrows / 4); i += NTHREADS) {
       const int r = i / (t.wrows / 4), c = (i % (t.wrows / 4)) * 4;
       *reinterpret_cast<f32x4*>(out + (size_t)r * p.N + c) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     return;
   }
-  const int kpe = (ne + BK - 1) / BK;  // K-steps per K block
   t.X = reinterpret_cast<const uint8_t*>(p.X + (size_t)s0 * p.x_ld + m0);
   t.x_ld = (size_t)p.x_ld * 2;
   t.x_seg = (size_t)p.x_part * 2;
@@ -848,7 +856,8 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_km_bf16_kernel(SegKmArgs p)
   t.W[0] = t.W[1] = reinterpret_cast<const uint8_t*>(p.W + (size_t)s0 * p.w_ld + n0);
   t.w_ld = (size_t)p.w_ld * 2;
   t.w_bytes = (uint32_t)((size_t)ne * p.w_ld * 2);
-  t.nk = 2 * kpe;
+  t.nk = g1 - g0;
+  t.kt0 = g0;
   t.kps = kpe;
   t.wsh = 0;
   t.w_seg = 0;

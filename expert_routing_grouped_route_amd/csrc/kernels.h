@@ -147,6 +147,9 @@ struct SegKmArgs {
   const int32_t* offsets; // [E+1] rows of each expert
   float* out;             // [E, M, N] fp32
   int E, M, N;
+  // slices > 1: one segment (offsets[0..1]) whose 2 * ceil(rows / 64) K-steps
+  // are cut into E = slices contiguous ranges, range e summed into out[e]
+  int slices;
 };
 bool seg_gemm_km_fits(const SegKmArgs& a, int64_t max_rows);
 void launch_seg_gemm_km_bf16(const SegKmArgs& a, hipStream_t stream);
