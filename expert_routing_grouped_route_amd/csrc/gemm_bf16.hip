@@ -764,7 +764,7 @@ __global__ __launch_bounds__(NTHREADS) void gate_up_raw_bf16_kernel(FfnArgs p, G
 
 // The routed down tiles alone (PARTS: A rows of several K blocks; WT:
 // weights in their stored layout).
-template <bool BUF, bool WT>
+template <bool BUF, bool WT, bool NT = false>
 __global__ __launch_bounds__(NTHREADS) void down_routed_bf16_kernel(FfnArgs p, GemmGrid g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int n_routed = p.tile_off[p.E] * g.nt_r;
@@ -772,7 +772,7 @@ __global__ __launch_bounds__(NTHREADS) void down_routed_bf16_kernel(FfnArgs p, G
   if (L >= n_routed) return;
   BTile t;
   down_tile<true, WT>(p, g, L, n_routed, t);
-  run_tile<false, BUF, false, true, false, WT>(t, smem);
+  run_tile<false, BUF, false, true, NT, WT>(t, smem);
 }
 
 // Weight-gradient tiles: expert e, 256-row m-tile, 256-column n-tile; K runs
@@ -821,6 +821,7 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_bf16_kernel(SegGemmArgs p) 
 // lo parts), against the same W rows.  Both tiles arrive as 64 rows of 256
 // columns and their fragments come out of LDS through transposing reads;
 // rows past the expert's last read zeros through the descriptors' ranges.
+template <bool NT>  // non-temporal output stores
 __global__ __launch_bounds__(NTHREADS) void seg_gemm_km_bf16_kernel(SegKmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int mt = (p.M + kBM - 1) / kBM, ntl = (p.N + BN - 1) / BN;
@@ -865,7 +866,7 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_km_bf16_kernel(SegKmArgs p)
   t.out_ld = p.N;
   t.out_cols = t.wrows;
   t.raw_off = 0;
-  run_tile<false, true, false, false, false, true, true>(t, smem);
+  run_tile<false, true, false, false, NT, true, true>(t, smem);
 }
 
 GemmGrid bf16_gate_up_grid(const FfnArgs& a) {
@@ -954,7 +955,11 @@ void launch_down_routed_bf16(const FfnArgs& a, hipStream_t stream) {
   const int64_t slots = g.routed ? pad_slots(g.routed, g.run) : 0;
   if (slots == 0) return;
   const bool buf = buffer_offsets_fit(a);
-  auto kern = a.wt ? (buf ? down_routed_bf16_kernel<true, true> : down_routed_bf16_kernel<false, true>)
+  // outputs larger than the 256 MB MALL take non-temporal stores
+  const bool nt = a.wt && buf && (uint64_t)a.R * a.d * 4 > (256ull << 20);
+  auto kern = a.wt ? (buf ? (nt ? down_routed_bf16_kernel<true, true, true>
+                                : down_routed_bf16_kernel<true, true>)
+                          : down_routed_bf16_kernel<false, true>)
                    : (buf ? down_routed_bf16_kernel<true, false> : down_routed_bf16_kernel<false, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)slots), dim3(NTHREADS), 0, stream, a, g);
 }
@@ -977,8 +982,10 @@ bool seg_gemm_km_fits(const SegKmArgs& a, int64_t max_rows) {
 void launch_seg_gemm_km_bf16(const SegKmArgs& a, hipStream_t stream) {
   const int64_t tiles = (int64_t)a.E * ((a.M + kBM - 1) / kBM) * ((a.N + BN - 1) / BN);
   if (tiles == 0) return;
-  hipLaunchKernelGGL(seg_gemm_km_bf16_kernel, dim3((unsigned)pad_slots(tiles, SEG_RUN)),
-                     dim3(NTHREADS), 0, stream, a);
+  // outputs larger than the 256 MB MALL take non-temporal stores
+  const bool nt = (uint64_t)a.E * a.M * a.N * 4 > (256ull << 20);
+  hipLaunchKernelGGL(nt ? seg_gemm_km_bf16_kernel<true> : seg_gemm_km_bf16_kernel<false>,
+                     dim3((unsigned)pad_slots(tiles, SEG_RUN)), dim3(NTHREADS), 0, stream, a);
 }
 
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream) {
