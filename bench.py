@@ -124,7 +124,7 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib, workload, command):
 
 # kernels of the layer path by role (regular expressions on demangled names)
 KERNEL_ROLES = (
-    ("route", r"route_bf16_kernel|route_f32_kernel"),
+    ("route", r"route_bf16_kernel|route_resident_bf16_kernel|route_f32_kernel"),
     ("dispatch_count", r"dispatch_count_kernel"),
     ("dispatch_rank", r"dispatch_rank_kernel"),
     ("row_scatter", r"scatter_rows_kernel"),
