@@ -61,7 +61,9 @@ def build_library(verbose: bool = False, jobs: int = 8) -> str:
     with ThreadPoolExecutor(max(1, min(jobs, len(SOURCES)))) as ex:
         objs = list(ex.map(one, SOURCES))
     tmp = LIB_PATH + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    # --no-undefined: a kernel whose host-side launch stub went missing fails
+    # here rather than when the library is loaded
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")

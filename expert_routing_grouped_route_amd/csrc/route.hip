@@ -10,15 +10,17 @@
 // bf16 logits run on the matrix cores, eight waves splitting the hidden
 // dimension, each wave holding its tokens x E experts of fp32 partial sums;
 // the partials meet in LDS in a fixed order.  Two kernels:
-//   * one block per 16, 32 or 64 tokens, the waves taking pairs of K-steps of
-//     32 round-robin (in an order rotated per block) and reading both x and
-//     W_r as they go;
-//   * for inputs with more 16-token groups than the GPU has CUs (and up to 64
-//     experts, d a power of two from 256 to 2048), one block per CU that keeps
-//     its share of W_r in registers and walks 16-token groups, loading the
-//     next group's x rows while the current one is reduced and routed.
+//   * for up to 64 experts and d a power of two from 256 to 2048: one block
+//     per 16-token group, up to one per CU, that keeps its share of W_r in
+//     registers (loaded once, through LDS in whole cache lines) and walks
+//     the groups, loading the next group's x rows while the current one is
+//     reduced and routed;
+//   * otherwise one block per 16, 32 or 64 tokens, the waves taking pairs of
+//     K-steps of 32 round-robin (in an order rotated per block) and reading
+//     both x and W_r as they go.
 // fp32 logits run on the vector ALUs in a fixed lane order.  The top-k then
-// takes one token per 16-lane row, each slot a row-wide arg-max through the
+// takes one token per 16-lane row, each slot a row-wide max of the logits'
+// integer images, then a row-wide min of the indices holding it, through the
 // VALU's cross-lane data-parallel moves.
 #include <algorithm>
 
@@ -27,83 +29,110 @@
 
 namespace moe {
 
-// Row-wide exchange within each group of 16 lanes on the VALU's data-parallel
-// primitives: CTRL 0xB1 swaps neighbours (quad_perm 1,0,3,2), 0x4E swaps lane
-// pairs (quad_perm 2,3,0,1), 0x141 mirrors each half row of 8, 0x140 mirrors
-// the row of 16.  Applied in that order, a symmetric pairwise rule leaves
-// every lane of the row with the row's result.
+// Row-wide reductions within each group of 16 lanes on the VALU's
+// data-parallel moves: CTRL 0xB1 swaps neighbours (quad_perm 1,0,3,2), 0x4E
+// swaps lane pairs (quad_perm 2,3,0,1), 0x141 mirrors each half row of 8,
+// 0x140 mirrors the row of 16.  Combining each lane with its partner in that
+// order leaves every lane of the row with the row's max (or min).
 template <int CTRL>
-__device__ __forceinline__ int row16_swap(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+__device__ __forceinline__ int row16_partner(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int row16_max(int v) {
+  v = max(v, row16_partner<0xB1>(v));
+  v = max(v, row16_partner<0x4E>(v));
+  v = max(v, row16_partner<0x141>(v));
+  return max(v, row16_partner<0x140>(v));
+}
+__device__ __forceinline__ int row16_min(int v) {
+  v = min(v, row16_partner<0xB1>(v));
+  v = min(v, row16_partner<0x4E>(v));
+  v = min(v, row16_partner<0x141>(v));
+  return min(v, row16_partner<0x140>(v));
+}
+// Lane j's value, in every lane of its row of 16.
+template <int J>
+__device__ __forceinline__ float row16_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + J, 0xF, 0xF, false));
 }
 
-// Keep the larger of (bv, bi) and (ov, oi): larger value first, then the lower
-// index; bi == kNone marks no candidate.  Bitwise logic and selects only, so
-// the comparison compiles without branches.
+// An integer image of an fp32 value whose signed order is the values' order,
+// with -0 taken to +0 so that the two compare equal (then the lower index
+// wins, as for any tie).  kDead lies below the image of every value.
 constexpr int kNone = 0x7fffffff;
-__device__ __forceinline__ void keep_better(float& bv, int& bi, float ov, int oi) {
-  const bool take = (oi != kNone) & ((bi == kNone) | (ov > bv) | ((ov == bv) & (oi < bi)));
-  bv = take ? ov : bv;
-  bi = take ? oi : bi;
+constexpr int kDead = (int)0x80000000;
+__device__ __forceinline__ int order_key(float v) {
+  int b = __float_as_int(v);
+  b = b == kDead ? 0 : b;
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float key_value(int key) {
+  return __int_as_float(key ^ ((key >> 31) & 0x7fffffff));
 }
 
-template <int CTRL>
-__device__ __forceinline__ void row16_step(float& bv, int& bi) {
-  const float ov = __int_as_float(row16_swap<CTRL>(__float_as_int(bv)));
-  const int oi = row16_swap<CTRL>(bi);
-  keep_better(bv, bi, ov, oi);
+// Top-k of one token per 16-lane row.  The token's E logits sit in LDS at `L`
+// (16 * NV floats readable there); lane c of the row holds experts c, c+16,
+// ...  Each slot takes the row's largest remaining value (a row-wide max of
+// the integer images), then the lowest index holding it (a row-wide min),
+// which leaves the race.  Lane c = threadIdx.x % 16 < k receives slot c's
+// expert and weight (other lanes: unspecified).  All 16 lanes of a row call
+// this together.
+template <int NV>  // E <= 16 * NV
+__device__ __forceinline__ void topk_row16_slot(const float* L, int E, int k, int& id_c,
+                                                float& w_c) {
+  const int c = threadIdx.x & 15;
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = L[c + 16 * i];  // all issued before the first use
+  int key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) key[i] = c + 16 * i < E ? order_key(v[i]) : kDead;
+  int key0 = 0, my_key = 0, my_i = 0;
+#pragma unroll 1
+  for (int j = 0; j < k; ++j) {
+    int lk = key[0];
+#pragma unroll
+    for (int i = 1; i < NV; ++i) lk = max(lk, key[i]);
+    const int m = row16_max(lk);
+    int cand = kNone;
+#pragma unroll
+    for (int i = NV - 1; i >= 0; --i) cand = key[i] == m ? c + 16 * i : cand;
+    const int win = row16_min(cand);
+    key0 = j == 0 ? m : key0;
+    my_key = c == j ? m : my_key;
+    my_i = c == j ? win : my_i;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) key[i] = win == c + 16 * i ? kDead : key[i];
+  }
+  // w_j = exp(L_j - L_0) / sum_j' exp(L_j' - L_0): the softmax over all E
+  // restricted to the kept k and renormalised (the full denominator cancels);
+  // lane j holds term j, and the sum runs over j in order in every lane
+  // (adding +0 for the slots past k leaves it unchanged).
+  const float v0 = key_value(key0);
+  const float term = expf(key_value(my_key) - v0);
+  float s = 0.0f;
+#define MOE_TOPK_SUM(J) s += J < k ? row16_bcast<J>(term) : 0.0f;
+  MOE_TOPK_SUM(0) MOE_TOPK_SUM(1) MOE_TOPK_SUM(2) MOE_TOPK_SUM(3)
+  MOE_TOPK_SUM(4) MOE_TOPK_SUM(5) MOE_TOPK_SUM(6) MOE_TOPK_SUM(7)
+  MOE_TOPK_SUM(8) MOE_TOPK_SUM(9) MOE_TOPK_SUM(10) MOE_TOPK_SUM(11)
+  MOE_TOPK_SUM(12) MOE_TOPK_SUM(13) MOE_TOPK_SUM(14) MOE_TOPK_SUM(15)
+#undef MOE_TOPK_SUM
+  static_assert(kMaxK == 16, "one broadcast per slot");
+  id_c = my_i;
+  w_c = term / s;
 }
 
-// Top-k of one token per 16-lane row.  The token's E logits sit in LDS at `L`;
-// lane c of the row considers experts c, c+16, ... (ascending, so a strict '>'
-// keeps the lowest index among equal values), and each slot is one row-wide
-// arg-max; lane c keeps slot c.  All 16 lanes of a row call this together;
-// `valid` false (a row past T) writes nothing.  Lane c < k writes slot c.
 template <int NV>  // E <= 16 * NV
 __device__ __forceinline__ void topk_row16(const float* L, int E, int k, bool valid,
                                            int32_t* __restrict__ ids_out,
                                            float* __restrict__ w_out) {
   const int c = threadIdx.x & 15;
-  float v[NV];
-  bool live[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = c + 16 * i;
-    live[i] = e < E;
-    v[i] = live[i] ? L[e] : 0.0f;
-  }
-  // w_j = exp(L_j - L_0) / sum_j' exp(L_j' - L_0): the softmax over all E
-  // restricted to the kept k and renormalised (the full denominator cancels);
-  // the sum runs over j in order in every lane.
-  float v0 = 0.0f, s = 0.0f;
-  float my_v = 0.0f;
-  int my_i = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k) {  // uniform across the row
-      float bv = 0.0f;
-      int bi = kNone;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const bool take = live[i] & ((bi == kNone) | (v[i] > bv));
-        bv = take ? v[i] : bv;
-        bi = take ? c + 16 * i : bi;
-      }
-      row16_step<0xB1>(bv, bi);
-      row16_step<0x4E>(bv, bi);
-      row16_step<0x141>(bv, bi);
-      row16_step<0x140>(bv, bi);
-      if (j == 0) v0 = bv;
-      s += expf(bv - v0);
-      my_v = c == j ? bv : my_v;
-      my_i = c == j ? bi : my_i;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) live[i] = live[i] & (bi != c + 16 * i);
-    }
-  }
+  int id_c;
+  float w_c;
+  topk_row16_slot<NV>(L, E, k, id_c, w_c);
   if (valid && c < k) {
-    ids_out[c] = my_i;
-    w_out[c] = expf(my_v - v0) / s;
+    ids_out[c] = id_c;
+    w_out[c] = w_c;
   }
 }
 
@@ -210,6 +239,10 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_bf16_kernel(
 
 // Barrier for LDS traffic only: waits for this wave's LDS accesses, not for
 // its global loads, which stay in flight across it.
+// s_waitcnt immediate for vmcnt(n), the other counters left alone
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | 0x70 | 0xF00; }
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   asm volatile("" ::: "memory");
@@ -232,7 +265,14 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_resident_bf16_kernel(
     float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ wts) {
   constexpr int EP = NET * 16 + 1;
   constexpr int NR = (16 * 16 * NET + 64 * kRouteWaves - 1) / (64 * kRouteWaves);
-  __shared__ float part[2][kRouteWaves][16][EP];
+  // LDS holds first the staged W_r (two buffers of KS KB per wave), then the
+  // groups' partial sums
+  constexpr bool STAGE = KS >= 2;
+  constexpr int PART_BYTES = 2 * kRouteWaves * 16 * EP * 4;
+  constexpr int STAGE_BYTES = STAGE ? 2 * kRouteWaves * KS * 1024 : 0;
+  __shared__ __align__(16) uint8_t lds[PART_BYTES > STAGE_BYTES ? PART_BYTES : STAGE_BYTES];
+  float(&part)[2][kRouteWaves][16][EP] =
+      *reinterpret_cast<float(*)[2][kRouteWaves][16][EP]>(lds);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, kq = (lane >> 4) * 8;
   const int k0 = wave * (KS * 32) + kq;     // this wave's columns, plus the lane's 8
@@ -240,11 +280,54 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_resident_bf16_kernel(
   if ((int)blockIdx.x >= ngroups) return;  // block-uniform
   // experts past E read a valid row; their results are dropped
   bf16x8 w[KS][NET];
+  if constexpr (STAGE) {
+    // W_r through LDS, one 16-expert tile per round, two rounds in flight:
+    // each load takes 8 rows x 128 B (whole cache lines; loading the
+    // fragments directly would take 16 rows x 64 B per instruction, half a
+    // line per row, which moves half as many bytes per cache request), and
+    // the fragments are then read from LDS in the product's layout.  A
+    // wave's slice of a row is KS * 64 B, bytes [wave KS 64, +KS 64) of it.
+    uint8_t* const sw = lds + wave * (2 * KS * 1024);
+    const uint8_t* const wb = reinterpret_cast<const uint8_t*>(wr);
+    auto issue = [&](int et) {
+      uint8_t* const dst = sw + (et & 1) * (KS * 1024);
 #pragma unroll
-  for (int et = 0; et < NET; ++et) {
-    const uint16_t* wp = wr + (size_t)min(et * 16 + r, E - 1) * d + k0;
+      for (int h = 0; h < 2; ++h) {
+        const int row = min(et * 16 + h * 8 + (lane >> 3), E - 1);
+        const uint8_t* src = wb + (size_t)row * d * 2 + wave * KS * 64 + (lane & 7) * 16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) w[ks][et] = as_bf16x8(ld_u32x4(wp + ks * 32));
+        for (int cc = 0; cc < KS / 2; ++cc)
+          __builtin_amdgcn_global_load_lds(src + cc * 128,
+                                           (lds_ptr_t)(dst + (h * (KS / 2) + cc) * 1024), 16, 0, 0);
+      }
+    };
+    issue(0);
+    if (NET > 1) issue(1);
+#pragma unroll
+    for (int et = 0; et < NET; ++et) {
+      if (et + 1 < NET) __builtin_amdgcn_s_waitcnt(vmcnt_imm(KS));  // tile et landed
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      const uint8_t* const src = sw + (et & 1) * (KS * 1024);
+      // row r = 8 h + r8 of the tile, K-chunk 4 ks + lane / 16 of the slice
+      const int h = (lane >> 3) & 1, r8 = lane & 7;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = (h * (KS / 2) + (ks >> 1)) * 1024 + (r8 * 8 + (ks & 1) * 4 + (lane >> 4)) * 16;
+        w[ks][et] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + off));
+      }
+      if (et + 2 < NET) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this buffer read out
+        issue(et + 2);
+      }
+    }
+    lds_barrier();  // every wave's staging read out before the partial sums land there
+  } else {
+#pragma unroll
+    for (int et = 0; et < NET; ++et) {
+      const uint16_t* wp = wr + (size_t)min(et * 16 + r, E - 1) * d + k0;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) w[ks][et] = as_bf16x8(ld_u32x4(wp + ks * 32));
+    }
   }
   // the (token, expert) entries this thread sums: idx = tid + 512 j
   int rt[NR], re[NR];
@@ -256,6 +339,27 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_resident_bf16_kernel(
     re[j] = idx < 16 * E ? idx - rt[j] * E : 0;
     rb[j] = (bias && rt[j] >= 0) ? bias[re[j]] : 0.0f;
   }
+  // A group's ids and weights are stored at the start of the next group,
+  // before its x loads are issued, by every lane of every wave (buffer
+  // stores; lanes with nothing to store point past the arrays, and such
+  // stores are dropped); the logits likewise, right after their sums (none
+  // without logits_out).  So the number of stores between a group's loads
+  // and their use is the same on every path.
+  constexpr uint32_t kDrop = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t ids_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(ids, 0, (int)((uint32_t)T * k * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wts_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(wts, 0, (int)((uint32_t)T * k * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t lg_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      logits_out, 0, logits_out ? (int)((uint32_t)T * E * 4) : 0, 0x00020000);
+  uint32_t p_off = kDrop;  // byte offset of this lane's pending slot
+  int p_id = 0;
+  float p_w = 0.0f;
+  auto flush = [&]() {
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)p_id, ids_rsrc, (int)p_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p_w), wts_rsrc, (int)p_off, 0, 0);
+    p_off = kDrop;
+  };
   auto load_x = [&](int g, bf16x8 (&xv)[KS]) {
     // rows past T read a valid row; their results are dropped
     const uint16_t* xp = x + (size_t)min(g * 16 + r, T - 1) * d + k0;
@@ -279,47 +383,60 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_resident_bf16_kernel(
     const int t0 = g * 16;
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
-      if (rt[j] >= 0) {
-        const int t = rt[j], e = re[j];
+      float v = 0.0f;
+      const int t = rt[j], e = re[j];
+      if (t >= 0) {
         float pv[kRouteWaves];
 #pragma unroll
         for (int w2 = 0; w2 < kRouteWaves; ++w2) pv[w2] = part[b][w2][t][e];
-        float v = pv[0];
+        v = pv[0];
 #pragma unroll
         for (int w2 = 1; w2 < kRouteWaves; ++w2) v += pv[w2];
         if (bias) v += rb[j];
         part[b][0][t][e] = v;
-        if (logits_out && t0 + t < T) logits_out[(size_t)(t0 + t) * E + e] = v;
       }
+      const uint32_t lo = (t >= 0 && t0 + t < T) ? (uint32_t)((t0 + t) * E + e) * 4 : kDrop;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), lg_rsrc, (int)lo, 0, 0);
     }
     lds_barrier();
     if (wave < 4) {  // one token per 16-lane row: waves 0..3 hold the group's 16 rows
-      const int t = wave * 4 + (lane >> 4);
-      const size_t tg = (size_t)min(t0 + t, T - 1);
-      topk_row16<NET>(&part[b][0][t][0], E, k, t0 + t < T, ids + tg * k, wts + tg * k);
+      const int t = wave * 4 + (lane >> 4), c = lane & 15;
+      topk_row16_slot<NET>(&part[b][0][t][0], E, k, p_id, p_w);
+      if (t0 + t < T && c < k) p_off = (uint32_t)((t0 + t) * k + c) * 4;
     }
     // the next group writes the other buffer; the one after passes that
     // group's first barrier, which every wave reaches only after this top-k
   };
-  // Two groups per trip, so that the register buffers swap without copies.
-  // The next group's loads are issued on every path (the last group of a
-  // block reads its own rows again, from cache), so the wait before a
-  // group's products leaves exactly the next group's loads in flight.
+  // Two groups per trip, so that the register buffers swap without copies;
+  // the loop has its only exit at the bottom (an exit in the middle turns,
+  // once the control flow is structured, into a path back to the top on
+  // which the other buffer's loads still count as in flight, and the top
+  // then waits for them).  In the loop every group's products start with the
+  // next group's loads in flight (after the last pair: the pair's second
+  // group again, from cache); an odd last group runs after the loop.
   bf16x8 xa[KS], xb[KS];
+  const int gs = (int)gridDim.x;
   int g = blockIdx.x;
   load_x(g, xa);
-  for (;;) {
-    int gn = g + (int)gridDim.x;
-    load_x(gn < ngroups ? gn : g, xb);
+  // The first group's rows arrive before the second group's are asked for:
+  // issued together, the two would share the memory system and the first
+  // group would wait for both.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  while (g + gs < ngroups) {
+    const int g2 = g + gs, g3 = g2 + gs;
+    flush();
+    load_x(g2, xb);
     group(g, 0, xa);
-    if (gn >= ngroups) break;
-    g = gn;
-    gn = g + (int)gridDim.x;
-    load_x(gn < ngroups ? gn : g, xa);
-    group(g, 1, xb);
-    if (gn >= ngroups) break;
-    g = gn;
+    flush();
+    load_x(g3 < ngroups ? g3 : g2, xa);
+    group(g2, 1, xb);
+    g = g3;
   }
+  if (g < ngroups) {
+    flush();
+    group(g, 0, xa);
+  }
+  flush();
 }
 
 // fp32 logits on the vector ALUs in a fixed order: lane l sums the rounded
@@ -409,10 +526,15 @@ void launch_route(const RouteArgs& a, hipStream_t stream) {
   const uint16_t* wr = static_cast<const uint16_t*>(a.wr);
   const int ngroups = (int)((a.T + 15) / 16);
   // router weights held in registers: up to 64 experts, d / 256 K-steps of 32
-  // per wave within the register budget of two waves per SIMD
+  // per wave within the register budget of two waves per SIMD.  It is the
+  // faster kernel at any token count: each block reads W_r once, in whole
+  // cache lines, where the other reads it in half lines.
   const int n_cu = device_cu_count();
-  if (ngroups > n_cu && a.E <= 64 && (a.d == 256 || a.d == 512 || a.d == 1024 || a.d == 2048)) {
-    const int grid_r = n_cu;
+  // (its stores are ranged buffer stores: byte offsets of ids, weights and
+  // logits within 2^31)
+  if (a.E <= 64 && (a.d == 256 || a.d == 512 || a.d == 1024 || a.d == 2048) &&
+      (int64_t)a.T * a.E * 4 < ((int64_t)1 << 31) && a.k <= a.E) {
+    const int grid_r = ngroups < n_cu ? ngroups : n_cu;
 #define MOE_ROUTE_RES(N, K)                                                                      \
   hipLaunchKernelGGL((route_resident_bf16_kernel<N, K>), dim3(grid_r), dim3(64 * kRouteWaves), 0, \
                      stream, x, wr, a.bias, (int)a.T, a.d, a.E, a.k, a.logits_out, a.ids, a.wts)
