@@ -11,7 +11,7 @@ namespace moe {
 // per-expert M-tile prefix table in units of this.
 constexpr int kBM = 256;
 // Assignments handled per block of the dispatch count/rank kernels (minimum).
-constexpr int kDispatchChunk = 1024;
+constexpr int kDispatchChunk = 256;
 // Tokens per block of the router.
 constexpr int kRouteTokens = 16;
 // Top-k upper limit.

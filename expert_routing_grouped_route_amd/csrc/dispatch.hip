@@ -69,9 +69,20 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
   __syncthreads();
   const int a0 = blockIdx.x * chunk, a1 = min(R, a0 + chunk);
-  for (int a = a0 + threadIdx.x; a < a1; a += 256) {
-    const int e = ids[a];
-    if ((unsigned)e < (unsigned)E && !is_condensed(ids, rep, k, a, e)) atomicAdd(&h[e], 1);
+  // one LDS atomic per distinct expert of a wave's 64 assignments: the lanes
+  // of an expert found by ballots over the bits of e, the lowest adding them
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t below = (1ull << (threadIdx.x & 63)) - 1ull;
+  for (int p = a0; p < a1; p += 256) {
+    const int a = p + (int)threadIdx.x;
+    const int e = a < a1 ? ids[a] : -1;
+    const bool ok = (unsigned)e < (unsigned)E && !is_condensed(ids, rep, k, a, e);
+    uint64_t peers = __ballot(ok);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t m = __ballot(ok && ((e >> bit) & 1));
+      peers &= ((e >> bit) & 1) ? m : ~m;
+    }
+    if (ok && (peers & below) == 0) atomicAdd(&h[e], __popcll(peers));
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) blk[(size_t)blockIdx.x * E + e] = h[e];
@@ -126,22 +137,39 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(
   __shared__ int buf[256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int a0 = blockIdx.x * chunk, a1 = min(R, a0 + chunk);
-  // expert e's total over all blocks and its count in the blocks before this one
+  // expert e's total over all blocks and its count in the blocks before this
+  // one: ng = 256 / E threads per expert, thread g of expert e summing the
+  // blocks g, g + ng, ..., sixteen loads in flight at a time; then the ng
+  // partial sums per expert (integers: the order does not matter)
   int total = 0, before = 0;
-  if (tid < E) {
-    int b = 0;
-    for (; b + 4 <= nblk; b += 4) {  // four independent loads in flight
-      const int c0 = blk[(size_t)(b + 0) * E + tid], c1 = blk[(size_t)(b + 1) * E + tid];
-      const int c2 = blk[(size_t)(b + 2) * E + tid], c3 = blk[(size_t)(b + 3) * E + tid];
-      before += (b + 0 < (int)blockIdx.x ? c0 : 0) + (b + 1 < (int)blockIdx.x ? c1 : 0) +
-                (b + 2 < (int)blockIdx.x ? c2 : 0) + (b + 3 < (int)blockIdx.x ? c3 : 0);
-      total += c0 + c1 + c2 + c3;
+  {
+    const int ng = 256 / E, e = tid % E, g = tid / E;
+    int tp = 0, bp = 0;
+    if (g < ng) {
+      constexpr int U = 16;
+      for (int b0 = g; b0 < nblk; b0 += U * ng) {
+        int c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int b = b0 + u * ng;
+          c[u] = b < nblk ? blk[(size_t)b * E + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          tp += c[u];
+          bp += b0 + u * ng < (int)blockIdx.x ? c[u] : 0;
+        }
+      }
     }
-    for (; b < nblk; ++b) {
-      const int c = blk[(size_t)b * E + tid];
-      before += b < (int)blockIdx.x ? c : 0;
-      total += c;
-    }
+    wc[0][tid] = tp;  // wc is free until the loop below
+    wc[1][tid] = bp;
+    __syncthreads();
+    if (tid < E)
+      for (int j = 0; j < ng; ++j) {
+        total += wc[0][j * E + tid];
+        before += wc[1][j * E + tid];
+      }
+    __syncthreads();
   }
   const int incl = block_inclusive_scan(tid < E ? total : 0, buf);
   if (tid < E) run[tid] = incl - total + before;
