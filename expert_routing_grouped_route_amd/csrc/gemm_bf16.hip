@@ -828,11 +828,23 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_km_bf16_kernel(SegKmArgs p)
   const int per_e = mt * ntl;
   const int L = slot_work(blockIdx.x, SEG_RUN);
   if (L >= p.E * per_e) return;
-  const int e = L / per_e, rem = L - e * per_e;
+  const int r = L / per_e, rem = L - r * per_e;
   const int m0 = (rem / ntl) * kBM, n0 = (rem % ntl) * BN;
-  // with slices, all "experts" share segment 0 and take slices of its K-steps
-  const int sg = p.slices > 1 ? 0 : e;
-  const int s0 = p.offsets[sg], ne = p.offsets[sg + 1] - s0;
+  // the r-th expert in the records' order (the tiles of the longest K loops
+  // first, so that the launch does not end on them), or expert r; with
+  // slices, all "experts" share segment 0 and take slices of its K-steps
+  int e, s0, ne;
+  if (p.rec) {
+    const int4 rc = *reinterpret_cast<const int4*>(p.rec + 4 * r);
+    e = rc.x;
+    s0 = rc.y;
+    ne = rc.z;
+  } else {
+    e = r;
+    const int sg = p.slices > 1 ? 0 : e;
+    s0 = p.offsets[sg];
+    ne = p.offsets[sg + 1] - s0;
+  }
   const int kpe = (ne + BK - 1) / BK;  // K-steps per K block
   const int nks = 2 * kpe;
   const int g0 = p.slices > 1 ? (int)((int64_t)e * nks / p.slices) : 0;
@@ -977,6 +989,24 @@ bool seg_gemm_km_fits(const SegKmArgs& a, int64_t max_rows) {
   // descriptor ranges and offsets of one expert's rows (at most max_rows)
   const uint64_t lim = 1ull << 32;
   return (uint64_t)max_rows * a.x_ld * 2 + 1024 < lim && (uint64_t)max_rows * a.w_ld * 2 + 1024 < lim;
+}
+
+__global__ __launch_bounds__(256) void seg_order_kernel(const int32_t* __restrict__ off, int E,
+                                                        int32_t* __restrict__ rec) {
+  __shared__ int cnt[256];
+  for (int e = threadIdx.x; e < E; e += 256) cnt[e] = off[e + 1] - off[e];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    const int c = cnt[e];
+    int rank = 0;
+    for (int j = 0; j < E; ++j) rank += (cnt[j] > c) | ((cnt[j] == c) & (j < e));
+    *reinterpret_cast<int4*>(rec + 4 * rank) = make_int4(e, off[e], c, 0);
+  }
+}
+
+void launch_seg_order(const int32_t* offsets, int E, int32_t* rec, hipStream_t stream) {
+  if (E <= 0 || E > 256) return;
+  hipLaunchKernelGGL(seg_order_kernel, dim3(1), dim3(256), 0, stream, offsets, E, rec);
 }
 
 void launch_seg_gemm_km_bf16(const SegKmArgs& a, hipStream_t stream) {

@@ -327,7 +327,7 @@ moe_status_t layer_fwd(const moe_dims_t* dims, const void* x, const void* w_rout
 // forward layout, then the backward scratch.
 struct BLayout {
   size_t xs, prefix, G, U, Ar, Abf, dA, y, dY, dXs, dw, dl, dls, rpart, Gs, Us, As, Asbf, dAs, dxs,
-      dGU, poff, tA, tB, off1, poff1, tiles1, off2, tiles2, wsdT,
+      dGU, poff, srec, tA, tB, off1, poff1, tiles1, off2, tiles2, wsdT,
       wsgT, wsuT, dOp, sGU, poffS, kpart, total;
   int64_t seg_ld;
   int ksplit;
@@ -370,6 +370,7 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.seg_ld = ((int64_t)(2 * (R + 63 * (size_t)D.E)) + 63) / 64 * 64;
   const size_t rows = std::max(std::max(d, I), (size_t)D.n_shared * Is);
   B.poff = take(bf ? ((size_t)D.E + 1) * 4 : 0);
+  B.srec = take(bf ? (size_t)D.E * 16 : 0);
   B.off1 = take(bf ? 8 : 0);
   B.poff1 = take(bf ? 8 : 0);
   const bool bsh = bf && D.n_shared > 0;
@@ -476,6 +477,7 @@ moe_status_t layer_bwd(const moe_dims_t* dims, const void* x, const void* w_rout
     ba.dOp = at<uint16_t>(ws, B.dOp);
     ba.dGU = at<uint16_t>(ws, B.dGU);
     ba.poff = at<int32_t>(ws, B.poff);
+    ba.srec = at<int32_t>(ws, B.srec);
     ba.seg_ld = B.seg_ld;
     ba.tA = at<uint16_t>(ws, B.tA);
     ba.tB = at<uint16_t>(ws, B.tB);
