@@ -120,6 +120,39 @@ __device__ __forceinline__ void lds_read_tr16_frags(uint32_t a0, uint32_t a1, bf
   f1 = __builtin_bit_cast(bf16x8, u32x4{l1.x, l1.y, h1.x, h1.y});
 }
 
+// The same for six fragments (both operands of a K-major sub-step) in one
+// block: twelve reads, then one wait, so a wave waits for the LDS once per
+// sub-step instead of once per pair of fragments.
+__device__ __forceinline__ void lds_read_tr16_frags6(uint32_t a0, uint32_t a1, uint32_t a2,
+                                                     uint32_t a3, uint32_t a4, uint32_t a5,
+                                                     bf16x8 (&f)[6]) {
+  u32x2 l0, h0, l1, h1, l2, h2, l3, h3, l4, h4, l5, h5;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %12\n\t"
+      "ds_read_b64_tr_b16 %1, %12 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %13\n\t"
+      "ds_read_b64_tr_b16 %3, %13 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %14\n\t"
+      "ds_read_b64_tr_b16 %5, %14 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %15\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %8, %16\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %10, %17\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1), "=&v"(l2), "=&v"(h2), "=&v"(l3), "=&v"(h3),
+        "=&v"(l4), "=&v"(h4), "=&v"(l5), "=&v"(h5)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a4), "v"(a5)
+      : "memory");
+  f[0] = __builtin_bit_cast(bf16x8, u32x4{l0.x, l0.y, h0.x, h0.y});
+  f[1] = __builtin_bit_cast(bf16x8, u32x4{l1.x, l1.y, h1.x, h1.y});
+  f[2] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+  f[3] = __builtin_bit_cast(bf16x8, u32x4{l3.x, l3.y, h3.x, h3.y});
+  f[4] = __builtin_bit_cast(bf16x8, u32x4{l4.x, l4.y, h4.x, h4.y});
+  f[5] = __builtin_bit_cast(bf16x8, u32x4{l5.x, l5.y, h5.x, h5.y});
+}
+
 // Hardware barrier with compiler-only fences: the waits that make LDS data
 // visible are issued explicitly before it.
 __device__ __forceinline__ void block_barrier() {
@@ -478,10 +511,12 @@ __device__ __forceinline__ void run_tile(const BTile& t, uint8_t* smem, float* g
     const uint8_t* xs_ = smem + (kt % NXB) * X_BYTES;
     const uint8_t* ws_ = smem + W_BASE + (kt % NWB) * W_BYTES;
     const int c = (((ks * 2 + kg) ^ cx) << 4);
-    if (KX) {
-      const uint32_t xb = (uint32_t)(uintptr_t)xs_ + ks * 16 * (kBM * 2);  // LDS byte address
-      lds_read_tr16_frags(xb + a_off[0], xb + a_off[1], f[0], f[1]);
-      lds_read_tr16_frags(xb + a_off[2], xb + a_off[3], f[2], f[3]);
+    if (KX) {  // (KX implies WT) both operands in one block
+      const uint32_t xb = (uint32_t)(uintptr_t)xs_ + ks * 16 * (kBM * 2);  // LDS byte addresses
+      const uint32_t wb = (uint32_t)(uintptr_t)ws_ + ks * 16 * (BN * 2);
+      lds_read_tr16_frags6(xb + a_off[0], xb + a_off[1], xb + a_off[2], xb + a_off[3],
+                           wb + b_off[0], wb + b_off[1], f);
+      return;
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) f[i] = as_bf16x8(ld_u32x4(xs_ + a_off[i] + c));
