@@ -27,7 +27,7 @@ struct BwdArgs {
   uint16_t* Abf;                           // bf16: [R,I] the SwiGLU product in bf16
   uint16_t* dGU;                           // bf16: [R, 4I] rows [dG hi | dG lo | dU hi | dU lo]
   int32_t* poff;                           // bf16: [E+1] padded per-expert parts (seg_offsets_kernel)
-  int32_t* srec;                           // bf16: [E][4] experts by falling row count (launch_seg_order)
+  int32_t* srec;                           // bf16: [8][cap][4] experts per XCD (launch_seg_sched)
   int64_t seg_ld;                          // bf16: row length of tA and tB (>= poff[E])
   uint16_t *tA, *tB;                       // bf16: [max(d, I, ns*Is), seg_ld] transposed operands
   int32_t *off1, *poff1;                   // bf16: [2] each, the T rows as one segment

@@ -1166,11 +1166,12 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
     if (R > 0)
       hipLaunchKernelGGL(gather_split_rows_kernel, dim3((unsigned)std::min<int64_t>(R, 16384)),
                          dim3(256), 0, s, a.dout, a.perm, a.w, a.k, R, d, a.tA);
-    // the experts' tiles largest first (their K loops run over the expert's
-    // rows, so the tiles of a hot expert are the longest)
-    launch_seg_order(a.offsets, E, a.srec, s);
-    launch_seg_gemm_km_bf16(
-        SegKmArgs{a.tA, 2 * (int64_t)d, d, a.Abf, I, a.offsets, a.dw_down, E, d, I, 0, a.srec}, s);
+    // all tiles of an expert on one XCD, the experts spread over the XCDs by
+    // cost (a tile's K loop runs over its expert's rows)
+    launch_seg_sched(a.offsets, E, a.srec, s);
+    launch_seg_gemm_km_bf16(SegKmArgs{a.tA, 2 * (int64_t)d, d, a.Abf, I, a.offsets, a.dw_down, E,
+                                      d, I, 0, a.srec, seg_sched_cap(E)},
+                            s);
   } else if (bf) {
     hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(64), 0, s, a.offsets, E, a.poff);
     launch_seg_transpose_gather(a.dout, d, a.perm, a.w, a.k, a.offsets, a.poff, E, a.seg_ld,
@@ -1196,11 +1197,11 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   if (km) {  // dGU rows: dG hi, dG lo, dU hi, dU lo
     const int64_t ld4 = 4 * (int64_t)I;
     launch_seg_gemm_km_bf16(SegKmArgs{a.dGU, ld4, I, static_cast<const uint16_t*>(a.xs), d,
-                                      a.offsets, a.dw_gate, E, I, d, 0, a.srec},
+                                      a.offsets, a.dw_gate, E, I, d, 0, a.srec, seg_sched_cap(E)},
                             s);
     launch_seg_gemm_km_bf16(SegKmArgs{a.dGU + 2 * (size_t)I, ld4, I,
                                       static_cast<const uint16_t*>(a.xs), d, a.offsets, a.dw_up, E,
-                                      I, d, 0, a.srec},
+                                      I, d, 0, a.srec, seg_sched_cap(E)},
                             s);
   } else if (bf) {
     launch_seg_transpose(a.xs, false, d, a.offsets, a.poff, E, a.seg_ld, a.tB, s);

@@ -861,25 +861,33 @@ __global__ __launch_bounds__(NTHREADS) void seg_gemm_km_bf16_kernel(SegKmArgs p)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int mt = (p.M + kBM - 1) / kBM, ntl = (p.N + BN - 1) / BN;
   const int per_e = mt * ntl;
-  const int L = slot_work(blockIdx.x, SEG_RUN);
-  if (L >= p.E * per_e) return;
-  const int r = L / per_e, rem = L - r * per_e;
-  const int m0 = (rem / ntl) * kBM, n0 = (rem % ntl) * BN;
-  // the r-th expert in the records' order (the tiles of the longest K loops
-  // first, so that the launch does not end on them), or expert r; with
-  // slices, all "experts" share segment 0 and take slices of its K-steps
-  int e, s0, ne;
+  // With the schedule (p.rec): block b runs on XCD b % 8 (blocks are dealt
+  // to the XCDs round-robin) and takes tile j % per_e of the (j / per_e)-th
+  // expert in that XCD's list, j = b / 8: all tiles of an expert on one XCD,
+  // so the tiles running there together share each K-step's operand rows in
+  // its L2 instead of every XCD fetching them.  Without it: expert L / per_e,
+  // runs of SEG_RUN works per XCD; with slices, all "experts" share segment
+  // 0 and take slices of its K-steps.
+  int e, s0, ne, rem;
   if (p.rec) {
-    const int4 rc = *reinterpret_cast<const int4*>(p.rec + 4 * r);
+    const int j = blockIdx.x >> 3, i = j / per_e;
+    if (i >= p.cap) return;
+    const int4 rc = *reinterpret_cast<const int4*>(p.rec + 4 * ((blockIdx.x & 7) * p.cap + i));
+    if (!rc.w) return;  // no expert in this place of the list
     e = rc.x;
     s0 = rc.y;
     ne = rc.z;
+    rem = j - i * per_e;
   } else {
-    e = r;
+    const int L = slot_work(blockIdx.x, SEG_RUN);
+    if (L >= p.E * per_e) return;
+    e = L / per_e;
+    rem = L - e * per_e;
     const int sg = p.slices > 1 ? 0 : e;
     s0 = p.offsets[sg];
     ne = p.offsets[sg + 1] - s0;
   }
+  const int m0 = (rem / ntl) * kBM, n0 = (rem % ntl) * BN;
   const int kpe = (ne + BK - 1) / BK;  // K-steps per K block
   const int nks = 2 * kpe;
   const int g0 = p.slices > 1 ? (int)((int64_t)e * nks / p.slices) : 0;
@@ -1026,22 +1034,55 @@ bool seg_gemm_km_fits(const SegKmArgs& a, int64_t max_rows) {
   return (uint64_t)max_rows * a.x_ld * 2 + 1024 < lim && (uint64_t)max_rows * a.w_ld * 2 + 1024 < lim;
 }
 
-__global__ __launch_bounds__(256) void seg_order_kernel(const int32_t* __restrict__ off, int E,
-                                                        int32_t* __restrict__ rec) {
-  __shared__ int cnt[256];
-  for (int e = threadIdx.x; e < E; e += 256) cnt[e] = off[e + 1] - off[e];
+// Experts to XCDs, longest first: expert e costs 2 ceil(n_e / 64) K-steps
+// per tile plus about five for a tile's start and epilogue (every expert has
+// the same number of tiles), experts are taken by falling cost (ties by
+// index) and each goes to the XCD with the least cost so far among those
+// with fewer than cap experts (ties to the lowest XCD).  One thread makes
+// the choices (at most 256 experts, 8 XCDs); the records are written by all.
+__global__ __launch_bounds__(256) void seg_sched_kernel(const int32_t* __restrict__ off, int E,
+                                                        int cap, int32_t* __restrict__ rec) {
+  __shared__ int cost[256], order[256], place[kSegXcds * kSegCapMax];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) cost[e] = 2 * ((off[e + 1] - off[e] + BK - 1) / BK) + 5;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
-    const int c = cnt[e];
+  for (int e = tid; e < E; e += 256) {
+    const int c = cost[e];
     int rank = 0;
-    for (int j = 0; j < E; ++j) rank += (cnt[j] > c) | ((cnt[j] == c) & (j < e));
-    *reinterpret_cast<int4*>(rec + 4 * rank) = make_int4(e, off[e], c, 0);
+    for (int j = 0; j < E; ++j) rank += (cost[j] > c) | ((cost[j] == c) & (j < e));
+    order[rank] = e;
+  }
+  for (int i = tid; i < kSegXcds * cap; i += 256) place[i] = -1;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t load[kSegXcds];
+    int n[kSegXcds];
+    for (int x = 0; x < kSegXcds; ++x) {
+      load[x] = 0;
+      n[x] = 0;
+    }
+    for (int r = 0; r < E; ++r) {
+      const int e = order[r];
+      int best = -1;
+      for (int x = 0; x < kSegXcds; ++x)
+        if (n[x] < cap && (best < 0 || load[x] < load[best])) best = x;
+      place[best * cap + n[best]] = e;
+      ++n[best];
+      load[best] += cost[e];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kSegXcds * cap; i += 256) {
+    const int e = place[i];
+    *reinterpret_cast<int4*>(rec + 4 * i) =
+        e >= 0 ? make_int4(e, off[e], off[e + 1] - off[e], 1) : make_int4(0, 0, 0, 0);
   }
 }
 
-void launch_seg_order(const int32_t* offsets, int E, int32_t* rec, hipStream_t stream) {
+void launch_seg_sched(const int32_t* offsets, int E, int32_t* rec, hipStream_t stream) {
   if (E <= 0 || E > 256) return;
-  hipLaunchKernelGGL(seg_order_kernel, dim3(1), dim3(256), 0, stream, offsets, E, rec);
+  hipLaunchKernelGGL(seg_sched_kernel, dim3(1), dim3(256), 0, stream, offsets, E,
+                     seg_sched_cap(E), rec);
 }
 
 void launch_seg_gemm_km_bf16(const SegKmArgs& a, hipStream_t stream) {
@@ -1049,8 +1090,10 @@ void launch_seg_gemm_km_bf16(const SegKmArgs& a, hipStream_t stream) {
   if (tiles == 0) return;
   // outputs larger than the 256 MB MALL take non-temporal stores
   const bool nt = (uint64_t)a.E * a.M * a.N * 4 > (256ull << 20);
+  const int64_t per_e = tiles / a.E;
+  const int64_t grid = a.rec ? (int64_t)kSegXcds * a.cap * per_e : pad_slots(tiles, SEG_RUN);
   hipLaunchKernelGGL(nt ? seg_gemm_km_bf16_kernel<true> : seg_gemm_km_bf16_kernel<false>,
-                     dim3((unsigned)pad_slots(tiles, SEG_RUN)), dim3(NTHREADS), 0, stream, a);
+                     dim3((unsigned)grid), dim3(NTHREADS), 0, stream, a);
 }
 
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream) {

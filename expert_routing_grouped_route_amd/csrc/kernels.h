@@ -150,14 +150,19 @@ struct SegKmArgs {
   // slices > 1: one segment (offsets[0..1]) whose 2 * ceil(rows / 64) K-steps
   // are cut into E = slices contiguous ranges, range e summed into out[e]
   int slices;
-  // or null: [E][4] records {expert, first row, rows, 0} in the order the
-  // experts' tiles are taken (launch_seg_order: most rows first)
+  // or null: the schedule of launch_seg_sched, [8][cap][4] records
+  // {expert, first row, rows, 1} (or zeros) listing the experts each XCD
+  // takes, all of an expert's tiles on one XCD
   const int32_t* rec;
+  int cap;                // places per XCD in rec: seg_sched_cap(E)
 };
 bool seg_gemm_km_fits(const SegKmArgs& a, int64_t max_rows);
-// The records of SegKmArgs::rec from offsets [E+1] (E <= 256): experts by
-// falling row count, ties by index.
-void launch_seg_order(const int32_t* offsets, int E, int32_t* rec, hipStream_t stream);
+// The schedule of SegKmArgs::rec from offsets [E+1] (E <= 256): experts to
+// the 8 XCDs by falling cost, each to the least loaded XCD with room.
+constexpr int kSegXcds = 8;
+constexpr int kSegCapMax = 256 / kSegXcds + 2;
+inline int seg_sched_cap(int E) { return (E + kSegXcds - 1) / kSegXcds + 2; }
+void launch_seg_sched(const int32_t* offsets, int E, int32_t* rec, hipStream_t stream);
 void launch_seg_gemm_km_bf16(const SegKmArgs& a, hipStream_t stream);
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream);
 void launch_gate_up_f32(const FfnArgs& a, hipStream_t stream);

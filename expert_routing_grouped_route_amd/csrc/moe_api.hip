@@ -370,7 +370,7 @@ BLayout backward_layout_of(const moe_dims_t& D) {
   B.seg_ld = ((int64_t)(2 * (R + 63 * (size_t)D.E)) + 63) / 64 * 64;
   const size_t rows = std::max(std::max(d, I), (size_t)D.n_shared * Is);
   B.poff = take(bf ? ((size_t)D.E + 1) * 4 : 0);
-  B.srec = take(bf ? (size_t)D.E * 16 : 0);
+  B.srec = take(bf ? (size_t)kSegXcds * seg_sched_cap((int)D.E) * 16 : 0);
   B.off1 = take(bf ? 8 : 0);
   B.poff1 = take(bf ? 8 : 0);
   const bool bsh = bf && D.n_shared > 0;
