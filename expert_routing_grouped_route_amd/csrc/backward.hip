@@ -24,6 +24,7 @@
 // element is summed in a fixed order and no atomics are used, so results are
 // reproducible bit for bit.
 #include <algorithm>
+#include <climits>
 
 #include "common.h"
 #include "kernels.h"
@@ -828,17 +829,101 @@ void launch_split_rows(const float* v, int64_t rows, int cols, uint16_t* out, in
                      dim3(256), 0, s, v, rows, cols, out, out_ld, hi_col, lo_col);
 }
 
+// Experts to XCDs, longest first: expert e costs 2 ceil(n_e / 64) K-steps
+// per tile plus about five for a tile's start and epilogue (every expert has
+// the same number of tiles), experts are taken by falling cost (ties by
+// index) and each goes to the XCD with the least cost so far among those
+// with fewer than cap experts (ties to the lowest XCD).  The choices are made
+// by one wave, lane x < 8 holding XCD x's cost and count: the minimum over
+// the eight lanes through DPP moves, then the lowest lane holding it from a
+// ballot; the sorted costs and experts sit in registers, lane l holding
+// places l, l + 64, ...  The records are written by all threads.
+template <int CTRL>
+__device__ __forceinline__ int sched_dpp(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+
+// The whole block (256 threads) makes the schedule.
+__device__ void seg_sched_block(const int32_t* __restrict__ off, int E, int cap,
+                                int32_t* __restrict__ rec) {
+  __shared__ int cost[256], ocost[256], order[256], place[kSegXcds * kSegCapMax];
+  if (E <= 0 || E > 256) return;  // (the layer's dimension checks keep E <= 256)
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) cost[e] = 2 * ((off[e + 1] - off[e] + 63) / 64) + 5;
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    const int c = cost[e];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < E; ++j) rank += (cost[j] > c) | ((cost[j] == c) & (j < e));
+    order[rank] = e;
+    ocost[rank] = c;
+  }
+  for (int i = tid; i < kSegXcds * cap; i += 256) place[i] = -1;
+  __syncthreads();
+  if (tid < 64) {
+    int oc[4], oe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = tid + 64 * i;
+      oc[i] = r < E ? ocost[r] : 0;
+      oe[i] = r < E ? order[r] : 0;
+    }
+    const bool xl = tid < kSegXcds;  // this lane stands for XCD tid
+    int load = 0, n = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jn = min(64, E - 64 * i);
+      for (int j = 0; j < jn; ++j) {
+        const int key = xl && n < cap ? load : INT_MAX;
+        int m = min(key, sched_dpp<0xB1>(key));  // lanes xor 1
+        m = min(m, sched_dpp<0x4E>(m));          // lanes xor 2
+        m = min(m, sched_dpp<0x141>(m));         // lane i with 7 - i of its eight
+        const unsigned long long b = __ballot(xl && key == m);
+        if (tid == __builtin_ctzll(b)) {
+          place[tid * cap + n] = __builtin_amdgcn_readlane(oe[i], j);
+          ++n;
+          load += __builtin_amdgcn_readlane(oc[i], j);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kSegXcds * cap; i += 256) {
+    const int e = place[i];
+    *reinterpret_cast<int4*>(rec + 4 * i) =
+        e >= 0 ? make_int4(e, off[e], off[e + 1] - off[e], 1) : make_int4(0, 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(256) void seg_sched_kernel(const int32_t* __restrict__ off, int E,
+                                                        int cap, int32_t* __restrict__ rec) {
+  seg_sched_block(off, E, cap, rec);
+}
+
+
 // Sorted row r of the gate-weighted dout, w[perm[r]] * v[perm[r] / k], as its
 // bf16 hi parts (columns 0..cols-1 of out row r) and lo parts (cols..2 cols-1),
-// rounded as split_rows_bf16_kernel rounds.
+// rounded as split_rows_bf16_kernel rounds.  With sched_rec, block 0 makes
+// the weight-gradient schedule instead (seg_sched_block, from the expert
+// offsets sched_off) while the other blocks take the rows: dispatched first,
+// it finishes under their work.
 __global__ __launch_bounds__(256) void gather_split_rows_kernel(const float* __restrict__ v,
                                                                 const int32_t* __restrict__ perm,
                                                                 const float* __restrict__ w, int k,
                                                                 int64_t rows, int cols,
-                                                                uint16_t* __restrict__ out) {
+                                                                uint16_t* __restrict__ out,
+                                                                const int32_t* __restrict__ sched_off,
+                                                                int sched_E,
+                                                                int32_t* __restrict__ sched_rec) {
 #pragma clang fp contract(off)  // the lo parts come from the rounded products
+  const int b0 = sched_rec ? 1 : 0;
+  if ((int)blockIdx.x < b0) {
+    seg_sched_block(sched_off, sched_E, seg_sched_cap(sched_E), sched_rec);
+    return;
+  }
   const int c4 = cols / 4;
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+  for (int64_t r = blockIdx.x - b0; r < rows; r += gridDim.x - b0) {
     const int a = perm[r];
     const float sc = w[a];
     const f32x4* src = reinterpret_cast<const f32x4*>(v + (int64_t)(a / k) * cols);
@@ -1034,6 +1119,12 @@ void launch_transpose_bf16(const void* in, int E, int P, int Q, void* out, hipSt
 
 }  // namespace
 
+void launch_seg_sched(const int32_t* offsets, int E, int32_t* rec, hipStream_t stream) {
+  if (E <= 0 || E > 256) return;
+  hipLaunchKernelGGL(seg_sched_kernel, dim3(1), dim3(256), 0, stream, offsets, E,
+                     seg_sched_cap(E), rec);
+}
+
 void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   const int64_t T = a.T, R = a.T * a.k;
   const int d = a.d, I = a.I, E = a.E;
@@ -1163,12 +1254,16 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
                                              E, 0, 0},
                                    R);
   if (km) {
+    // the gathered dout rows, and (block 0 of the same launch) the schedule
+    // of the weight-gradient tiles: all tiles of an expert on one XCD, the
+    // experts spread over the XCDs by cost (a tile's K loop runs over its
+    // expert's rows)
     if (R > 0)
-      hipLaunchKernelGGL(gather_split_rows_kernel, dim3((unsigned)std::min<int64_t>(R, 16384)),
-                         dim3(256), 0, s, a.dout, a.perm, a.w, a.k, R, d, a.tA);
-    // all tiles of an expert on one XCD, the experts spread over the XCDs by
-    // cost (a tile's K loop runs over its expert's rows)
-    launch_seg_sched(a.offsets, E, a.srec, s);
+      hipLaunchKernelGGL(gather_split_rows_kernel, dim3((unsigned)std::min<int64_t>(R, 16384) + 1),
+                         dim3(256), 0, s, a.dout, a.perm, a.w, a.k, R, d, a.tA, a.offsets, E,
+                         a.srec);
+    else
+      launch_seg_sched(a.offsets, E, a.srec, s);
     launch_seg_gemm_km_bf16(SegKmArgs{a.tA, 2 * (int64_t)d, d, a.Abf, I, a.offsets, a.dw_down, E,
                                       d, I, 0, a.srec, seg_sched_cap(E)},
                             s);

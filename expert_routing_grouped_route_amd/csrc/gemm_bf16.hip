@@ -41,7 +41,6 @@
 // the tile table the dispatch scan wrote.  Each XCD takes runs of 8
 // consecutive works, which share A-row tiles and weight slices in its L2.
 #include <algorithm>
-#include <climits>
 #include <type_traits>
 
 #include "grouped_gemm.h"
@@ -1033,77 +1032,6 @@ bool seg_gemm_km_fits(const SegKmArgs& a, int64_t max_rows) {
   // descriptor ranges and offsets of one expert's rows (at most max_rows)
   const uint64_t lim = 1ull << 32;
   return (uint64_t)max_rows * a.x_ld * 2 + 1024 < lim && (uint64_t)max_rows * a.w_ld * 2 + 1024 < lim;
-}
-
-// Experts to XCDs, longest first: expert e costs 2 ceil(n_e / 64) K-steps
-// per tile plus about five for a tile's start and epilogue (every expert has
-// the same number of tiles), experts are taken by falling cost (ties by
-// index) and each goes to the XCD with the least cost so far among those
-// with fewer than cap experts (ties to the lowest XCD).  The choices are made
-// by one wave, lane x < 8 holding XCD x's cost and count: the minimum over
-// the eight lanes through DPP moves, then the lowest lane holding it from a
-// ballot; the sorted costs and experts sit in registers, lane l holding
-// places l, l + 64, ...  The records are written by all threads.
-template <int CTRL>
-__device__ __forceinline__ int sched_dpp(int v) {
-  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
-}
-
-__global__ __launch_bounds__(256) void seg_sched_kernel(const int32_t* __restrict__ off, int E,
-                                                        int cap, int32_t* __restrict__ rec) {
-  __shared__ int cost[256], ocost[256], order[256], place[kSegXcds * kSegCapMax];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 256) cost[e] = 2 * ((off[e + 1] - off[e] + BK - 1) / BK) + 5;
-  __syncthreads();
-  for (int e = tid; e < E; e += 256) {
-    const int c = cost[e];
-    int rank = 0;
-#pragma unroll 8
-    for (int j = 0; j < E; ++j) rank += (cost[j] > c) | ((cost[j] == c) & (j < e));
-    order[rank] = e;
-    ocost[rank] = c;
-  }
-  for (int i = tid; i < kSegXcds * cap; i += 256) place[i] = -1;
-  __syncthreads();
-  if (tid < 64) {
-    int oc[4], oe[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = tid + 64 * i;
-      oc[i] = r < E ? ocost[r] : 0;
-      oe[i] = r < E ? order[r] : 0;
-    }
-    const bool xl = tid < kSegXcds;  // this lane stands for XCD tid
-    int load = 0, n = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int jn = min(64, E - 64 * i);
-      for (int j = 0; j < jn; ++j) {
-        const int key = xl && n < cap ? load : INT_MAX;
-        int m = min(key, sched_dpp<0xB1>(key));  // lanes xor 1
-        m = min(m, sched_dpp<0x4E>(m));          // lanes xor 2
-        m = min(m, sched_dpp<0x141>(m));         // lane i with 7 - i of its eight
-        const unsigned long long b = __ballot(xl && key == m);
-        if (tid == __builtin_ctzll(b)) {
-          place[tid * cap + n] = __builtin_amdgcn_readlane(oe[i], j);
-          ++n;
-          load += __builtin_amdgcn_readlane(oc[i], j);
-        }
-      }
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < kSegXcds * cap; i += 256) {
-    const int e = place[i];
-    *reinterpret_cast<int4*>(rec + 4 * i) =
-        e >= 0 ? make_int4(e, off[e], off[e + 1] - off[e], 1) : make_int4(0, 0, 0, 0);
-  }
-}
-
-void launch_seg_sched(const int32_t* offsets, int E, int32_t* rec, hipStream_t stream) {
-  if (E <= 0 || E > 256) return;
-  hipLaunchKernelGGL(seg_sched_kernel, dim3(1), dim3(256), 0, stream, offsets, E,
-                     seg_sched_cap(E), rec);
 }
 
 void launch_seg_gemm_km_bf16(const SegKmArgs& a, hipStream_t stream) {

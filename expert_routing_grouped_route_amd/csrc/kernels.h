@@ -161,7 +161,7 @@ bool seg_gemm_km_fits(const SegKmArgs& a, int64_t max_rows);
 // the 8 XCDs by falling cost, each to the least loaded XCD with room.
 constexpr int kSegXcds = 8;
 constexpr int kSegCapMax = 256 / kSegXcds + 2;
-inline int seg_sched_cap(int E) { return (E + kSegXcds - 1) / kSegXcds + 2; }
+constexpr int seg_sched_cap(int E) { return (E + kSegXcds - 1) / kSegXcds + 2; }
 void launch_seg_sched(const int32_t* offsets, int E, int32_t* rec, hipStream_t stream);
 void launch_seg_gemm_km_bf16(const SegKmArgs& a, hipStream_t stream);
 void launch_down_bf16(const FfnArgs& a, hipStream_t stream);
