@@ -42,18 +42,6 @@ __device__ __forceinline__ float load_elem(const void* p, int64_t i) {
   return static_cast<const float*>(p)[i];
 }
 
-// Group g's M-tiles of `tile` rows start at prefix[g]; prefix[G] is the total.
-__global__ __launch_bounds__(64) void tile_prefix_kernel(const int32_t* __restrict__ off, int G,
-                                                         int tile, int32_t* __restrict__ prefix) {
-  if (threadIdx.x != 0) return;
-  int acc = 0;
-  for (int g = 0; g < G; ++g) {
-    prefix[g] = acc;
-    acc += (off[g + 1] - off[g] + tile - 1) / tile;
-  }
-  prefix[G] = acc;
-}
-
 // C(m, n) = [C(m, n) +] sum_k A(m, k) B(k, n), with A(m, k) at
 // A[g*a_g + m*a_sm + k*a_sk] and so on.  RAGGED_K false: group g owns the
 // rows off[g] .. off[g+1] of A and C (global row numbers) and tiles come from
@@ -361,7 +349,7 @@ struct GemmOp {
   const void* B; bool b_bf16; int64_t b_sk, b_sn, b_g;
   float* C; int64_t c_sm, c_sn, c_g;
   const int32_t* off;     // ragged offsets [G+1] or null
-  const int32_t* prefix;  // ragged M: M-tile prefix [G+1] (from tile_prefix_kernel)
+  const int32_t* prefix;  // ragged M: M-tile prefix [G+1] (launch_segment_tables)
   int G, ext;             // groups; extent when off is null
   int64_t m_bound;        // ragged M: bound of the M-tiles over all groups
   int M, N, K;
@@ -958,24 +946,6 @@ __global__ __launch_bounds__(64) void seg_offsets_kernel(const int32_t* __restri
   poff[E] = acc;
 }
 
-// One segment of T rows: off = {0, T}, poff = {0, 2 * roundup(T, 64)}.
-__global__ __launch_bounds__(64) void single_seg_offsets_kernel(int T, int32_t* __restrict__ off,
-                                                                int32_t* __restrict__ poff) {
-  if (threadIdx.x != 0) return;
-  off[0] = 0;
-  off[1] = T;
-  poff[0] = 0;
-  poff[1] = 2 * ((T + 63) / 64 * 64);
-}
-
-// Two row groups of T rows each: off = {0, T, 2T}.
-__global__ __launch_bounds__(64) void two_seg_offsets_kernel(int T, int32_t* __restrict__ off) {
-  if (threadIdx.x != 0) return;
-  off[0] = 0;
-  off[1] = T;
-  off[2] = 2 * T;
-}
-
 // S slices of one segment's reduction index, 2 * roundup(T, 64) columns:
 // slice e covers the 64-column steps [e*n/S, (e+1)*n/S) of its n steps.
 __global__ __launch_bounds__(64) void split_seg_offsets_kernel(int T, int S,
@@ -1133,8 +1103,11 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
   // (the caller's choice, for comparisons of the two)
   const bool mf = !a.valu;
   const int tt = mf ? MT : GT;
-  // M-tile prefix of the experts' row segments
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.offsets, E, tt, a.prefix);
+  // M-tile prefix of the experts' row segments, and (bf16 layers with shared
+  // experts) the one- and two-segment tables of the shared experts' products
+  const bool shtab = bf && a.ns > 0;
+  launch_segment_tables(a.offsets, E, tt, a.prefix, T, shtab ? a.off1 : nullptr, a.poff1,
+                        a.tiles1, a.off2, a.tiles2, a.ctr, s);
   const int64_t mt_bound = (R + (int64_t)E * (tt - 1)) / tt;
 
   auto ragged_m = [&](const void* A, bool ab, int64_t a_sm, const void* B, bool bb, int64_t b_sk,
@@ -1392,9 +1365,6 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       launch_down_routed_bf16(f1, s);
     };
     if (bf) {
-      hipLaunchKernelGGL(single_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.off1,
-                         a.poff1);
-      launch_tile_table(a.off1, 1, a.tiles1, a.ctr, s);
       f1.offsets = a.off1;
       f1.tile_off = a.tiles1;
       f1.ctr = a.ctr;
@@ -1498,8 +1468,6 @@ void launch_layer_bwd(const BwdArgs& a, hipStream_t s) {
       // [dG_s hi | lo] against W_sg^T, rows T..2T-1 [dU_s hi | lo] against
       // W_su^T (the group-1 weight, d*ld elements after W_sg^T); their
       // products go to the two slabs of dxs, added in bwd_dx_kernel
-      hipLaunchKernelGGL(two_seg_offsets_kernel, dim3(1), dim3(64), 0, s, (int)T, a.off2);
-      launch_tile_table(a.off2, 2, a.tiles2, a.ctr, s);
       f1.offsets = a.off2;
       f1.tile_off = a.tiles2;
       f1.R = 2 * T;

@@ -285,4 +285,46 @@ void launch_tile_table(const int32_t* offsets, int E, int32_t* tiles, int32_t* c
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(256), 0, stream, offsets, E, tiles, ctr);
 }
 
+// The backward's small tables in one launch: the M-tile prefix of G row
+// segments (offsets [G+1], tiles of `tile` rows: prefix[g] = tiles before
+// segment g, prefix[G] = all; G <= 256), and, with off1 non-null, the tables
+// of one segment of T rows (off1 = {0, T}, poff1 = {0, 2 roundup(T, 64)}, its
+// tile table tiles1) and of two segments of T rows each (off2 = {0, T, 2T},
+// tiles2), with the GEMM counters zeroed as the tile table's launch zeroes
+// them.
+__global__ __launch_bounds__(256) void segment_tables_kernel(
+    const int32_t* __restrict__ offsets, int G, int tile, int32_t* __restrict__ prefix, int T,
+    int32_t* __restrict__ off1, int32_t* __restrict__ poff1, int32_t* __restrict__ tiles1,
+    int32_t* __restrict__ off2, int32_t* __restrict__ tiles2, int32_t* __restrict__ ctr) {
+  __shared__ int buf[256];
+  const int tid = threadIdx.x;
+  const int nt = tid < G ? (offsets[tid + 1] - offsets[tid] + tile - 1) / tile : 0;
+  const int incl = block_inclusive_scan(nt, buf);
+  if (tid < G) prefix[tid] = incl - nt;
+  if (tid == G - 1) prefix[G] = incl;
+  if (G == 0 && tid == 0) prefix[0] = 0;
+  if (!off1) return;  // block-uniform
+  if (tid == 0) {
+    off1[0] = 0;
+    off1[1] = T;
+    poff1[0] = 0;
+    poff1[1] = 2 * ((T + 63) / 64 * 64);
+    off2[0] = 0;
+    off2[1] = T;
+    off2[2] = 2 * T;
+  }
+  if (tid < kGemmCounters) ctr[tid] = 0;
+  __syncthreads();  // buf is reused
+  write_tile_table(tid < 1 ? T : 0, 1, tiles1, buf);
+  __syncthreads();
+  write_tile_table(tid < 2 ? T : 0, 2, tiles2, buf);
+}
+
+void launch_segment_tables(const int32_t* offsets, int G, int tile, int32_t* prefix, int64_t T,
+                           int32_t* off1, int32_t* poff1, int32_t* tiles1, int32_t* off2,
+                           int32_t* tiles2, int32_t* ctr, hipStream_t stream) {
+  hipLaunchKernelGGL(segment_tables_kernel, dim3(1), dim3(256), 0, stream, offsets, G, tile,
+                     prefix, (int)T, off1, poff1, tiles1, off2, tiles2, ctr);
+}
+
 }  // namespace moe

@@ -53,6 +53,13 @@ void launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
 // Tile table from expert offsets (for a grouped FFN call on its own); also
 // zeroes the GEMM work counters.
+// The backward's small tables, one launch: the M-tile prefix of G <= 256 row
+// segments (tiles of `tile` rows), and with off1 non-null the row offsets and
+// tile tables of one segment of T rows (off1, poff1, tiles1) and of two
+// segments of T rows (off2, tiles2).
+void launch_segment_tables(const int32_t* offsets, int G, int tile, int32_t* prefix, int64_t T,
+                           int32_t* off1, int32_t* poff1, int32_t* tiles1, int32_t* off2,
+                           int32_t* tiles2, int32_t* ctr, hipStream_t stream);
 void launch_tile_table(const int32_t* offsets, int E, int32_t* tiles, int32_t* ctr,
                        hipStream_t stream);
 constexpr int kGemmCounters = 16;  // 8 per grouped GEMM launch (one per XCD)
